@@ -1,0 +1,197 @@
+"""Python binding of libaqp.so: quantized paged attention for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/aqp.h``; there is no Python or
+CPU fallback. Importing this package without the built library raises.
+
+Functions accept torch tensors (device memory for device arguments) or plain
+integers (raw pointers); bf16 data travels as ``torch.bfloat16`` or
+``torch.int16`` / ``torch.uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libaqp.so")
+
+KV_AUTO, KV_FP8_E4M3, KV_FP8_E5M2, KV_INT8 = 0, 1, 2, 3
+SCALE_PER_TENSOR, SCALE_PER_TOKEN_HEAD = 0, 1
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_SCHEDULE_MISMATCH, ERR_SCRATCH_TOO_SMALL, ERR_HIP = 0, -1, -2, -3, -4, -5
+
+
+class AqpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"aqp status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32)]
+
+
+class AttnParams(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("window", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float), ("softcap", ctypes.c_float), ("decode_parallelism", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m attention_quantized_paged_amd.build` "
+                          "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.aqp_parse_kv_dtype.argtypes = [ctypes.c_char_p, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.aqp_cache_bytes.argtypes = [ctypes.POINTER(CacheDesc), ctypes.POINTER(sz), ctypes.POINTER(sz),
+                                    ctypes.POINTER(sz)]
+    lib.aqp_cache_write.argtypes = [ctypes.POINTER(CacheDesc), P, P, P, i64, i64, P, f32, f32, P]
+    lib.aqp_get_schedule.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(CacheDesc), P, P, i32, P,
+                                     ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.aqp_paged_attention.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(CacheDesc), P, P, P, P, P, f32,
+                                        f32, P, sz, P, P]
+    lib.aqp_last_error.argtypes = []
+    lib.aqp_last_error.restype = ctypes.c_char_p
+    for fn in ("aqp_parse_kv_dtype", "aqp_cache_bytes", "aqp_cache_write", "aqp_get_schedule", "aqp_paged_attention"):
+        getattr(lib, fn).restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("aqp_parse_kv_dtype", "aqp_cache_bytes", "aqp_cache_write", "aqp_get_schedule", "aqp_paged_attention",
+            "aqp_last_error")
+
+
+def _check(rc: int) -> None:
+    if rc != OK:
+        raise AqpError(rc, _lib.aqp_last_error().decode())
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    return x.data_ptr()  # torch tensor
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev_ok(t, name: str) -> None:
+    if hasattr(t, "is_cuda") and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if hasattr(t, "is_contiguous") and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def parse_kv_dtype(s: str) -> Tuple[int, int]:
+    dt, md = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.aqp_parse_kv_dtype(s.encode(), ctypes.byref(dt), ctypes.byref(md)))
+    return dt.value, md.value
+
+
+def cache_desc(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, kv_cache_dtype: str) -> CacheDesc:
+    dt, md = parse_kv_dtype(kv_cache_dtype)
+    return CacheDesc(num_blocks, block_size, num_kv_heads, head_dim, dt, md)
+
+
+def attn_params(num_q_heads: int, num_kv_heads: int, head_dim: int, max_blocks_per_seq: int, causal: bool = True,
+                window: int = 0, sm_scale: float = 0.0, softcap: float = 0.0,
+                decode_parallelism: int = 0) -> AttnParams:
+    return AttnParams(num_q_heads, num_kv_heads, head_dim, int(causal), window, max_blocks_per_seq, sm_scale,
+                      softcap, decode_parallelism, 0)
+
+
+def cache_bytes(desc: CacheDesc) -> Tuple[int, int, int]:
+    p, b, t = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_lib.aqp_cache_bytes(ctypes.byref(desc), ctypes.byref(p), ctypes.byref(b), ctypes.byref(t)))
+    return p.value, b.value, t.value
+
+
+def cache_write(desc: CacheDesc, cache, k, v, slot_mapping, k_scale: float = 1.0, v_scale: float = 1.0,
+                token_stride: Optional[int] = None, stream=None) -> None:
+    """k, v: bf16 [N, Hkv, D] (token stride may exceed Hkv*D); slot_mapping: int64 [N]."""
+    n = int(k.shape[0]) if hasattr(k, "shape") else 0
+    if token_stride is None:
+        token_stride = int(k.stride(0)) if hasattr(k, "stride") else desc.num_kv_heads * desc.head_dim
+    for t, nm in ((cache, "cache"), (slot_mapping, "slot_mapping")):
+        _dev_ok(t, nm)
+    _check(_lib.aqp_cache_write(ctypes.byref(desc), _ptr(cache), _ptr(k), _ptr(v), n, token_stride,
+                                _ptr(slot_mapping), float(k_scale), float(v_scale), _stream(stream)))
+
+
+@dataclass
+class Schedule:
+    meta: np.ndarray      # host bytes
+    scratch_bytes: int
+    header: dict
+
+
+_HDR_FIELDS = ("magic version dtype mode kv_elem_bytes staged_elem_bytes scale_bytes head_dim block_size num_blocks "
+               "num_q_heads num_kv_heads causal window max_blocks_per_seq num_seqs sm_scale softcap total_q_tokens "
+               "tile_keys dec_iter_keys dec_waves pf_rows pf_kv_tile heads_per_unit dec_lds_bytes pf_lds_bytes "
+               "num_dec_wgs num_dec_segs num_parts num_comb num_pf_items group_heads").split()
+_HDR_FIELDS64 = "off_dec_segs off_dec_wg_start off_comb off_pf_items meta_bytes scratch_bytes page_bytes block_bytes dec_kv_keys".split()
+
+
+def parse_header(meta: np.ndarray) -> dict:
+    n32 = len(_HDR_FIELDS)
+    w = meta[: 4 * n32].view(np.uint32)
+    out = {}
+    for i, name in enumerate(_HDR_FIELDS):
+        if name in ("sm_scale", "softcap"):
+            out[name] = float(w[i:i + 1].view(np.float32)[0])
+        elif name in ("magic", "version"):
+            out[name] = int(w[i])
+        else:
+            out[name] = int(w[i:i + 1].view(np.int32)[0])
+    off = (4 * n32 + 7) // 8 * 8
+    w64 = meta[off: off + 8 * len(_HDR_FIELDS64)].view(np.int64)
+    for i, name in enumerate(_HDR_FIELDS64):
+        out[name] = int(w64[i])
+    return out
+
+
+def get_schedule(params: AttnParams, desc: CacheDesc, seq_lens, query_start_loc) -> Schedule:
+    """seq_lens, query_start_loc: host int32 arrays (numpy or CPU tensors)."""
+    sl = np.ascontiguousarray(np.asarray(seq_lens), dtype=np.int32)
+    qsl = np.ascontiguousarray(np.asarray(query_start_loc), dtype=np.int32)
+    if qsl.shape[0] != sl.shape[0] + 1:
+        raise ValueError("query_start_loc must have num_seqs + 1 entries")
+    nbytes, scratch = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(_lib.aqp_get_schedule(ctypes.byref(params), ctypes.byref(desc), sl.ctypes.data, qsl.ctypes.data,
+                                 sl.shape[0], None, ctypes.byref(nbytes), ctypes.byref(scratch)))
+    meta = np.zeros(nbytes.value, dtype=np.uint8)
+    _check(_lib.aqp_get_schedule(ctypes.byref(params), ctypes.byref(desc), sl.ctypes.data, qsl.ctypes.data,
+                                 sl.shape[0], meta.ctypes.data, ctypes.byref(nbytes), ctypes.byref(scratch)))
+    return Schedule(meta, scratch.value, parse_header(meta))
+
+
+def paged_attention(params: AttnParams, desc: CacheDesc, cache, q, block_tables, meta_host, meta_dev,
+                    k_scale: float, v_scale: float, scratch, scratch_bytes: int, out, stream=None) -> None:
+    for t, nm in ((cache, "cache"), (q, "q"), (block_tables, "block_tables"), (meta_dev, "meta_dev"), (out, "out")):
+        _dev_ok(t, nm)
+    _check(_lib.aqp_paged_attention(ctypes.byref(params), ctypes.byref(desc), _ptr(cache), _ptr(q),
+                                    _ptr(block_tables), _ptr(meta_host), _ptr(meta_dev), float(k_scale),
+                                    float(v_scale), _ptr(scratch), int(scratch_bytes), _ptr(out), _stream(stream)))
+
+
+def last_error() -> str:
+    return _lib.aqp_last_error().decode()

@@ -1,0 +1,451 @@
+// Host side of the C ABI: argument validation, cache geometry, the per-batch
+// schedule, and kernel launches. No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "aqp_internal.h"
+
+namespace aqp {
+
+static thread_local std::string g_last_error;
+
+void set_error(const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+static int fail(int code, const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Which (dtype, mode) pairs are built: per-tensor fp8 (e4m3, e5m2) as on the
+// PR 39445 page, per-token-head int8 / fp8 e4m3 as on the PR 38378 page.
+static int check_dtype_mode(int32_t dtype, int32_t mode, const char** why) {
+  if (mode != AQP_SCALE_PER_TENSOR && mode != AQP_SCALE_PER_TOKEN_HEAD) { *why = "unknown scale mode"; return AQP_ERR_INVALID; }
+  if (dtype == AQP_KV_AUTO) { *why = "kv dtype 'auto' (unquantised cache) is not supported by this build"; return AQP_ERR_UNSUPPORTED; }
+  if (dtype != AQP_KV_FP8_E4M3 && dtype != AQP_KV_FP8_E5M2 && dtype != AQP_KV_INT8) { *why = "unknown kv dtype"; return AQP_ERR_INVALID; }
+  if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_INT8) { *why = "int8 with per-tensor scales is not supported"; return AQP_ERR_UNSUPPORTED; }
+  if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_FP8_E5M2) { *why = "fp8_e5m2 with per-token-head scales is not supported"; return AQP_ERR_UNSUPPORTED; }
+  return AQP_OK;
+}
+
+int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
+  int rc = check_dtype_mode(d.dtype, d.mode, why);
+  if (rc) return rc;
+  if (d.num_blocks < 0 || d.num_kv_heads <= 0 || d.block_size <= 0 || d.head_dim <= 0) { *why = "non-positive cache dimension"; return AQP_ERR_INVALID; }
+  if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256) { *why = "head_dim must be 64, 128 or 256"; return AQP_ERR_UNSUPPORTED; }
+  if (d.block_size % kTileKeys != 0) { *why = "block_size must be a multiple of 16"; return AQP_ERR_UNSUPPORTED; }
+  if ((int64_t)d.block_size * d.head_dim > (1ll << 30)) { *why = "block_size too large"; return AQP_ERR_UNSUPPORTED; }
+  g->head_dim = d.head_dim;
+  g->block_size = d.block_size;
+  g->kv_elem_bytes = 1;      // every supported dtype stores one byte per element
+  g->staged_elem_bytes = 1;  // the kernels stage raw codes in LDS and widen them in registers
+  g->scale_bytes = d.mode == AQP_SCALE_PER_TOKEN_HEAD ? 4 : 0;
+  g->pad_ = 0;
+  g->page_bytes = round_up((int64_t)d.block_size * d.head_dim * g->kv_elem_bytes + (int64_t)d.block_size * g->scale_bytes, 128);
+  g->block_bytes = 2 * (int64_t)d.num_kv_heads * g->page_bytes;
+  g->total_bytes = (int64_t)d.num_blocks * g->block_bytes;
+  // Decode work-group: each wave stages one iteration of V codes; at the end
+  // waves 1..3 hand their (O, m, l) for up to 16 heads to wave 0.
+  const int32_t dec_stage = kDecWaves * kDecIterKeys * d.head_dim * g->staged_elem_bytes;
+  const int32_t dec_merge = (kDecWaves - 1) * kMaxHeadsPerUnit * (d.head_dim + 2) * 4;
+  g->dec_lds_bytes = std::max(dec_stage, dec_merge);
+  // Prefill work-group: double-buffered K and V tiles of codes plus their row scales.
+  g->pf_lds_bytes = 2 * (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes + 2 * kPfKvTile * 4);
+  return AQP_OK;
+}
+
+}  // namespace aqp
+
+using namespace aqp;
+
+extern "C" const char* aqp_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int aqp_parse_kv_dtype(const char* s, int32_t* dtype, int32_t* mode) {
+  if (!s || !dtype || !mode) return fail(AQP_ERR_INVALID, "aqp_parse_kv_dtype: null argument");
+  struct { const char* name; int32_t dt, md; } table[] = {
+      {"fp8", AQP_KV_FP8_E4M3, AQP_SCALE_PER_TENSOR},
+      {"fp8_e4m3", AQP_KV_FP8_E4M3, AQP_SCALE_PER_TENSOR},
+      {"fp8_e5m2", AQP_KV_FP8_E5M2, AQP_SCALE_PER_TENSOR},
+      {"int8_per_token_head", AQP_KV_INT8, AQP_SCALE_PER_TOKEN_HEAD},
+      {"fp8_per_token_head", AQP_KV_FP8_E4M3, AQP_SCALE_PER_TOKEN_HEAD},
+  };
+  for (auto& e : table) {
+    if (std::strcmp(s, e.name) == 0) { *dtype = e.dt; *mode = e.md; return AQP_OK; }
+  }
+  if (std::strcmp(s, "auto") == 0) {
+    *dtype = AQP_KV_AUTO;
+    *mode = AQP_SCALE_PER_TENSOR;
+    return fail(AQP_ERR_UNSUPPORTED, "kv_cache_dtype 'auto' (unquantised cache) is not supported by this build");
+  }
+  return fail(AQP_ERR_INVALID, "unknown kv_cache_dtype '%s'", s);
+}
+
+extern "C" int aqp_cache_bytes(const aqp_cache_desc* desc, size_t* page_bytes, size_t* block_bytes, size_t* total_bytes) {
+  if (!desc) return fail(AQP_ERR_INVALID, "aqp_cache_bytes: null descriptor");
+  Geometry g;
+  const char* why = "";
+  int rc = make_geometry(*desc, &g, &why);
+  if (rc) return fail(rc, "aqp_cache_bytes: %s", why);
+  if (page_bytes) *page_bytes = (size_t)g.page_bytes;
+  if (block_bytes) *block_bytes = (size_t)g.block_bytes;
+  if (total_bytes) *total_bytes = (size_t)g.total_bytes;
+  return AQP_OK;
+}
+
+extern "C" int aqp_cache_write(const aqp_cache_desc* desc, void* cache, const void* k, const void* v, int64_t num_tokens,
+                               int64_t token_stride, const int64_t* slot_mapping, float k_scale, float v_scale,
+                               void* stream) {
+  if (!desc) return fail(AQP_ERR_INVALID, "aqp_cache_write: null descriptor");
+  Geometry g;
+  const char* why = "";
+  int rc = make_geometry(*desc, &g, &why);
+  if (rc) return fail(rc, "aqp_cache_write: %s", why);
+  if (num_tokens < 0) return fail(AQP_ERR_INVALID, "aqp_cache_write: negative num_tokens");
+  if (num_tokens == 0) return AQP_OK;
+  if (!cache || !k || !v || !slot_mapping) return fail(AQP_ERR_INVALID, "aqp_cache_write: null pointer");
+  if (token_stride < (int64_t)desc->num_kv_heads * desc->head_dim)
+    return fail(AQP_ERR_INVALID, "aqp_cache_write: token_stride %lld < num_kv_heads * head_dim", (long long)token_stride);
+  if (token_stride % 8 != 0 || ((uintptr_t)k % 16) || ((uintptr_t)v % 16))
+    return fail(AQP_ERR_INVALID, "aqp_cache_write: k/v must be 16-byte aligned with a token_stride that is a multiple of 8");
+  if (desc->mode == AQP_SCALE_PER_TENSOR && (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale < 0 || v_scale < 0))
+    return fail(AQP_ERR_INVALID, "aqp_cache_write: per-tensor scales must be finite and non-negative");
+  CacheWriteArgs a;
+  a.cache = (uint8_t*)cache;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.token_stride = token_stride;
+  a.page_bytes = g.page_bytes;
+  a.block_bytes = g.block_bytes;
+  a.total_slots = (int64_t)desc->num_blocks * desc->block_size;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.head_dim = desc->head_dim;
+  a.block_size = desc->block_size;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return launch_cache_write(desc->dtype, desc->mode, a, stream);
+}
+
+// ---- schedule -------------------------------------------------------------
+
+static int check_params(const aqp_attn_params& p, const aqp_cache_desc& d, const char** why) {
+  if (p.num_kv_heads != d.num_kv_heads) { *why = "params.num_kv_heads differs from the cache's"; return AQP_ERR_INVALID; }
+  if (p.head_dim != d.head_dim) { *why = "params.head_dim differs from the cache's"; return AQP_ERR_INVALID; }
+  if (p.num_q_heads <= 0 || p.num_q_heads % p.num_kv_heads != 0) { *why = "num_q_heads must be a positive multiple of num_kv_heads"; return AQP_ERR_INVALID; }
+  if (p.num_q_heads / p.num_kv_heads > kPfRows) { *why = "q heads per KV head above 128 are not supported"; return AQP_ERR_UNSUPPORTED; }
+  if (p.causal != 0 && p.causal != 1) { *why = "causal must be 0 or 1"; return AQP_ERR_INVALID; }
+  if (p.window < 0) { *why = "negative window"; return AQP_ERR_INVALID; }
+  if (p.window > 0 && !p.causal) { *why = "a sliding window needs causal attention"; return AQP_ERR_UNSUPPORTED; }
+  if (p.max_blocks_per_seq <= 0) { *why = "max_blocks_per_seq must be positive"; return AQP_ERR_INVALID; }
+  if (!(p.sm_scale >= 0.0f) || !std::isfinite(p.sm_scale)) { *why = "sm_scale must be finite and >= 0"; return AQP_ERR_INVALID; }
+  if (!(p.softcap >= 0.0f) || !std::isfinite(p.softcap)) { *why = "softcap must be finite and >= 0"; return AQP_ERR_INVALID; }
+  if (p.decode_parallelism < 0) { *why = "negative decode_parallelism"; return AQP_ERR_INVALID; }
+  return AQP_OK;
+}
+
+static float effective_sm_scale(const aqp_attn_params& p) {
+  return p.sm_scale > 0.0f ? p.sm_scale : (float)(1.0 / std::sqrt((double)p.head_dim));
+}
+
+extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_desc* desc, const int32_t* seq_lens,
+                                const int32_t* qsl, int32_t num_seqs, void* meta_host, size_t* meta_bytes,
+                                size_t* scratch_bytes) {
+  if (!params || !desc || !meta_bytes) return fail(AQP_ERR_INVALID, "aqp_get_schedule: null argument");
+  if (num_seqs < 0) return fail(AQP_ERR_INVALID, "aqp_get_schedule: negative num_seqs");
+  if (num_seqs > 0 && (!seq_lens || !qsl)) return fail(AQP_ERR_INVALID, "aqp_get_schedule: null seq_lens / query_start_loc");
+  Geometry g;
+  const char* why = "";
+  int rc = make_geometry(*desc, &g, &why);
+  if (rc) return fail(rc, "aqp_get_schedule: %s", why);
+  rc = check_params(*params, *desc, &why);
+  if (rc) return fail(rc, "aqp_get_schedule: %s", why);
+  const aqp_attn_params& p = *params;
+  const int32_t G = p.num_q_heads / p.num_kv_heads;
+  const int32_t bs = desc->block_size;
+  if (num_seqs > 0 && qsl[0] != 0) return fail(AQP_ERR_INVALID, "aqp_get_schedule: query_start_loc[0] must be 0");
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t L = seq_lens[b], ql = (int64_t)qsl[b + 1] - qsl[b];
+    if (L < 0 || ql < 0 || ql > L)
+      return fail(AQP_ERR_INVALID, "aqp_get_schedule: sequence %d has seq_len %lld and query_len %lld (need 0 <= query_len <= seq_len)", b, (long long)L, (long long)ql);
+    if ((L + bs - 1) / bs > p.max_blocks_per_seq)
+      return fail(AQP_ERR_INVALID, "aqp_get_schedule: sequence %d needs %lld blocks > max_blocks_per_seq %d", b, (long long)((L + bs - 1) / bs), p.max_blocks_per_seq);
+  }
+  const int64_t total_q = num_seqs > 0 ? qsl[num_seqs] : 0;
+  if (total_q > INT32_MAX / 2) return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: too many query tokens");
+
+  // ---- decode: units (sequence, KV head, head group) over their visible keys,
+  // cut into equal runs of 16-key tiles, one run per work-group.
+  struct Unit { int32_t seq, kvh, head0, nheads, lo, hi, q_tok; int64_t t0, ntiles; };
+  std::vector<Unit> units;
+  const int32_t hpu = std::min<int32_t>(G, kMaxHeadsPerUnit);
+  int64_t total_tiles = 0, dec_keys = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t L = seq_lens[b], ql = qsl[b + 1] - qsl[b];
+    if (ql != 1) continue;
+    const int32_t pos = L - 1;
+    const int32_t lo = (p.window > 0 && pos - p.window + 1 > 0) ? pos - p.window + 1 : 0;
+    const int32_t hi = L;  // the single query sees every key up to its own position
+    const int64_t t0 = lo / kTileKeys, t1 = (hi + kTileKeys - 1) / kTileKeys;
+    for (int32_t h = 0; h < p.num_kv_heads; ++h) {
+      dec_keys += hi - lo;
+      for (int32_t h0 = 0; h0 < G; h0 += kMaxHeadsPerUnit) {
+        units.push_back({b, h, h0, std::min<int32_t>(kMaxHeadsPerUnit, G - h0), lo, hi, qsl[b], t0, t1 - t0});
+        total_tiles += t1 - t0;
+      }
+    }
+  }
+  std::vector<DecSeg> segs;
+  std::vector<int32_t> wg_start;
+  std::vector<CombItem> comb;
+  int32_t num_parts = 0;
+  int32_t num_wgs = 0;
+  if (total_tiles > 0) {
+    const int64_t target = p.decode_parallelism > 0 ? p.decode_parallelism : kDefaultDecodeWGs;
+    const int64_t by_size = (total_tiles * kTileKeys + kMinDecodeKeysPerWG - 1) / kMinDecodeKeysPerWG;
+    int64_t P = std::max<int64_t>(1, std::min(target, by_size));
+    const int64_t per = (total_tiles + P - 1) / P;
+    P = (total_tiles + per - 1) / per;
+    num_wgs = (int32_t)P;
+    // first pass: count segments per unit to know which units are split
+    std::vector<int32_t> unit_nseg(units.size(), 0);
+    {
+      int64_t base = 0;
+      for (size_t u = 0; u < units.size(); ++u) {
+        const int64_t a = base, e = base + units[u].ntiles;
+        unit_nseg[u] = (int32_t)((e - 1) / per - a / per + 1);
+        base = e;
+      }
+    }
+    std::vector<int32_t> unit_first_part(units.size(), -1);
+    for (size_t u = 0; u < units.size(); ++u) {
+      if (unit_nseg[u] > 1) {
+        unit_first_part[u] = num_parts;
+        comb.push_back({units[u].kvh, units[u].head0, units[u].nheads, units[u].q_tok, num_parts, unit_nseg[u], 0, 0});
+        num_parts += unit_nseg[u];
+      }
+    }
+    // second pass: emit segments grouped by work-group
+    wg_start.assign(P + 1, 0);
+    int64_t base = 0;
+    int32_t w_cur = 0;
+    for (size_t u = 0; u < units.size(); ++u) {
+      const Unit& U = units[u];
+      int64_t a = base;
+      const int64_t e = base + U.ntiles;
+      int32_t k = 0;
+      while (a < e) {
+        const int64_t w = a / per;
+        const int64_t b_end = std::min(e, (w + 1) * per);
+        while (w_cur < w) wg_start[++w_cur] = (int32_t)segs.size();
+        const int64_t tile_lo = U.t0 + (a - base), tile_hi = U.t0 + (b_end - base);
+        DecSeg s;
+        s.seq = U.seq;
+        s.kvh = U.kvh;
+        s.head0 = U.head0;
+        s.nheads = U.nheads;
+        s.k_lo = (int32_t)std::max<int64_t>(U.lo, tile_lo * kTileKeys);
+        s.k_hi = (int32_t)std::min<int64_t>(U.hi, tile_hi * kTileKeys);
+        s.q_tok = U.q_tok;
+        s.part = unit_nseg[u] > 1 ? unit_first_part[u] + k : -1;
+        segs.push_back(s);
+        ++k;
+        a = b_end;
+      }
+      base = e;
+    }
+    while (w_cur < P) wg_start[++w_cur] = (int32_t)segs.size();
+  }
+
+  // ---- prefill items: (sequence, KV head, run of query tokens), all G heads of
+  // the KV head in one item; heaviest (most keys) first.
+  std::vector<PfItem> pf;
+  const int32_t tpi = std::max<int32_t>(1, kPfRows / G);
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t L = seq_lens[b], ql = qsl[b + 1] - qsl[b];
+    if (ql <= 1) continue;
+    for (int32_t q0 = 0; q0 < ql; q0 += tpi) {
+      const int32_t q1 = std::min(ql, q0 + tpi);
+      const int32_t khi = p.causal ? (L - ql + q1) : L;  // exclusive end of the last row's keys
+      for (int32_t h = 0; h < p.num_kv_heads; ++h) pf.push_back({b, h, q0, q1, L, ql, qsl[b], khi});
+    }
+  }
+  std::stable_sort(pf.begin(), pf.end(), [&](const PfItem& x, const PfItem& y) {
+    auto work = [&](const PfItem& it) {
+      const int32_t first = it.L - it.ql + it.q_lo;
+      const int32_t lo = (p.window > 0 && first - p.window + 1 > 0) ? first - p.window + 1 : 0;
+      return (int64_t)it.k_hi_max - lo;
+    };
+    return work(x) > work(y);
+  });
+
+  // ---- sizes and layout
+  int64_t off = round_up(sizeof(SchedHeader), 256);
+  const int64_t off_segs = off;
+  off = round_up(off + (int64_t)segs.size() * sizeof(DecSeg), 256);
+  const int64_t off_wgs = off;
+  off = round_up(off + (int64_t)wg_start.size() * sizeof(int32_t), 256);
+  const int64_t off_comb = off;
+  off = round_up(off + (int64_t)comb.size() * sizeof(CombItem), 256);
+  const int64_t off_pf = off;
+  off = round_up(off + (int64_t)pf.size() * sizeof(PfItem), 256);
+  const int64_t need = off;
+  const int64_t scratch = (int64_t)num_parts * part_floats(hpu, desc->head_dim) * 4;
+  if (scratch_bytes) *scratch_bytes = (size_t)scratch;
+  if (!meta_host) { *meta_bytes = (size_t)need; return AQP_OK; }
+  if (*meta_bytes < (size_t)need) {
+    size_t have = *meta_bytes;
+    *meta_bytes = (size_t)need;
+    return fail(AQP_ERR_INVALID, "aqp_get_schedule: meta buffer of %zu bytes, need %lld", have, (long long)need);
+  }
+  *meta_bytes = (size_t)need;
+  uint8_t* m = (uint8_t*)meta_host;
+  std::memset(m, 0, (size_t)need);
+  SchedHeader h;
+  std::memset(&h, 0, sizeof h);
+  h.magic = kMagic;
+  h.version = kVersion;
+  h.dtype = desc->dtype;
+  h.mode = desc->mode;
+  h.kv_elem_bytes = g.kv_elem_bytes;
+  h.staged_elem_bytes = g.staged_elem_bytes;
+  h.scale_bytes = g.scale_bytes;
+  h.head_dim = desc->head_dim;
+  h.block_size = desc->block_size;
+  h.num_blocks = desc->num_blocks;
+  h.num_q_heads = p.num_q_heads;
+  h.num_kv_heads = p.num_kv_heads;
+  h.causal = p.causal;
+  h.window = p.window;
+  h.max_blocks_per_seq = p.max_blocks_per_seq;
+  h.num_seqs = num_seqs;
+  h.sm_scale = effective_sm_scale(p);
+  h.softcap = p.softcap;
+  h.total_q_tokens = (int32_t)total_q;
+  h.tile_keys = kTileKeys;
+  h.dec_iter_keys = kDecIterKeys;
+  h.dec_waves = kDecWaves;
+  h.pf_rows = kPfRows;
+  h.pf_kv_tile = kPfKvTile;
+  h.heads_per_unit = kMaxHeadsPerUnit;
+  h.dec_lds_bytes = g.dec_lds_bytes;
+  h.pf_lds_bytes = g.pf_lds_bytes;
+  h.num_dec_wgs = num_wgs;
+  h.num_dec_segs = (int32_t)segs.size();
+  h.num_parts = num_parts;
+  h.num_comb = (int32_t)comb.size();
+  h.num_pf_items = (int32_t)pf.size();
+  h.group_heads = hpu;
+  h.off_dec_segs = off_segs;
+  h.off_dec_wg_start = off_wgs;
+  h.off_comb = off_comb;
+  h.off_pf_items = off_pf;
+  h.meta_bytes = need;
+  h.scratch_bytes = scratch;
+  h.page_bytes = g.page_bytes;
+  h.block_bytes = g.block_bytes;
+  h.dec_kv_keys = dec_keys;
+  std::memcpy(m, &h, sizeof h);
+  if (!segs.empty()) std::memcpy(m + off_segs, segs.data(), segs.size() * sizeof(DecSeg));
+  if (!wg_start.empty()) std::memcpy(m + off_wgs, wg_start.data(), wg_start.size() * sizeof(int32_t));
+  if (!comb.empty()) std::memcpy(m + off_comb, comb.data(), comb.size() * sizeof(CombItem));
+  if (!pf.empty()) std::memcpy(m + off_pf, pf.data(), pf.size() * sizeof(PfItem));
+  return AQP_OK;
+}
+
+// ---- attention -----------------------------------------------------------
+
+#define MISMATCH_IF(cond, what)                                                      \
+  do {                                                                               \
+    if (cond) return fail(AQP_ERR_SCHEDULE_MISMATCH, "aqp_paged_attention: schedule was built for a different %s", what); \
+  } while (0)
+
+extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cache_desc* desc, const void* cache,
+                                   const void* q, const int32_t* block_tables, const void* meta_host,
+                                   const void* meta_dev, float k_scale, float v_scale, void* scratch,
+                                   size_t scratch_bytes, void* out, void* stream) {
+  if (!params || !desc || !meta_host) return fail(AQP_ERR_INVALID, "aqp_paged_attention: null argument");
+  Geometry g;
+  const char* why = "";
+  int rc = make_geometry(*desc, &g, &why);
+  if (rc) return fail(rc, "aqp_paged_attention: %s", why);
+  rc = check_params(*params, *desc, &why);
+  if (rc) return fail(rc, "aqp_paged_attention: %s", why);
+  SchedHeader h;
+  std::memcpy(&h, meta_host, sizeof h);
+  if (h.magic != kMagic || h.version != kVersion) return fail(AQP_ERR_SCHEDULE_MISMATCH, "aqp_paged_attention: meta is not an aqp schedule of this version");
+  // The schedule must describe exactly this cache and these parameters; its
+  // element sizes and tile geometry must be the ones the kernels are built with.
+  MISMATCH_IF(h.dtype != desc->dtype || h.mode != desc->mode, "kv dtype / scale mode");
+  MISMATCH_IF(h.kv_elem_bytes != g.kv_elem_bytes || h.staged_elem_bytes != g.staged_elem_bytes || h.scale_bytes != g.scale_bytes, "KV element size");
+  MISMATCH_IF(h.head_dim != desc->head_dim || h.block_size != desc->block_size || h.num_blocks != desc->num_blocks, "cache geometry");
+  MISMATCH_IF(h.page_bytes != g.page_bytes || h.block_bytes != g.block_bytes, "page layout");
+  MISMATCH_IF(h.num_q_heads != params->num_q_heads || h.num_kv_heads != params->num_kv_heads, "head count");
+  MISMATCH_IF(h.causal != params->causal || h.window != params->window || h.max_blocks_per_seq != params->max_blocks_per_seq, "mask / block-table shape");
+  MISMATCH_IF(h.sm_scale != effective_sm_scale(*params) || h.softcap != params->softcap, "logit scale / soft-cap");
+  MISMATCH_IF(h.tile_keys != kTileKeys || h.dec_iter_keys != kDecIterKeys || h.dec_waves != kDecWaves || h.pf_rows != kPfRows ||
+              h.pf_kv_tile != kPfKvTile || h.heads_per_unit != kMaxHeadsPerUnit || h.dec_lds_bytes != g.dec_lds_bytes ||
+              h.pf_lds_bytes != g.pf_lds_bytes, "tile geometry");
+  if ((int64_t)scratch_bytes < h.scratch_bytes)
+    return fail(AQP_ERR_SCRATCH_TOO_SMALL, "aqp_paged_attention: scratch of %zu bytes, schedule needs %lld", scratch_bytes, (long long)h.scratch_bytes);
+  if (h.scratch_bytes > 0 && !scratch) return fail(AQP_ERR_INVALID, "aqp_paged_attention: null scratch");
+  if (h.total_q_tokens == 0) return AQP_OK;
+  if (!cache || !q || !block_tables || !meta_dev || !out) return fail(AQP_ERR_INVALID, "aqp_paged_attention: null pointer");
+  if (desc->mode == AQP_SCALE_PER_TENSOR && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
+    return fail(AQP_ERR_INVALID, "aqp_paged_attention: per-tensor scales must be finite");
+  AttnArgs a;
+  a.cache = (const uint8_t*)cache;
+  a.q = (const uint16_t*)q;
+  a.block_tables = block_tables;
+  a.meta_dev = (const uint8_t*)meta_dev;
+  a.scratch = (float*)scratch;
+  a.out = (uint16_t*)out;
+  a.page_bytes = g.page_bytes;
+  a.block_bytes = g.block_bytes;
+  a.head_dim = desc->head_dim;
+  a.block_size = desc->block_size;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.num_q_heads = params->num_q_heads;
+  a.group = params->num_q_heads / params->num_kv_heads;
+  a.max_blocks_per_seq = params->max_blocks_per_seq;
+  a.window = params->window;
+  a.causal = params->causal;
+  a.sm_scale = h.sm_scale;
+  a.softcap = params->softcap;
+  a.k_scale = desc->mode == AQP_SCALE_PER_TENSOR ? k_scale : 1.0f;
+  a.v_scale = desc->mode == AQP_SCALE_PER_TENSOR ? v_scale : 1.0f;
+  a.hdr = &h;
+  if (h.num_pf_items > 0) {
+    rc = launch_prefill(desc->dtype, desc->mode, a, stream);
+    if (rc) return rc;
+  }
+  if (h.num_dec_segs > 0) {
+    rc = launch_decode(desc->dtype, desc->mode, a, stream);
+    if (rc) return rc;
+    if (h.num_comb > 0) {
+      rc = launch_combine(a, stream);
+      if (rc) return rc;
+    }
+  }
+  return AQP_OK;
+}

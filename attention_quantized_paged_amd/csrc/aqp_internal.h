@@ -1,0 +1,137 @@
+// Library-internal definitions shared by the host code and the HIP kernels:
+// cache geometry, schedule metadata layout and kernel launch entry points.
+//
+// The schedule records the element sizes and tile geometry it was built
+// with; the launcher compares them with what the compiled kernels use and
+// refuses a mismatch. This is the lesson of the "Fix CPU FP8 attention
+// scheduler scratch sizing" page (vllm PR 50194, Motivation and Review):
+// the scheduler sized tiles and scratch from one element size while the
+// runtime used another, and a large prefill wrote past its scratch buffer.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/aqp.h"
+
+namespace aqp {
+
+constexpr uint32_t kMagic = 0x53505141u;  // "AQPS"
+constexpr uint32_t kVersion = 1;
+
+// ---- compile-time tile geometry of the kernels ----------------------------
+constexpr int kTileKeys = 16;        // keys per KV tile: one 16-row MFMA operand; block_size % 16 == 0
+constexpr int kDecIterKeys = 32;     // keys per decode iteration (two tiles: one 32-deep PV MFMA)
+constexpr int kDecWaves = 4;         // waves per decode work-group (they split a segment's iterations)
+constexpr int kMaxHeadsPerUnit = 16; // q heads per MFMA column block
+constexpr int kPfRowsPerWave = 32;   // prefill: query rows (token, head) per wave
+constexpr int kPfWaves = 4;          // prefill: waves per work-group
+constexpr int kPfRows = kPfRowsPerWave * kPfWaves;  // query rows per prefill work item
+constexpr int kPfKvTile = 32;        // prefill: keys staged in LDS per step
+constexpr int kDefaultDecodeWGs = 1024;  // 256 CUs x 4 work-groups
+constexpr int kMinDecodeKeysPerWG = 512;
+
+// Geometry derived from the cache descriptor. One function computes it for
+// both the scheduler and the launcher.
+struct Geometry {
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t kv_elem_bytes;      // bytes per stored K/V element (1 for every supported dtype)
+  int32_t staged_elem_bytes;  // bytes per element as staged in LDS by the kernels
+  int32_t scale_bytes;        // inline scale bytes per row (4 per token-head, else 0)
+  int32_t pad_;
+  int64_t page_bytes;
+  int64_t block_bytes;
+  int64_t total_bytes;
+  int32_t dec_lds_bytes;      // LDS per decode work-group
+  int32_t pf_lds_bytes;       // LDS per prefill work-group
+};
+
+// Fills g; returns AQP_OK or an error status with *why set.
+int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why);
+
+// ---- schedule metadata -----------------------------------------------------
+// Layout: [SchedHeader][DecSeg x num_dec_segs][int32 dec_wg_start x (num_dec_wgs+1)]
+//         [CombItem x num_comb][PfItem x num_pf_items], each array 256-byte aligned.
+struct SchedHeader {
+  uint32_t magic, version;
+  // what the schedule was built for
+  int32_t dtype, mode, kv_elem_bytes, staged_elem_bytes, scale_bytes;
+  int32_t head_dim, block_size, num_blocks, num_q_heads, num_kv_heads;
+  int32_t causal, window, max_blocks_per_seq, num_seqs;
+  float sm_scale, softcap;
+  int32_t total_q_tokens;
+  // tile geometry the work items were cut with
+  int32_t tile_keys, dec_iter_keys, dec_waves, pf_rows, pf_kv_tile, heads_per_unit;
+  int32_t dec_lds_bytes, pf_lds_bytes;
+  // work
+  int32_t num_dec_wgs, num_dec_segs, num_parts, num_comb, num_pf_items, group_heads;
+  int64_t off_dec_segs, off_dec_wg_start, off_comb, off_pf_items;
+  int64_t meta_bytes, scratch_bytes;
+  int64_t page_bytes, block_bytes;
+  int64_t dec_kv_keys;  // total visible (key, KV head) pairs of the decode work (for reporting)
+};
+
+static_assert(offsetof(SchedHeader, off_dec_segs) == 136, "SchedHeader layout is part of the metadata format");
+static_assert(sizeof(SchedHeader) == 208, "SchedHeader layout is part of the metadata format");
+
+// Decode segment: keys [k_lo, k_hi) of (sequence, KV head, q heads
+// [head0, head0 + nheads) of that KV head's group), one query token.
+// part < 0: the segment is the whole visible range -> write the output;
+// otherwise write partial (m, l, O) slot `part` of the scratch.
+struct DecSeg {
+  int32_t seq, kvh, head0, nheads, k_lo, k_hi, q_tok, part;
+};
+
+// Merge of partial slots [first_part, first_part + num_parts) into the output
+// rows of q heads [head0, head0 + nheads) of KV head kvh, query token q_tok.
+struct CombItem {
+  int32_t kvh, head0, nheads, q_tok, first_part, num_parts, pad0, pad1;
+};
+
+// Prefill item: query tokens [q_lo, q_hi) (indices within the sequence) of
+// sequence seq, all G q heads of KV head kvh. The sequence has L keys and ql
+// queries; its first query is token q_start of q / out.
+struct PfItem {
+  int32_t seq, kvh, q_lo, q_hi, L, ql, q_start, k_hi_max;
+};
+
+// Scratch of a partial slot: nh = min(G, 16) heads x (D floats of O, then m, l).
+inline int64_t part_floats(int32_t group_heads, int32_t head_dim) {
+  return (int64_t)group_heads * (head_dim + 2);
+}
+
+// ---- kernel launchers (defined in the .hip files) ---------------------------
+struct CacheWriteArgs {
+  uint8_t* cache;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int64_t* slots;
+  int64_t num_tokens, token_stride;
+  int64_t page_bytes, block_bytes;
+  int64_t total_slots;
+  int32_t num_kv_heads, head_dim, block_size;
+  float k_scale, v_scale;
+};
+int launch_cache_write(int dtype, int mode, const CacheWriteArgs& a, void* stream);
+
+struct AttnArgs {
+  const uint8_t* cache;
+  const uint16_t* q;
+  const int32_t* block_tables;
+  const uint8_t* meta_dev;
+  float* scratch;
+  uint16_t* out;
+  int64_t page_bytes, block_bytes;
+  int32_t head_dim, block_size, num_kv_heads, num_q_heads, group, max_blocks_per_seq;
+  int32_t window, causal;
+  float sm_scale, softcap, k_scale, v_scale;
+  const SchedHeader* hdr;  // host copy
+};
+int launch_decode(int dtype, int mode, const AttnArgs& a, void* stream);
+int launch_combine(const AttnArgs& a, void* stream);
+int launch_prefill(int dtype, int mode, const AttnArgs& a, void* stream);
+
+void set_error(const char* fmt, ...);
+
+}  // namespace aqp

@@ -1,0 +1,185 @@
+/*
+ * aqp -- quantized paged attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the library (libaqp.so). Plain pointers and sizes only; every
+ * device buffer is allocated and owned by the caller; the library allocates no
+ * device memory and keeps no state beyond a per-thread last-error message.
+ *
+ * The operations follow three pages summarising vLLM pull requests:
+ *  [P39445] "CPU backend adds FP8 KV-cache quantisation" (PR 39445)
+ *  [P50194] "Fix CPU FP8 attention scheduler scratch sizing" (PR 50194)
+ *  [P38378] "Per-token-head INT8/FP8 KV quantisation for Triton" (PR 38378)
+ *
+ * Conventions shared by every entry point:
+ *  - Return value: an aqp_status; AQP_OK (0) or a negative code. On a
+ *    negative code aqp_last_error() describes the failure and nothing was
+ *    launched. There is no silent fallback to another precision or path: an
+ *    unsupported combination is an error ([P39445] Motivation and
+ *    Risk/Impact: the old silent downgrade to bf16 is what the pages remove).
+ *  - Device work is enqueued asynchronously on `stream` (a hipStream_t; NULL
+ *    is the default stream). Pointers named *_host are host memory; all other
+ *    array pointers are device memory.
+ *  - bf16 tensors are arrays of uint16 bit patterns.
+ */
+#ifndef AQP_H
+#define AQP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* KV cache element type. Indices 0..2 are the kv_cache_dtype indices of
+ * [P50194] Code excerpt (0 = auto, 1 = fp8_e4m3, 2 = fp8_e5m2); 3 adds int8
+ * for the per-token-head mode of [P38378]. */
+typedef enum {
+  AQP_KV_AUTO = 0,     /* unquantised cache: not supported by this build (AQP_ERR_UNSUPPORTED) */
+  AQP_KV_FP8_E4M3 = 1, /* OCP E4M3, finite-only ("fn"), largest code 448 */
+  AQP_KV_FP8_E5M2 = 2, /* OCP E5M2, largest finite code 57344 */
+  AQP_KV_INT8 = 3      /* two's-complement int8, codes in [-128, 127] */
+} aqp_kv_dtype;
+
+/* Scale granularity ([P38378] Implementation item 1: the quantisation-mode
+ * switch between per-tensor and per-token-head). */
+typedef enum {
+  AQP_SCALE_PER_TENSOR = 0,    /* one k_scale and one v_scale, passed by the caller */
+  AQP_SCALE_PER_TOKEN_HEAD = 1 /* one dynamic scale per (token, KV head), K and V apart, stored in the cache */
+} aqp_scale_mode;
+
+typedef enum {
+  AQP_OK = 0,
+  AQP_ERR_INVALID = -1,           /* null pointer, bad shape or value */
+  AQP_ERR_UNSUPPORTED = -2,       /* valid request this build does not implement */
+  AQP_ERR_SCHEDULE_MISMATCH = -3, /* schedule built for other parameters / element size */
+  AQP_ERR_SCRATCH_TOO_SMALL = -4, /* scratch smaller than the schedule requires */
+  AQP_ERR_HIP = -5                /* HIP runtime error (message has the HIP error string) */
+} aqp_status;
+
+/* Geometry of one paged KV cache allocation.
+ *
+ * Layout (the library's own; both the cache write and the attention kernels
+ * use it, and the tests' reader follows the same definition):
+ *  - num_blocks blocks, block b at byte b * block_bytes;
+ *  - block_bytes = 2 * num_kv_heads * page_bytes: the K pages of heads
+ *    0..Hkv-1, then the V pages;
+ *  - a page holds block_size rows of head_dim code bytes, token-major (row
+ *    = one token of one head), followed in per-token-head mode by block_size
+ *    fp32 scales (the scale of row r at page + block_size*head_dim + 4*r:
+ *    the inline scale storage of [P38378] Implementation item 2, kept at the
+ *    page tail so rows stay 16-byte aligned);
+ *  - page_bytes is that content rounded up to a multiple of 128 bytes;
+ *  - slot s is row (s % block_size) of block (s / block_size).
+ * Supported: head_dim in {64, 128, 256}; block_size a positive multiple of 16. */
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* aqp_kv_dtype */
+  int32_t mode;  /* aqp_scale_mode */
+} aqp_cache_desc;
+
+/* Attention parameters ([P50194] Code excerpt: the scheduler's num_heads_q,
+ * num_heads_kv, head_dim, causal, window_size; the harness's soft_cap). */
+typedef struct {
+  int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads; q head h reads KV head h / (Hq / Hkv) */
+  int32_t num_kv_heads;       /* must equal the cache's */
+  int32_t head_dim;           /* must equal the cache's */
+  int32_t causal;             /* 1: query i of a sequence with L keys and ql queries sits at position
+                                 L - ql + i and sees keys j <= that position; 0: sees all L keys */
+  int32_t window;             /* 0: none; W > 0: only keys j with position - j < W (needs causal = 1) */
+  int32_t max_blocks_per_seq; /* row stride of block_tables */
+  float sm_scale;             /* logit scale; 0 means 1/sqrt(head_dim) */
+  float softcap;              /* 0: none; c > 0: logit z -> c * tanh(z / c), applied after sm_scale */
+  int32_t decode_parallelism; /* waves the decode work is split across; 0 = default (4096) */
+  int32_t reserved;
+} aqp_attn_params;
+
+/* Parse a kv_cache_dtype string ([P50194] Code excerpt: parse_fp8_kv_dtype
+ * maps the string to the dtype index; [P38378] Risk/Impact names the
+ * per-token-head strings).
+ *   "fp8", "fp8_e4m3"       -> FP8_E4M3, PER_TENSOR
+ *   "fp8_e5m2"              -> FP8_E5M2, PER_TENSOR
+ *   "int8_per_token_head"   -> INT8,     PER_TOKEN_HEAD
+ *   "fp8_per_token_head"    -> FP8_E4M3, PER_TOKEN_HEAD
+ *   "auto"                  -> AUTO, PER_TENSOR, returns AQP_ERR_UNSUPPORTED
+ * Anything else: AQP_ERR_INVALID. Outputs are written only on AQP_OK (and for
+ * "auto"). */
+int aqp_parse_kv_dtype(const char* s, int32_t* dtype, int32_t* mode);
+
+/* Byte sizes of the cache layout described at aqp_cache_desc. Any output
+ * pointer may be NULL. Errors: INVALID / UNSUPPORTED for an unsupported
+ * geometry. */
+int aqp_cache_bytes(const aqp_cache_desc* desc, size_t* page_bytes, size_t* block_bytes, size_t* total_bytes);
+
+/* Quantise new keys and values into the paged cache (reshape-and-cache with
+ * quantisation: [P39445] Implementation items 1 and 3; [P38378]
+ * Implementation item 3).
+ *   k, v:          bf16 [num_tokens, Hkv, head_dim]; token t's head h starts at element
+ *                  t * token_stride + h * head_dim (token_stride >= Hkv * head_dim).
+ *   slot_mapping:  int64 [num_tokens]; slot < 0 means "do not store" (padding); slots
+ *                  must be distinct; a slot >= num_blocks * block_size is not stored either.
+ *   k_scale, v_scale: per-tensor mode only (ignored per token-head): dequantised
+ *                  value = code * scale.
+ * Per row (token, head, K or V), in fp32:
+ *   s    = per tensor: the given scale; per token-head: max_d |x_d| / qmax
+ *          (qmax = 448 for E4M3, 127 for INT8), stored inline;
+ *   inv  = (s == 0) ? 0 : 1 / s  (correctly rounded);
+ *   code = fp8: round-to-nearest-even of x_d * inv, saturated to the largest finite code;
+ *          int8: round-to-nearest-even, clamped to [-128, 127].
+ * Errors: INVALID (null pointers, negative sizes, stride too small), UNSUPPORTED
+ * (dtype/mode combination not built: per token-head needs INT8 or E4M3;
+ * per tensor needs E4M3 or E5M2), HIP. */
+int aqp_cache_write(const aqp_cache_desc* desc, void* cache, const void* k, const void* v, int64_t num_tokens,
+                    int64_t token_stride, const int64_t* slot_mapping, float k_scale, float v_scale, void* stream);
+
+/* Build the per-batch attention schedule on the host ([P50194]
+ * Implementation item 1 and Code excerpt: get_scheduler_metadata takes the
+ * sequence lengths, query start locations, heads, head_dim, causal and window
+ * flags and -- the fix -- the KV cache dtype, so that the tile geometry and the
+ * scratch size are derived from the real KV element size).
+ *   seq_lens_host:        int32 [num_seqs]: keys of each sequence (including its new tokens)
+ *   query_start_loc_host: int32 [num_seqs + 1]: query tokens of sequence b are
+ *                         [qsl[b], qsl[b+1]) of q / out; qsl[0] = 0; 0 <= ql <= L.
+ *   meta_host:            output buffer of *meta_bytes bytes; NULL = size query only.
+ *   meta_bytes:           in: capacity of meta_host; out: bytes needed/written.
+ *   scratch_bytes:        out: device scratch aqp_paged_attention needs with this schedule.
+ * Sequences with q_len == 1 become decode work, the others prefill work. The
+ * metadata is self-contained: it records the parameters and element sizes it
+ * was built for, the geometry, and every work item. The caller copies the
+ * meta_bytes bytes to device memory unchanged and passes both copies to
+ * aqp_paged_attention.
+ * Errors: INVALID, UNSUPPORTED. */
+int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_desc* desc, const int32_t* seq_lens_host,
+                     const int32_t* query_start_loc_host, int32_t num_seqs, void* meta_host, size_t* meta_bytes,
+                     size_t* scratch_bytes);
+
+/* Paged attention over the quantised cache with dequantisation fused into
+ * the QK^T and PV products and an online softmax ([P39445] Implementation
+ * item 2: the dequantise step inside the tile GEMMs, scale folding;
+ * [P38378] Implementation item 3: dequantisation of KV tiles inside the
+ * unified varlen attention).
+ *   q:            bf16 [T_q, Hq, head_dim] contiguous, T_q = qsl[num_seqs].
+ *   block_tables: int32 [num_seqs, max_blocks_per_seq]: physical block of each logical block.
+ *   meta_host / meta_dev: the same schedule bytes, in host and device memory.
+ *   k_scale, v_scale: per-tensor mode only.
+ *   scratch:      device buffer of at least the schedule's scratch_bytes (may be NULL if 0).
+ *   out:          bf16 [T_q, Hq, head_dim]; every row of every query token is written.
+ * Per query row: z_j = sm_scale * q . k_j (k_j dequantised), soft-capped if
+ * set, masked by causality and window; softmax over the visible keys; output
+ * = sum_j p_j v_j rounded to bf16.
+ * Errors: INVALID, SCHEDULE_MISMATCH (schedule built for another cache
+ * descriptor, dtype, element size or parameter set), SCRATCH_TOO_SMALL, HIP. */
+int aqp_paged_attention(const aqp_attn_params* params, const aqp_cache_desc* desc, const void* cache,
+                        const void* q, const int32_t* block_tables, const void* meta_host, const void* meta_dev,
+                        float k_scale, float v_scale, void* scratch, size_t scratch_bytes, void* out, void* stream);
+
+/* Message of the last non-OK status returned on this thread ("" if none). */
+const char* aqp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AQP_H */

@@ -1,0 +1,155 @@
+"""GPU parity: the HIP path through the C ABI against the oracle.
+
+Cache bytes and scales bit-exact; attention within max-abs 2e-2 and rel-RMS
+5e-3 of the oracle's fp64 result (rounded to bf16)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_common import Run, compare, say, to_dev, OFMT
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def aqp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_quantized_paged_amd as m
+    return m
+
+
+W = workloads
+
+# Small versions of every configuration: the oracle finishes them in seconds, they still
+# span several tiles, several KV splits and ragged tails.
+SMALL = [
+    W.CFG1,
+    W.scaled(W.CFG2, name="prefill_small_d256_bs2176", seqs=((200, 200), (77, 77), (129, 300)), num_blocks=6),
+    W.scaled(W.CFG3, name="decode_small_llama8b", seqs=((1, 700), (1, 33), (1, 1500), (1, 16), (1, 1)),
+             num_blocks=300),
+    W.scaled(W.CFG4, name="mixed_small_int8_pth", seqs=((1, 600), (1, 257)) + ((70, 310),), num_blocks=120),
+    W.scaled(W.CFG5A, name="longctx_small_e4m3_pth", seqs=((1, 2000), (1, 700)), window=500, num_blocks=200),
+    W.scaled(W.CFG5B, name="longctx_small_e5m2_pt", seqs=((1, 2000), (1, 700)), window=500, num_blocks=200),
+    # extra strength: small cap and window at prefill, short q lengths, G = 32 (two head groups), D = 64
+    W.Workload("prefill_cap5_w37_d128", "fp8_e4m3", ((17, 17), (2, 50), (9, 90), (33, 40)), 8, 2, 128, 32, 20,
+               window=37, softcap=5.0, seed=77),
+    W.Workload("mqa_g32_decode_pth", "fp8_per_token_head", ((1, 300), (1, 45), (5, 60)), 32, 1, 128, 16, 40, seed=78),
+    W.Workload("d64_int8_mixed", "int8_per_token_head", ((1, 100), (12, 12), (1, 3)), 8, 4, 64, 16, 20, seed=79),
+    W.Workload("d256_e5m2_decode", "fp8_e5m2", ((1, 333), (1, 1024)), 16, 2, 256, 64, 40, softcap=20.0, seed=80),
+    W.Workload("noncausal_prefill", "fp8_e4m3", ((40, 40), (7, 7)), 8, 2, 128, 16, 10, causal=False, seed=81),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_parity(aqp, w):
+    r = Run(w, torch, aqp, par=7)
+    r.cache_matches()
+    out = r.gpu_attention()
+    ref, rows = r.oracle_attention()
+    compare(out[rows], ref, w.name)
+
+
+@pytest.mark.parametrize("par", [1, 3, 64, 4096])
+def test_decode_split_counts(aqp, par):
+    """The same decode batch cut into 1 .. many work-groups gives the same result."""
+    w = W.scaled(W.CFG3, name=f"decode_split_{par}", seqs=((1, 3000), (1, 129), (1, 2047)), num_blocks=400)
+    r = Run(w, torch, aqp, par=par)
+    out = r.gpu_attention()
+    ref, rows = r.oracle_attention()
+    compare(out[rows], ref, w.name)
+
+
+def test_block_permutation_bit_identical(aqp):
+    """Same keys in a contiguous pool or a permuted one: bit-identical GPU output."""
+    w = W.scaled(W.CFG4, name="perm_a", seqs=((1, 500), (40, 200)), num_blocks=60)
+    r1 = Run(w, torch, aqp)
+    o1 = r1.gpu_attention()
+    b = r1.b
+    # remap every physical block through a permutation and rewrite the cache
+    perm = np.random.default_rng(5).permutation(w.num_blocks).astype(np.int32)
+    bt2 = np.where(b.block_tables >= 0, perm[np.maximum(b.block_tables, 0)], -1).astype(np.int32)
+    slots2 = perm[b.slots_hist // w.block_size].astype(np.int64) * w.block_size + b.slots_hist % w.block_size
+    r1.gcache.zero_()
+    aqp.cache_write(r1.desc, r1.gcache, to_dev(b.k_hist, torch), to_dev(b.v_hist, torch), to_dev(slots2, torch))
+    b.block_tables = bt2
+    o2 = r1.gpu_attention()
+    assert np.array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("dtype_str", ["fp8_e4m3", "fp8_e5m2", "int8_per_token_head", "fp8_per_token_head"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_cache_write_bit_exact(aqp, dtype_str, D):
+    """Random slots (some negative), a fused-QKV token stride, specials (zero rows, huge and tiny
+    values): GPU cache bytes equal the oracle's, starting from the same fill."""
+    rng = np.random.default_rng(D + len(dtype_str))
+    say(f"[case] cache_write {dtype_str} D={D}")
+    hkv, bs, nb, n = 3, 32, 12, 200
+    desc = aqp.cache_desc(nb, bs, hkv, D, dtype_str)
+    od = oracle.CacheDesc(nb, bs, hkv, D, OFMT[desc.dtype], desc.mode)
+    x = (rng.standard_normal((n, 3 * hkv, D)) * np.exp(rng.uniform(-8, 8, (n, 3 * hkv, 1)))).astype(np.float32)
+    x[0] = 0.0
+    x[1, :, 5] = -0.0
+    x[2, :, 7] = 1e30
+    x[3] *= 1e-30
+    qkv = workloads.bf16_round(x)  # [n, q|k|v heads, D]: k = heads hkv..2hkv, v = 2hkv..3hkv
+    k = np.ascontiguousarray(qkv[:, hkv:2 * hkv])
+    v = np.ascontiguousarray(qkv[:, 2 * hkv:])
+    slots = rng.permutation(nb * bs)[:n].astype(np.int64)
+    slots[::11] = -1
+    ks, vs = 0.37, 2.5e-3
+    ocache = np.full(od.total_bytes, 0x5A, np.uint8)
+    oracle.cache_write(od, ocache, k, v, slots, ks, vs)
+    g = torch.full((od.total_bytes,), 0x5A, dtype=torch.uint8, device="cuda")
+    dq = to_dev(qkv, torch)
+    # k and v as strided views of the fused tensor
+    kview = dq[:, hkv:2 * hkv]
+    vview = dq[:, 2 * hkv:]
+    aqp.cache_write(desc, g, kview, vview, to_dev(slots, torch), ks, vs, token_stride=3 * hkv * D)
+    torch.cuda.synchronize()
+    gh = g.cpu().numpy()
+    bad = np.nonzero(gh != ocache)[0]
+    assert bad.size == 0, f"{bad.size} bytes differ at {bad[:10]}"
+
+
+@pytest.mark.parametrize("dtype_str,scale", [("fp8_e4m3", 1.0), ("fp8_e4m3", 1 / 448.0), ("fp8_e4m3", 3.7),
+                                             ("fp8_e5m2", 1.0), ("fp8_e5m2", 1e-3), ("fp8_e5m2", 0.011)])
+def test_codec_every_bf16_pattern(aqp, dtype_str, scale):
+    """Every finite bf16 bit pattern through the cache write at a per-tensor scale: bit-exact
+    against the oracle's encoder (the hardware conversion's rounding, saturation and zero signs)."""
+    say(f"[case] codec grid {dtype_str} scale={scale}")
+    pats = np.arange(65536, dtype=np.uint32)
+    f = (pats << 16).view(np.float32)
+    pats = pats[np.isfinite(f)].astype(np.uint16)
+    D, hkv = 128, 1
+    n = (pats.size + D - 1) // D
+    pad = np.zeros(n * D, np.uint16)
+    pad[: pats.size] = pats
+    k = pad.reshape(n, hkv, D)
+    v = np.ascontiguousarray(k[::-1])
+    desc = aqp.cache_desc((n + 15) // 16, 16, hkv, D, dtype_str)
+    od = oracle.CacheDesc(desc.num_blocks, 16, hkv, D, OFMT[desc.dtype], desc.mode)
+    slots = np.arange(n, dtype=np.int64)
+    ocache = np.zeros(od.total_bytes, np.uint8)
+    oracle.cache_write(od, ocache, k, v, slots, scale, scale)
+    g = torch.zeros(od.total_bytes, dtype=torch.uint8, device="cuda")
+    aqp.cache_write(desc, g, to_dev(k, torch), to_dev(v, torch), to_dev(slots, torch), scale, scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy(), ocache)
+
+
+def test_empty_and_zero_query_batches(aqp):
+    desc = aqp.cache_desc(4, 16, 2, 64, "fp8_e4m3")
+    params = aqp.attn_params(4, 2, 64, 2)
+    s = aqp.get_schedule(params, desc, np.zeros(0, np.int32), np.zeros(1, np.int32))
+    assert s.header["num_dec_segs"] == 0 and s.header["num_pf_items"] == 0
+    cache = torch.zeros(aqp.cache_bytes(desc)[2], dtype=torch.uint8, device="cuda")
+    out = torch.zeros((1, 4, 64), dtype=torch.int16, device="cuda")
+    aqp.paged_attention(params, desc, cache, out, torch.zeros((1, 2), dtype=torch.int32, device="cuda"), s.meta,
+                        torch.from_numpy(s.meta).cuda(), 1.0, 1.0, None, 0, out)
+    # sequences with no queries produce no work
+    s2 = aqp.get_schedule(params, desc, np.array([20, 5], np.int32), np.array([0, 0, 0], np.int32))
+    assert s2.header["total_q_tokens"] == 0

@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI (no GPU): exported symbols, dtype parsing,
+layout sizes against the oracle's independent layout, and error paths that
+must fail before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import attention_quantized_paged_amd as aqp
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _declared_symbols():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(aqp_[a-z_0-9]+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_symbols()
+    assert declared >= {"aqp_cache_write", "aqp_get_schedule", "aqp_paged_attention", "aqp_parse_kv_dtype",
+                        "aqp_cache_bytes", "aqp_last_error"}
+    lib = ctypes.CDLL(aqp.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+
+
+def _golden_dtypes():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "kv_cache_dtypes.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            s, idx, mode = line.split()
+            rows.append((s, int(idx), {"per_tensor": 0, "per_token_head": 1}[mode]))
+    return rows
+
+
+@pytest.mark.parametrize("s,idx,mode", _golden_dtypes())
+def test_parse_kv_dtype_matches_pages(s, idx, mode):
+    if s == "auto":
+        with pytest.raises(aqp.AqpError) as e:
+            aqp.parse_kv_dtype(s)
+        assert e.value.status == aqp.ERR_UNSUPPORTED
+    else:
+        assert aqp.parse_kv_dtype(s) == (idx, mode)
+
+
+def test_parse_rejects_unknown():
+    with pytest.raises(aqp.AqpError) as e:
+        aqp.parse_kv_dtype("fp4")
+    assert e.value.status == aqp.ERR_INVALID
+    assert aqp.parse_kv_dtype("fp8") == (aqp.KV_FP8_E4M3, aqp.SCALE_PER_TENSOR)
+
+
+FMT = {aqp.KV_FP8_E4M3: oracle.FMT_E4M3, aqp.KV_FP8_E5M2: oracle.FMT_E5M2, aqp.KV_INT8: oracle.FMT_INT8}
+
+
+@pytest.mark.parametrize("dtype_str", ["fp8_e4m3", "fp8_e5m2", "int8_per_token_head", "fp8_per_token_head"])
+@pytest.mark.parametrize("nb,bs,h,d", [(8, 16, 2, 64), (4, 2176, 2, 256), (40000, 16, 8, 128), (3, 32, 3, 128)])
+def test_cache_bytes_match_oracle_layout(dtype_str, nb, bs, h, d):
+    desc = aqp.cache_desc(nb, bs, h, d, dtype_str)
+    pb, bb, tb = aqp.cache_bytes(desc)
+    od = oracle.CacheDesc(nb, bs, h, d, FMT[desc.dtype], desc.mode)
+    assert (pb, bb, tb) == (od.page_bytes, od.block_bytes, od.total_bytes)
+
+
+@pytest.mark.parametrize("bad", [dict(head_dim=96), dict(block_size=8), dict(block_size=1), dict(num_kv_heads=0)])
+def test_unsupported_geometry(bad):
+    kw = dict(num_blocks=4, block_size=16, num_kv_heads=2, head_dim=64)
+    kw.update(bad)
+    desc = aqp.CacheDesc(kw["num_blocks"], kw["block_size"], kw["num_kv_heads"], kw["head_dim"], aqp.KV_FP8_E4M3, 0)
+    with pytest.raises(aqp.AqpError) as e:
+        aqp.cache_bytes(desc)
+    assert e.value.status in (aqp.ERR_UNSUPPORTED, aqp.ERR_INVALID)
+
+
+@pytest.mark.parametrize("dt,md", [(aqp.KV_INT8, 0), (aqp.KV_FP8_E5M2, 1), (aqp.KV_AUTO, 0)])
+def test_unbuilt_dtype_mode_pairs_are_errors(dt, md):
+    with pytest.raises(aqp.AqpError) as e:
+        aqp.cache_bytes(aqp.CacheDesc(4, 16, 2, 64, dt, md))
+    assert e.value.status == aqp.ERR_UNSUPPORTED
+
+
+def test_cache_write_argument_errors():
+    desc = aqp.cache_desc(4, 16, 2, 64, "fp8_e4m3")
+    with pytest.raises(aqp.AqpError) as e:  # null pointers
+        aqp._check(aqp._lib.aqp_cache_write(ctypes.byref(desc), None, None, None, 5, 128, None, 1.0, 1.0, None))
+    assert e.value.status == aqp.ERR_INVALID
+    with pytest.raises(aqp.AqpError) as e:  # stride smaller than a token
+        aqp._check(aqp._lib.aqp_cache_write(ctypes.byref(desc), 16, 16, 16, 5, 64, 16, 1.0, 1.0, None))
+    assert e.value.status == aqp.ERR_INVALID
+    with pytest.raises(aqp.AqpError) as e:  # negative per-tensor scale
+        aqp._check(aqp._lib.aqp_cache_write(ctypes.byref(desc), 16, 16, 16, 5, 128, 16, -1.0, 1.0, None))
+    assert e.value.status == aqp.ERR_INVALID
+    # zero tokens: nothing to do, no device touched
+    aqp._check(aqp._lib.aqp_cache_write(ctypes.byref(desc), None, None, None, 0, 128, None, 1.0, 1.0, None))

@@ -1,0 +1,188 @@
+"""Schedule invariants (host only): every visible (query, q head, key) is
+covered exactly once; split ranges tile the visible range; the scratch size
+matches the partial slots; the header records the element sizes and
+geometry; a schedule built for one cache/parameter set is refused for another
+(the scheduler/runtime sizing disagreement of the PR 50194 page)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import attention_quantized_paged_amd as aqp
+import workloads
+
+SEG = np.dtype([(n, "<i4") for n in "seq kvh head0 nheads k_lo k_hi q_tok part".split()])
+COMB = np.dtype([(n, "<i4") for n in "kvh head0 nheads q_tok first_part num_parts pad0 pad1".split()])
+PF = np.dtype([(n, "<i4") for n in "seq kvh q_lo q_hi L ql q_start k_hi_max".split()])
+
+
+def _arrays(s):
+    h, m = s.header, s.meta
+    segs = m[h["off_dec_segs"]: h["off_dec_segs"] + 32 * h["num_dec_segs"]].view(SEG)
+    wgs = m[h["off_dec_wg_start"]: h["off_dec_wg_start"] + 4 * (h["num_dec_wgs"] + 1)].view(np.int32)
+    comb = m[h["off_comb"]: h["off_comb"] + 32 * h["num_comb"]].view(COMB)
+    pf = m[h["off_pf_items"]: h["off_pf_items"] + 32 * h["num_pf_items"]].view(PF)
+    return segs, wgs, comb, pf
+
+
+def _sched(seqs, hq, hkv, d, bs, dtype="fp8_e4m3", window=0, causal=True, par=0, nb=None):
+    sl = np.array([L for _, L in seqs], np.int32)
+    qsl = np.concatenate([[0], np.cumsum([q for q, _ in seqs])]).astype(np.int32)
+    mb = int(max(1, max((L + bs - 1) // bs for L in sl)))
+    desc = aqp.cache_desc(nb or 4 * mb * len(seqs), bs, hkv, d, dtype)
+    params = aqp.attn_params(hq, hkv, d, mb, causal=causal, window=window, decode_parallelism=par)
+    return aqp.get_schedule(params, desc, sl, qsl), sl, qsl, params, desc
+
+
+CASES = [
+    (((1, 17), (1, 40)), 4, 2, 64, 16, 0, 0),
+    (((1, 1000), (1, 33), (5, 70), (1, 16), (0, 9), (1, 1)), 8, 2, 128, 16, 0, 3),
+    (((1, 5000),) * 3 + ((64, 300),), 32, 1, 128, 32, 700, 7),  # G = 32 > 16: two head groups
+    (workloads.CFG3.seqs, 32, 8, 128, 16, 0, 0),
+    (workloads.CFG4.seqs, 32, 8, 128, 16, 0, 0),
+    (workloads.CFG5A.seqs, 64, 8, 128, 16, 4096, 0),
+    (workloads.CFG2.seqs, 16, 2, 256, 2176, 0, 0),
+]
+
+
+@pytest.mark.parametrize("seqs,hq,hkv,d,bs,window,par", CASES)
+def test_decode_coverage_exact(seqs, hq, hkv, d, bs, window, par):
+    s, sl, qsl, params, desc = _sched(seqs, hq, hkv, d, bs, window=window, par=par)
+    h = s.header
+    segs, wgs, comb, pf = _arrays(s)
+    G = hq // hkv
+    assert h["kv_elem_bytes"] == 1 and h["head_dim"] == d and h["block_size"] == bs
+    assert wgs[0] == 0 and wgs[-1] == len(segs) and np.all(np.diff(wgs) >= 0)
+    # coverage: for each decode (seq, kvh, head) the union of segment ranges is the visible range, disjoint
+    cover = {}
+    for sg in segs:
+        assert sg["k_lo"] < sg["k_hi"]
+        for hh in range(sg["head0"], sg["head0"] + sg["nheads"]):
+            cover.setdefault((sg["seq"], sg["kvh"], hh), []).append((sg["k_lo"], sg["k_hi"], sg["part"]))
+    expect = set()
+    for b, (ql, L) in enumerate(seqs):
+        if ql != 1:
+            continue
+        lo = max(0, L - window) if window else 0
+        for kvh in range(hkv):
+            for hh in range(G):
+                key = (b, kvh, hh)
+                expect.add(key)
+                rs = sorted(cover[key])
+                assert rs[0][0] == lo and rs[-1][1] == L
+                assert all(rs[i][1] == rs[i + 1][0] for i in range(len(rs) - 1))
+                if len(rs) == 1:
+                    assert rs[0][2] == -1
+                else:
+                    assert all(r[2] >= 0 for r in rs)
+    assert set(cover) == expect
+    # partial slots: each used exactly once and named by exactly one merge item
+    parts = sorted(sg["part"] for sg in segs if sg["part"] >= 0)
+    assert parts == list(range(h["num_parts"]))
+    from_comb = sorted(p for c in comb for p in range(c["first_part"], c["first_part"] + c["num_parts"]))
+    assert from_comb == parts
+    assert h["scratch_bytes"] == h["num_parts"] * min(G, 16) * (d + 2) * 4 == s.scratch_bytes
+    # balance: work-groups get equal numbers of 16-key tiles (the last may get fewer)
+    if len(segs):
+        tiles = []
+        for w in range(h["num_dec_wgs"]):
+            t = 0
+            for sg in segs[wgs[w]: wgs[w + 1]]:
+                t += (sg["k_hi"] - 1) // 16 - sg["k_lo"] // 16 + 1
+            tiles.append(t // max(1, (G + 15) // 16 if False else 1))
+        assert len(tiles) == h["num_dec_wgs"] and min(tiles) > 0
+
+
+@pytest.mark.parametrize("seqs,hq,hkv,d,bs,window,par", CASES)
+def test_prefill_coverage_and_order(seqs, hq, hkv, d, bs, window, par):
+    s, sl, qsl, params, desc = _sched(seqs, hq, hkv, d, bs, window=window, par=par)
+    _, _, _, pf = _arrays(s)
+    G = hq // hkv
+    seen = {}
+    for it in pf:
+        assert 0 <= it["q_lo"] < it["q_hi"] <= it["ql"]
+        assert (it["q_hi"] - it["q_lo"]) * G <= 128
+        for t in range(it["q_lo"], it["q_hi"]):
+            key = (it["seq"], it["kvh"], t)
+            assert key not in seen
+            seen[key] = 1
+        assert it["k_hi_max"] == it["L"] - it["ql"] + it["q_hi"]
+    expect = {(b, k, t) for b, (ql, L) in enumerate(seqs) if ql > 1 for k in range(hkv) for t in range(ql)}
+    assert set(seen) == expect
+    work = [it["k_hi_max"] - (max(0, it["L"] - it["ql"] + it["q_lo"] - window + 1) if window else 0) for it in pf]
+    assert work == sorted(work, reverse=True)
+
+
+def test_schedule_records_element_sizes_and_is_checked():
+    s, sl, qsl, params, desc = _sched(((1, 40), (8, 20)), 4, 2, 64, 16)
+    h = s.header
+    assert (h["magic"], h["kv_elem_bytes"], h["staged_elem_bytes"], h["scale_bytes"]) == (0x53505141, 1, 1, 0)
+    assert h["dtype"] == aqp.KV_FP8_E4M3 and h["mode"] == aqp.SCALE_PER_TENSOR
+
+    def call(p, d, meta, scratch_bytes=1 << 20):
+        return aqp._lib.aqp_paged_attention(ctypes.byref(p), ctypes.byref(d), 16, 16, 16, meta.ctypes.data, 16,
+                                            1.0, 1.0, 16, scratch_bytes, 16, None)
+
+    # built for e4m3 per tensor, used with a per-token-head cache: refused before any launch
+    d2 = aqp.cache_desc(desc.num_blocks, 16, 2, 64, "fp8_per_token_head")
+    assert call(params, d2, s.meta) == aqp.ERR_SCHEDULE_MISMATCH
+    d3 = aqp.cache_desc(desc.num_blocks, 16, 2, 64, "fp8_e5m2")
+    assert call(params, d3, s.meta) == aqp.ERR_SCHEDULE_MISMATCH
+    d4 = aqp.cache_desc(desc.num_blocks, 32, 2, 64, "fp8_e4m3")
+    assert call(params, d4, s.meta) == aqp.ERR_SCHEDULE_MISMATCH
+    p2 = aqp.attn_params(4, 2, 64, params.max_blocks_per_seq, window=8)
+    assert call(p2, desc, s.meta) == aqp.ERR_SCHEDULE_MISMATCH
+    p3 = aqp.attn_params(4, 2, 64, params.max_blocks_per_seq, softcap=30.0)
+    assert call(p3, desc, s.meta) == aqp.ERR_SCHEDULE_MISMATCH
+    bad = s.meta.copy()
+    bad[:4] = 0
+    assert call(params, desc, bad) == aqp.ERR_SCHEDULE_MISMATCH
+    # a tampered element size in the header is refused
+    bad = s.meta.copy()
+    bad[16:20] = np.array([2], np.int32).view(np.uint8)  # kv_elem_bytes
+    assert call(params, desc, bad) == aqp.ERR_SCHEDULE_MISMATCH
+    assert "element size" in aqp.last_error()
+
+
+def test_scratch_too_small_is_refused():
+    s, sl, qsl, params, desc = _sched(((1, 9000), (1, 5000)), 8, 2, 128, 16)
+    assert s.scratch_bytes > 0
+    rc = aqp._lib.aqp_paged_attention(ctypes.byref(params), ctypes.byref(desc), 16, 16, 16, s.meta.ctypes.data, 16,
+                                      1.0, 1.0, 16, s.scratch_bytes - 4, 16, None)
+    assert rc == aqp.ERR_SCRATCH_TOO_SMALL
+
+
+@pytest.mark.parametrize("seqs,err", [(((2, 1),), aqp.ERR_INVALID), (((-1, 5),), aqp.ERR_INVALID)])
+def test_bad_lengths(seqs, err):
+    sl = np.array([L for _, L in seqs], np.int32)
+    qsl = np.concatenate([[0], np.cumsum([q for q, _ in seqs])]).astype(np.int32)
+    desc = aqp.cache_desc(8, 16, 2, 64, "fp8_e4m3")
+    with pytest.raises(aqp.AqpError) as e:
+        aqp.get_schedule(aqp.attn_params(4, 2, 64, 4), desc, sl, qsl)
+    assert e.value.status == err
+
+
+def test_param_errors():
+    desc = aqp.cache_desc(8, 16, 2, 64, "fp8_e4m3")
+    sl, qsl = np.array([10], np.int32), np.array([0, 1], np.int32)
+    for p, err in [(aqp.attn_params(3, 2, 64, 4), aqp.ERR_INVALID),
+                   (aqp.attn_params(4, 2, 128, 4), aqp.ERR_INVALID),
+                   (aqp.attn_params(4, 2, 64, 4, causal=False, window=4), aqp.ERR_UNSUPPORTED),
+                   (aqp.attn_params(4, 2, 64, 0), aqp.ERR_INVALID),
+                   (aqp.attn_params(4, 2, 64, 4, softcap=-1.0), aqp.ERR_INVALID)]:
+        with pytest.raises(aqp.AqpError) as e:
+            aqp.get_schedule(p, desc, sl, qsl)
+        assert e.value.status == err
+    # too few block-table columns for the sequence
+    with pytest.raises(aqp.AqpError):
+        aqp.get_schedule(aqp.attn_params(4, 2, 64, 0 + 1), desc, np.array([40], np.int32), qsl)
+
+
+def test_large_block_size_geometry_is_consistent():
+    """Block size 2176 with head_dim 256 (the page's large-prefill regression shape): the LDS the
+    schedule sizes equals what the kernels' tiles need, from the 1-byte element size."""
+    s, *_ = _sched(((1024, 1024),) * 4, 16, 2, 256, 2176)
+    h = s.header
+    assert h["pf_kv_tile"] == 32 and h["staged_elem_bytes"] == 1
+    assert h["pf_lds_bytes"] == 2 * (2 * 32 * 256 * 1 + 2 * 32 * 4)
+    assert h["dec_lds_bytes"] == max(4 * 32 * 256, 3 * 16 * (256 + 2) * 4)
