@@ -12,7 +12,6 @@ from __future__ import annotations
 
 import ctypes
 import os
-from dataclasses import dataclass
 from typing import Optional, Tuple
 
 import numpy as np
@@ -137,11 +136,20 @@ def cache_write(desc: CacheDesc, cache, k, v, slot_mapping, k_scale: float = 1.0
                                 _ptr(slot_mapping), float(k_scale), float(v_scale), _stream(stream)))
 
 
-@dataclass
 class Schedule:
-    meta: np.ndarray      # host bytes
-    scratch_bytes: int
-    header: dict
+    """Host bytes of a schedule (``meta``; may be a view of a caller buffer), its scratch size,
+    and its header fields (parsed on first use)."""
+
+    def __init__(self, meta: np.ndarray, scratch_bytes: int):
+        self.meta = meta
+        self.scratch_bytes = scratch_bytes
+        self._header = None
+
+    @property
+    def header(self) -> dict:
+        if self._header is None:
+            self._header = parse_header(self.meta)
+        return self._header
 
 
 _HDR_FIELDS = ("magic version dtype mode kv_elem_bytes staged_elem_bytes scale_bytes head_dim block_size num_blocks "
@@ -169,19 +177,33 @@ def parse_header(meta: np.ndarray) -> dict:
     return out
 
 
-def get_schedule(params: AttnParams, desc: CacheDesc, seq_lens, query_start_loc) -> Schedule:
-    """seq_lens, query_start_loc: host int32 arrays (numpy or CPU tensors)."""
-    sl = np.ascontiguousarray(np.asarray(seq_lens), dtype=np.int32)
-    qsl = np.ascontiguousarray(np.asarray(query_start_loc), dtype=np.int32)
+def get_schedule(params: AttnParams, desc: CacheDesc, seq_lens, query_start_loc,
+                 out: Optional[np.ndarray] = None) -> Schedule:
+    """seq_lens, query_start_loc: host int32 arrays. With ``out`` (a uint8 host buffer, e.g. the
+    numpy view of a pinned tensor) the schedule is written there in one call when it fits."""
+    sl = seq_lens if (isinstance(seq_lens, np.ndarray) and seq_lens.dtype == np.int32 and
+                      seq_lens.flags["C_CONTIGUOUS"]) else np.ascontiguousarray(np.asarray(seq_lens), dtype=np.int32)
+    qsl = query_start_loc if (isinstance(query_start_loc, np.ndarray) and query_start_loc.dtype == np.int32 and
+                              query_start_loc.flags["C_CONTIGUOUS"]) else \
+        np.ascontiguousarray(np.asarray(query_start_loc), dtype=np.int32)
     if qsl.shape[0] != sl.shape[0] + 1:
         raise ValueError("query_start_loc must have num_seqs + 1 entries")
-    nbytes, scratch = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    scratch = ctypes.c_size_t(0)
+    if out is not None:
+        nbytes = ctypes.c_size_t(out.size)
+        rc = _lib.aqp_get_schedule(ctypes.byref(params), ctypes.byref(desc), sl.ctypes.data, qsl.ctypes.data,
+                                   sl.shape[0], out.ctypes.data, ctypes.byref(nbytes), ctypes.byref(scratch))
+        if rc == OK:
+            return Schedule(out[: nbytes.value], scratch.value)
+        if nbytes.value <= out.size:
+            _check(rc)
+    nbytes = ctypes.c_size_t(0)
     _check(_lib.aqp_get_schedule(ctypes.byref(params), ctypes.byref(desc), sl.ctypes.data, qsl.ctypes.data,
                                  sl.shape[0], None, ctypes.byref(nbytes), ctypes.byref(scratch)))
     meta = np.zeros(nbytes.value, dtype=np.uint8)
     _check(_lib.aqp_get_schedule(ctypes.byref(params), ctypes.byref(desc), sl.ctypes.data, qsl.ctypes.data,
                                  sl.shape[0], meta.ctypes.data, ctypes.byref(nbytes), ctypes.byref(scratch)))
-    return Schedule(meta, scratch.value, parse_header(meta))
+    return Schedule(meta, scratch.value)
 
 
 def paged_attention(params: AttnParams, desc: CacheDesc, cache, q, block_tables, meta_host, meta_dev,

@@ -66,12 +66,25 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
   g->total_bytes = (int64_t)d.num_blocks * g->block_bytes;
   // Decode work-group: each wave stages one iteration of V codes; at the end
   // waves 1..3 hand their (O, m, l) for up to 16 heads to wave 0.
-  const int32_t dec_stage = kDecWaves * kDecIterKeys * d.head_dim * g->staged_elem_bytes;
+  const int32_t dec_stage = kDecWaves * kDecIterKeys * (d.head_dim * g->staged_elem_bytes + kDecVRowPad);
   const int32_t dec_merge = (kDecWaves - 1) * kMaxHeadsPerUnit * (d.head_dim + 2) * 4;
   g->dec_lds_bytes = std::max(dec_stage, dec_merge);
   // Prefill work-group: double-buffered K and V tiles of codes plus their row scales.
   g->pf_lds_bytes = 2 * (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes + 2 * kPfKvTile * 4);
   return AQP_OK;
+}
+
+int device_cu_count() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cached = n;
+    else
+      cached = 256;
+    (void)hipGetLastError();
+  }
+  return cached;
 }
 
 }  // namespace aqp
@@ -197,7 +210,18 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   // ---- decode: units (sequence, KV head, head group) over their visible keys,
   // cut into equal runs of 16-key tiles, one run per work-group.
   struct Unit { int32_t seq, kvh, head0, nheads, lo, hi, q_tok; int64_t t0, ntiles; };
-  std::vector<Unit> units;
+  // per-thread work buffers, reused across calls (the schedule is rebuilt every batch)
+  static thread_local std::vector<Unit> units;
+  static thread_local std::vector<DecSeg> segs;
+  static thread_local std::vector<int32_t> wg_start;
+  static thread_local std::vector<CombItem> comb;
+  static thread_local std::vector<PfItem> pf;
+  static thread_local std::vector<int32_t> unit_nseg, unit_first_part;
+  units.clear();
+  segs.clear();
+  wg_start.clear();
+  comb.clear();
+  pf.clear();
   const int32_t hpu = std::min<int32_t>(G, kMaxHeadsPerUnit);
   int64_t total_tiles = 0, dec_keys = 0;
   for (int32_t b = 0; b < num_seqs; ++b) {
@@ -215,20 +239,18 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
       }
     }
   }
-  std::vector<DecSeg> segs;
-  std::vector<int32_t> wg_start;
-  std::vector<CombItem> comb;
   int32_t num_parts = 0;
   int32_t num_wgs = 0;
   if (total_tiles > 0) {
-    const int64_t target = p.decode_parallelism > 0 ? p.decode_parallelism : kDefaultDecodeWGs;
+    const int64_t target = p.decode_parallelism > 0 ? p.decode_parallelism
+                                                    : (int64_t)device_cu_count() * decode_wgs_per_cu(desc->head_dim);
     const int64_t by_size = (total_tiles * kTileKeys + kMinDecodeKeysPerWG - 1) / kMinDecodeKeysPerWG;
     int64_t P = std::max<int64_t>(1, std::min(target, by_size));
     const int64_t per = (total_tiles + P - 1) / P;
     P = (total_tiles + per - 1) / per;
     num_wgs = (int32_t)P;
     // first pass: count segments per unit to know which units are split
-    std::vector<int32_t> unit_nseg(units.size(), 0);
+    unit_nseg.assign(units.size(), 0);
     {
       int64_t base = 0;
       for (size_t u = 0; u < units.size(); ++u) {
@@ -237,7 +259,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
         base = e;
       }
     }
-    std::vector<int32_t> unit_first_part(units.size(), -1);
+    unit_first_part.assign(units.size(), -1);
     for (size_t u = 0; u < units.size(); ++u) {
       if (unit_nseg[u] > 1) {
         unit_first_part[u] = num_parts;
@@ -279,7 +301,6 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
 
   // ---- prefill items: (sequence, KV head, run of query tokens), all G heads of
   // the KV head in one item; heaviest (most keys) first.
-  std::vector<PfItem> pf;
   const int32_t tpi = std::max<int32_t>(1, kPfRows / G);
   for (int32_t b = 0; b < num_seqs; ++b) {
     const int32_t L = seq_lens[b], ql = qsl[b + 1] - qsl[b];
@@ -290,7 +311,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
       for (int32_t h = 0; h < p.num_kv_heads; ++h) pf.push_back({b, h, q0, q1, L, ql, qsl[b], khi});
     }
   }
-  std::stable_sort(pf.begin(), pf.end(), [&](const PfItem& x, const PfItem& y) {
+  if (pf.size() > 1) std::stable_sort(pf.begin(), pf.end(), [&](const PfItem& x, const PfItem& y) {
     auto work = [&](const PfItem& it) {
       const int32_t first = it.L - it.ql + it.q_lo;
       const int32_t lo = (p.window > 0 && first - p.window + 1 > 0) ? first - p.window + 1 : 0;
@@ -320,7 +341,13 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   }
   *meta_bytes = (size_t)need;
   uint8_t* m = (uint8_t*)meta_host;
-  std::memset(m, 0, (size_t)need);
+  // zero only the alignment gaps; every array byte is written below
+  auto zero_gap = [&](int64_t from, int64_t to) { if (to > from) std::memset(m + from, 0, (size_t)(to - from)); };
+  zero_gap(sizeof(SchedHeader), off_segs);
+  zero_gap(off_segs + (int64_t)segs.size() * (int64_t)sizeof(DecSeg), off_wgs);
+  zero_gap(off_wgs + (int64_t)wg_start.size() * 4, off_comb);
+  zero_gap(off_comb + (int64_t)comb.size() * (int64_t)sizeof(CombItem), off_pf);
+  zero_gap(off_pf + (int64_t)pf.size() * (int64_t)sizeof(PfItem), need);
   SchedHeader h;
   std::memset(&h, 0, sizeof h);
   h.magic = kMagic;

@@ -21,15 +21,21 @@ constexpr uint32_t kVersion = 1;
 
 // ---- compile-time tile geometry of the kernels ----------------------------
 constexpr int kTileKeys = 16;        // keys per KV tile: one 16-row MFMA operand; block_size % 16 == 0
-constexpr int kDecIterKeys = 32;     // keys per decode iteration (two tiles: one 32-deep PV MFMA)
+constexpr int kDecIterKeys = 16;     // keys per decode iteration (one tile; PV on 16x16x16 MFMA)
+constexpr int kDecVRowPad = 32;      // bytes of padding per staged V row (spreads transposed LDS reads over banks)
 constexpr int kDecWaves = 4;         // waves per decode work-group (they split a segment's iterations)
 constexpr int kMaxHeadsPerUnit = 16; // q heads per MFMA column block
 constexpr int kPfRowsPerWave = 32;   // prefill: query rows (token, head) per wave
 constexpr int kPfWaves = 4;          // prefill: waves per work-group
 constexpr int kPfRows = kPfRowsPerWave * kPfWaves;  // query rows per prefill work item
 constexpr int kPfKvTile = 32;        // prefill: keys staged in LDS per step
-constexpr int kDefaultDecodeWGs = 1024;  // 256 CUs x 4 work-groups
 constexpr int kMinDecodeKeysPerWG = 512;
+// Decode work-groups resident per CU for each head_dim (registers of the
+// compiled kernel: 3, 3 and 2 waves per SIMD). The default decode split uses
+// exactly one resident wave of equal work-groups.
+constexpr int decode_wgs_per_cu(int head_dim) { return head_dim <= 128 ? 3 : 2; }
+// Compute units of the current device (256 on MI355X; 256 when no device is visible).
+int device_cu_count();
 
 // Geometry derived from the cache descriptor. One function computes it for
 // both the scheduler and the launcher.

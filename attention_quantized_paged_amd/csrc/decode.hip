@@ -11,7 +11,7 @@
 //
 // gfx950 mapping, per work-group of 4 waves and per schedule segment
 // (keys [k_lo, k_hi) of one (sequence, KV head, group of <= 16 q heads)):
-//  * a wave takes 32-key iterations w, w+4, ... of the segment;
+//  * a wave takes 16-key tiles w, w+4, ... of the segment;
 //  * K: each lane loads D/4 contiguous code bytes of one key straight from HBM
 //    (16 keys x D bytes of a page per tile); the codes are widened to bf16 in
 //    registers and fed to v_mfma_f32_16x16x32_bf16 as S^T = K * Q^T with the
@@ -21,13 +21,20 @@
 //    its logit and each value's scale its probability;
 //  * softmax: running max / sum in the exp2 domain, the max reduced across the
 //    four lanes that share a head with two xor shuffles;
-//  * V: the two 16-key tiles of codes are staged in the wave's own LDS buffer
-//    and read back with ds_read_b64_tr_b8, which hands each lane 8 keys of one
-//    head-dim column: exactly the key-contiguous operand O^T = V^T * P^T needs,
-//    so the probabilities stay in the registers the QK^T product left them in;
+//  * V: the tile's codes are staged in the wave's own LDS buffer and read back
+//    with ds_read_b64_tr_b8, which hands each lane 4 keys of one head-dim column
+//    for two column tiles at once: the key-contiguous operand that
+//    O^T = V^T * P^T on v_mfma_f32_16x16x16_bf16 needs, so the probabilities
+//    stay in the registers the QK^T product left them in;
 //  * the four waves' (m, l, O) are merged in LDS; the result is either the
 //    output row (bf16) or a partial slot for the split-KV merge kernel.
 #include "device_common.h"
+
+// Decode waves per SIMD the register allocation targets for head_dim <= 128
+// (head_dim 256 targets 2).
+#ifndef AQP_DECODE_WAVES_PER_EU
+#define AQP_DECODE_WAVES_PER_EU 3
+#endif
 
 namespace aqp {
 
@@ -47,26 +54,41 @@ struct DecArgs {
 };
 
 template <int D, int MODE>
-struct IterRegs {
+struct TileRegs {
   static constexpr int KV4 = D / 64;  // uint4 per lane per 16-key tile (D/4 bytes)
-  uint4 ka[KV4], kb[KV4];             // K codes: tile A / tile B, one key row slice per lane
-  uint4 va[KV4], vb[KV4];             // V codes: tile A / tile B, coalesced slices
-  float4 ksa, ksb, vsa, vsb;          // per token-head scales of the lane's 4 keys in each tile
-  bool oka, okb;                      // tile lies in a block the table maps to a valid block id
+  uint4 k[KV4];                       // K codes: one key row slice per lane (MFMA A layout)
+  uint4 v[KV4];                       // V codes: coalesced slices of the tile
+  float4 ks, vs;                      // per token-head scales of the lane's 4 keys
+  bool ok;                            // the tile's block id is inside the pool
 };
 
 template <int D, int DT, int MODE>
-__global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? AQP_DECODE_WAVES_PER_EU : 2))) void decode_kernel(DecArgs a) {
   constexpr int KV4 = D / 64;
   constexpr int NT = D / 16;   // 16-wide head-dim tiles of the output
   constexpr int QS = D / 32;   // 32-deep MFMA steps of QK^T
+  constexpr int VROW = D + kDecVRowPad;  // staged V row stride in LDS
+  constexpr int STEP = kDecWaves * kDecIterKeys;  // keys between a wave's consecutive tiles
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
   const int kg = lane >> 4;
-  uint8_t* vbuf = smem + wave * (kDecIterKeys * D);
+  uint8_t* vbuf = smem + wave * (kDecIterKeys * VROW);
+  // where this lane's V chunks go in the padded staging rows
+  int vdst[KV4];
+#pragma unroll
+  for (int c = 0; c < KV4; ++c) {
+    const int o = lane * 16 + c * 1024;
+    vdst[c] = (o / D) * VROW + (o % D);
+  }
+  // transposed-read address of this lane: rows i = 0..3 and 4..7 are keys 4kg + (i & 3), the
+  // second four 16 columns further, so one read yields the operands of two head-dim tiles
+  const int tr_i = r16 >> 1;
+  const int tr_off = (4 * kg + (tr_i & 3)) * VROW + (tr_i >> 2) * 16 + (r16 & 1) * 8;
   const int s_begin = a.wg_start[blockIdx.x], s_end = a.wg_start[blockIdx.x + 1];
+  // without a soft-cap, log2(e) folds into the logit scale
+  const float xscale = a.softcap > 0.0f ? a.logit_scale : a.logit_scale * kLog2e;
 
   for (int si = s_begin; si < s_end; ++si) {
     const DecSeg sg = a.segs[si];
@@ -90,134 +112,133 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
     const int it_base = (sg.k_lo / kTileKeys) * kTileKeys;
     const int n_iter = (sg.k_hi - it_base + kDecIterKeys - 1) / kDecIterKeys;
 
-    float m = -INFINITY;  // running max (log2 domain) of this lane's head
-    float l = 0.0f;       // running sum of this lane's keys
+    float m = -INFINITY;  // reference max (log2 domain) of this lane's head
+    float l = 0.0f;       // sum of this lane's probabilities relative to m
     f32x4 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto load = [&](IterRegs<D, MODE>& R, int it) {
-      const int kA = it_base + it * kDecIterKeys;
-      const int kB = kA + kTileKeys;
-      const bool bok = kB < sg.k_hi;
-      int32_t blkA = bt[kA / a.block_size];
-      int32_t blkB = bok ? bt[kB / a.block_size] : blkA;
+    // position of a tile: logical block index and first row, advanced incrementally
+    struct Pos { int k0, bi, r0; };
+    auto advance = [&](Pos p) {
+      p.k0 += STEP;
+      p.r0 += STEP;
+      while (p.r0 >= a.block_size) { p.r0 -= a.block_size; ++p.bi; }
+      return p;
+    };
+
+    auto load = [&](TileRegs<D, MODE>& R, const Pos& p) {
+      int32_t blk = bt[p.bi];
       // an entry outside the pool masks its tile instead of reading outside the cache
-      R.oka = (uint32_t)blkA < (uint32_t)a.num_blocks;
-      R.okb = bok && (uint32_t)blkB < (uint32_t)a.num_blocks;
-      if (!R.oka) blkA = 0;
-      if (!R.okb) blkB = blkA;
-      const int rowA = kA % a.block_size, rowB = bok ? kB % a.block_size : rowA;
-      const int64_t pa = (int64_t)blkA * a.block_bytes, pb = (int64_t)blkB * a.block_bytes;
-      const uint8_t* ka = kbase + pa + (int64_t)(rowA + r16) * D + kg * (D / 4);
-      const uint8_t* kb = kbase + pb + (int64_t)(rowB + r16) * D + kg * (D / 4);
-      const uint8_t* va = vbase + pa + (int64_t)rowA * D + lane * 16;
-      const uint8_t* vb = vbase + pb + (int64_t)rowB * D + lane * 16;
+      R.ok = (uint32_t)blk < (uint32_t)a.num_blocks;
+      if (!R.ok) blk = 0;
+      const int64_t pb = (int64_t)blk * a.block_bytes;
+      const uint8_t* kp = kbase + pb + (int64_t)(p.r0 + r16) * D + kg * (D / 4);
+      const uint8_t* vp = vbase + pb + (int64_t)p.r0 * D + lane * 16;
 #pragma unroll
       for (int c = 0; c < KV4; ++c) {
-        R.ka[c] = *(const uint4*)(ka + c * 16);
-        R.kb[c] = *(const uint4*)(kb + c * 16);
-        R.va[c] = *(const uint4*)(va + c * 1024);
-        R.vb[c] = *(const uint4*)(vb + c * 1024);
+        R.k[c] = *(const uint4*)(kp + c * 16);
+        R.v[c] = *(const uint4*)(vp + c * 1024);
       }
       if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
-        const int64_t so = (int64_t)a.block_size * D;
-        R.ksa = *(const float4*)(kbase + pa + so + 4 * (rowA + 4 * kg));
-        R.ksb = *(const float4*)(kbase + pb + so + 4 * (rowB + 4 * kg));
-        R.vsa = *(const float4*)(vbase + pa + so + 4 * (rowA + 4 * kg));
-        R.vsb = *(const float4*)(vbase + pb + so + 4 * (rowB + 4 * kg));
+        const int64_t so = (int64_t)a.block_size * D + 4 * (p.r0 + 4 * kg);
+        R.ks = *(const float4*)(kbase + pb + so);
+        R.vs = *(const float4*)(vbase + pb + so);
       }
     };
 
-    auto compute = [&](const IterRegs<D, MODE>& R, int it) {
-      const int kA = it_base + it * kDecIterKeys;
-      const int kB = kA + kTileKeys;
-      // ---- S^T = K * Q^T for the two tiles
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const TileRegs<D, MODE>& R, const Pos& p) {
+      // ---- S^T = K * Q^T: lane holds keys k0 + 4kg + r of head r16
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < QS; ++st) {
-        const uint4 wa = R.ka[st / 2], wb = R.kb[st / 2];
-        const uint32_t a0 = (st & 1) ? wa.z : wa.x, a1 = (st & 1) ? wa.w : wa.y;
-        const uint32_t b0 = (st & 1) ? wb.z : wb.x, b1 = (st & 1) ? wb.w : wb.y;
-        sa = mfma16x16x32(widen8<DT>(a0, a1), qb[st], sa);
-        sb = mfma16x16x32(widen8<DT>(b0, b1), qb[st], sb);
+        const uint4 w = R.k[st / 2];
+        const uint32_t w0 = (st & 1) ? w.z : w.x, w1 = (st & 1) ? w.w : w.y;
+        s = mfma16x16x32(widen8<DT>(w0, w1), qb[st], s);
       }
-      // ---- logits of keys kA + 4kg + r (tile A) and kB + 4kg + r (tile B) for head r16
-      float x[8];
+      float x[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) { x[r] = sa[r] * a.logit_scale; x[4 + r] = sb[r] * a.logit_scale; }
+      for (int r = 0; r < 4; ++r) x[r] = s[r] * xscale;
       if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
-        x[0] *= R.ksa.x; x[1] *= R.ksa.y; x[2] *= R.ksa.z; x[3] *= R.ksa.w;
-        x[4] *= R.ksb.x; x[5] *= R.ksb.y; x[6] *= R.ksb.z; x[7] *= R.ksb.w;
+        x[0] *= R.ks.x; x[1] *= R.ks.y; x[2] *= R.ks.z; x[3] *= R.ks.w;
       }
       if (a.softcap > 0.0f) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = a.softcap * tanh_via_exp2(x[e] * a.inv_softcap);
+        for (int r = 0; r < 4; ++r) x[r] = a.softcap * kLog2e * tanh_via_exp2(x[r] * a.inv_softcap);
       }
-      uint32_t vmask0 = 0, vmask1 = 0;
+      // masking is needed only on the segment's edge tiles (and tiles of an invalid block)
+      const bool full = R.ok && p.k0 >= sg.k_lo && p.k0 + kTileKeys <= sg.k_hi;
+      uint32_t vmask = 0xFFFFFFFFu;
+      if (!full) {
+        vmask = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = (e < 4 ? kA : kB) + 4 * kg + (e & 3);
-        const bool ok = key >= sg.k_lo && key < sg.k_hi && (e < 4 ? R.oka : R.okb);
-        x[e] = ok ? x[e] * kLog2e : -INFINITY;
-        if (ok) { if (e < 4) vmask0 |= 0xFFu << (8 * e); else vmask1 |= 0xFFu << (8 * (e - 4)); }
+        for (int r = 0; r < 4; ++r) {
+          const int key = p.k0 + 4 * kg + r;
+          const bool ok = R.ok && key >= sg.k_lo && key < sg.k_hi;
+          x[r] = ok ? x[r] : -INFINITY;
+          if (ok) vmask |= 0xFFu << (8 * r);
+        }
       }
-      float mx = x[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mx = fmaxf(mx, shfl_xor_f(mx, 16));
       mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      float p[8], psum = 0.0f;
+      // lazy rescaling: the reference max moves (and O, l are rescaled) only when some head's
+      // max exceeds it by more than 2^8, so probabilities stay <= 256 and the common case
+      // leaves the accumulators alone
+      if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f) != 0) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.0f : m_new));
+        l *= alpha;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(x[e] - m_use); psum += p[e]; }
-      l = l * alpha + psum;
-      m = m_new;
+        for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+        m = m_new;
+      }
+      const float m_use = m == -INFINITY ? 0.0f : m;
+      float p4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p4[r] = fast_exp2(x[r] - m_use);
+      l += (p4[0] + p4[1]) + (p4[2] + p4[3]);
       if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
-        p[0] *= R.vsa.x; p[1] *= R.vsa.y; p[2] *= R.vsa.z; p[3] *= R.vsa.w;
-        p[4] *= R.vsb.x; p[5] *= R.vsb.y; p[6] *= R.vsb.z; p[7] *= R.vsb.w;
+        p4[0] *= R.vs.x; p4[1] *= R.vs.y; p4[2] *= R.vs.z; p4[3] *= R.vs.w;
       }
-      bf16x8 pb;
+      bf16x4 pb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[e];
+      for (int r = 0; r < 4; ++r) pb[r] = (__bf16)p4[r];
+      // ---- stage the V tile, read it transposed: O^T[d][head] += V^T[d][keys] P^T[keys][head]
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] *= alpha;
-      // ---- stage V codes: tile A rows 0..15, tile B rows 16..31 of the wave's buffer
-#pragma unroll
-      for (int c = 0; c < KV4; ++c) {
-        *(uint4*)(vbuf + lane * 16 + c * 1024) = R.va[c];
-        *(uint4*)(vbuf + kTileKeys * D + lane * 16 + c * 1024) = R.vb[c];
-      }
+      for (int c = 0; c < KV4; ++c) *(uint4*)(vbuf + vdst[c]) = R.v[c];
       wave_lds_sync();
-      // lane (column d = r16 of the tile, group kg) reads keys {4kg..4kg+3} of tile A and B:
-      // row i of the transposed read is key (i < 4 ? 4kg + i : 16 + 4kg + i - 4).
-      const int i = r16 >> 1;
-      const int row = (i < 4) ? (4 * kg + i) : (kTileKeys + 4 * kg + i - 4);
-      const uint8_t* rp = vbuf + row * D + (r16 & 1) * 8;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const i32x2 v = lds_read_tr8(rp + t * 16);
-        const bf16x8 va = widen8<DT>((uint32_t)v.x & vmask0, (uint32_t)v.y & vmask1);
-        acc[t] = mfma16x16x32(va, pb, acc[t]);
+      for (int t2 = 0; t2 < NT / 2; ++t2) {
+        const i32x2 v = lds_read_tr8(vbuf + tr_off + t2 * 32);
+        acc[2 * t2] = mfma16x16x16(widen4v<DT>((uint32_t)v.x & vmask), pb, acc[2 * t2]);
+        acc[2 * t2 + 1] = mfma16x16x16(widen4v<DT>((uint32_t)v.y & vmask), pb, acc[2 * t2 + 1]);
       }
       wave_lds_sync();
     };
 
-    // software pipeline: the loads of the wave's next iteration are in flight
-    // while the current one is computed
-    {
-      IterRegs<D, MODE> R0, R1;
+    // software pipeline: the loads of the wave's next tile are in flight while
+    // the current one is computed
+    if (wave < n_iter) {
+      Pos p0, p1;
+      p0.k0 = it_base + wave * kDecIterKeys;
+      p0.bi = p0.k0 / a.block_size;
+      p0.r0 = p0.k0 - p0.bi * a.block_size;
+      TileRegs<D, MODE> R0, R1;
+      load(R0, p0);
       int it = wave;
-      if (it < n_iter) load(R0, it);
-      while (it < n_iter) {
-        if (it + kDecWaves < n_iter) load(R1, it + kDecWaves);
-        compute(R0, it);
+      while (true) {
+        p1 = advance(p0);
+        const bool more1 = it + kDecWaves < n_iter;
+        if (more1) load(R1, p1);
+        compute(R0, p0);
+        if (!more1) break;
         it += kDecWaves;
-        if (it >= n_iter) break;
-        if (it + kDecWaves < n_iter) load(R0, it + kDecWaves);
-        compute(R1, it);
+        p0 = advance(p1);
+        const bool more0 = it + kDecWaves < n_iter;
+        if (more0) load(R0, p0);
+        compute(R1, p1);
+        if (!more0) break;
         it += kDecWaves;
       }
     }

@@ -9,6 +9,7 @@
 namespace aqp {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -22,6 +23,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 // and holds C rows 4*(l/16) .. +3 of column (l % 16).
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x16 bf16 MFMA: lane l supplies A row (l % 16), k = 4*(l/16) .. +3; B column (l % 16),
+// same k; C as above.
+__device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // Widen four 1-byte codes (one dword) to four bf16, exactly: every E4M3, E5M2
@@ -58,6 +65,13 @@ __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
   widen4<DT>(w1, r2, r3);
   uint4 u = make_uint4(r0, r1, r2, r3);
   return __builtin_bit_cast(bf16x8, u);
+}
+
+template <int DT>
+__device__ __forceinline__ bf16x4 widen4v(uint32_t w) {
+  uint32_t r0, r1;
+  widen4<DT>(w, r0, r1);
+  return __builtin_bit_cast(bf16x4, make_uint2(r0, r1));
 }
 
 // LDS transpose read of 8-bit data (gfx950 ds_read_b64_tr_b8). Within each

@@ -1,0 +1,289 @@
+"""Benchmark of the quantized paged attention hot path on one MI355X.
+
+One step = one pass of the whole path over one decode batch: quantised cache
+write of the step's new tokens, the host schedule (built and uploaded), and
+paged attention (decode kernel + split-KV merge). Workload: 64 sequences with
+one query each, contexts uniform in [512, 8192] (seeded), 32 q heads / 8 KV
+heads, head_dim 128, block_size 16, fp8 e4m3 per-tensor cache over a pool of
+40000 blocks (randomly permuted block tables), bf16 N(0,1) inputs with 1 % of
+the entries scaled by 20. Inputs are synthetic (seeded) and resident in HBM
+before timing starts.
+
+value = algorithmic KV bytes read per step (every visible key and value code)
+        x steps / elapsed wall time of the timed steps, in GB/s.
+A secondary figure runs the large causal prefill (4 x 1024 tokens, 16/2 heads,
+head_dim 256, block_size 2176, fp8 e4m3) and reports TFLOP/s over its
+algorithmic flops (4 * D per visible (query, key) pair per q head).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="time a plain 1 GiB device-to-device copy (calibrates the HBM byte counters)")
+    return ap.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "device_common.h", "aqp_internal.h"):
+        with open(os.path.join(ROOT, "attention_quantized_paged_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(bytes_alg_per_launch: float):
+    """HBM bytes per launch of the decode kernel from the committed rocprofv3 counter summary,
+    or None if it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "decode_kernel_decode64_fp8e4m3_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def setup_decode(torch, aqp, W, args):
+    w = W.CFG3
+    b = W.make_batch(w)
+    desc = aqp.cache_desc(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
+    total = aqp.cache_bytes(desc)[2]
+    cache = torch.zeros(total, dtype=torch.uint8, device="cuda")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
+    old = ~b.new_mask
+    aqp.cache_write(desc, cache, dev(b.k_hist[old]), dev(b.v_hist[old]), dev(b.slots_hist[old]), b.k_scale, b.v_scale)
+    new_k, new_v, new_s = dev(b.k_hist[b.new_mask]), dev(b.v_hist[b.new_mask]), dev(b.slots_hist[b.new_mask])
+    q = dev(b.q)
+    out = torch.empty_like(q)
+    bt = dev(b.block_tables)
+    params = aqp.attn_params(w.num_q_heads, w.num_kv_heads, w.head_dim, b.block_tables.shape[1])
+    sch = aqp.get_schedule(params, desc, b.seq_lens, b.query_start_loc)
+    # The schedule of each step is built into one of two pinned host buffers and uploaded on a
+    # second stream (default priority) into one of two device buffers, so the upload of step
+    # i+1 overlaps the kernels of step i. Each buffer is reused only after the work that read it
+    # has completed.
+    cap = sch.meta.size + (1 << 16)
+    meta_pinned = [torch.empty(cap, dtype=torch.uint8).pin_memory() for _ in range(2)]
+    meta_np = [t.numpy() for t in meta_pinned]
+    meta_dev = [torch.empty(cap, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    copied = [torch.cuda.Event(), torch.cuda.Event()]   # upload of buffer slot finished
+    consumed = [torch.cuda.Event(), torch.cuda.Event()]  # attention that read slot finished
+    used = [False, False]
+    copy_stream = torch.cuda.Stream()
+    scratch = torch.empty(max(sch.scratch_bytes, 4) * 2, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    return dict(w=w, b=b, desc=desc, cache=cache, new=(new_k, new_v, new_s), q=q, out=out, bt=bt, params=params,
+                meta_pinned=meta_pinned, meta_np=meta_np, meta_dev=meta_dev, copied=copied, consumed=consumed,
+                used=used, copy_stream=copy_stream, scratch=scratch, sched=sch, step=0,
+                main_stream=torch.cuda.current_stream(), stream=torch.cuda.current_stream().cuda_stream)
+
+
+def decode_step(torch, aqp, s, ev=None):
+    b = s["b"]
+    st = s["stream"]
+    main, cs = s["main_stream"], s["copy_stream"]
+    nk, nv, ns = s["new"]
+    aqp.cache_write(s["desc"], s["cache"], nk, nv, ns, b.k_scale, b.v_scale, stream=st)
+    slot = s["step"] & 1
+    s["step"] += 1
+    if s["used"][slot]:
+        s["copied"][slot].synchronize()  # the pinned buffer's previous upload is done
+    sch = aqp.get_schedule(s["params"], s["desc"], b.seq_lens, b.query_start_loc, out=s["meta_np"][slot])
+    n = sch.meta.size
+    with torch.cuda.stream(cs):
+        if s["used"][slot]:
+            cs.wait_event(s["consumed"][slot])  # the device buffer's previous reader is done
+        s["meta_dev"][slot][:n].copy_(s["meta_pinned"][slot][:n], non_blocking=True)
+        s["copied"][slot].record(cs)
+    main.wait_event(s["copied"][slot])
+    if ev is not None:
+        ev[0].record(main)
+    aqp.paged_attention(s["params"], s["desc"], s["cache"], s["q"], s["bt"], sch.meta, s["meta_dev"][slot],
+                        b.k_scale, b.v_scale, s["scratch"], s["scratch"].numel(), s["out"], stream=st)
+    if ev is not None:
+        ev[1].record(main)
+    s["consumed"][slot].record(main)
+    s["used"][slot] = True
+    return sch
+
+
+def run_prefill(torch, aqp, W, args):
+    w = W.CFG2
+    b = W.make_batch(w)
+    desc = aqp.cache_desc(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
+    cache = torch.zeros(aqp.cache_bytes(desc)[2], dtype=torch.uint8, device="cuda")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
+    aqp.cache_write(desc, cache, dev(b.k_hist), dev(b.v_hist), dev(b.slots_hist), b.k_scale, b.v_scale)
+    q = dev(b.q)
+    out = torch.empty_like(q)
+    bt = dev(b.block_tables)
+    params = aqp.attn_params(w.num_q_heads, w.num_kv_heads, w.head_dim, b.block_tables.shape[1])
+    sch = aqp.get_schedule(params, desc, b.seq_lens, b.query_start_loc)
+    meta_dev = torch.from_numpy(sch.meta).cuda()
+    scratch = torch.empty(max(sch.scratch_bytes, 4), dtype=torch.uint8, device="cuda")
+    call = lambda: aqp.paged_attention(params, desc, cache, q, bt, sch.meta, meta_dev, b.k_scale, b.v_scale, scratch,
+                                       scratch.numel(), out)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    reps = 20
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+    flops = W.prefill_flops(w)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+            "ms_per_call": round(ms, 4), "flops": flops, "timing": "median of 20 HIP-event pairs, L2 warm"}
+
+
+def cpu_baseline(W, s, target_seconds=10.0):
+    """The oracle (plain C, OpenMP) running the same step on the host: quantised cache write of
+    the step's new tokens into its own cache, then attention for every sequence of the batch.
+    Repeated until about target_seconds of work; KV bytes read per second."""
+    import oracle
+    w, b = s["w"], s["b"]
+    fmt = {1: oracle.FMT_E4M3, 2: oracle.FMT_E5M2, 3: oracle.FMT_INT8}[s["desc"].dtype]
+    od = oracle.CacheDesc(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, fmt, s["desc"].mode)
+    ocache = np.zeros(od.total_bytes, dtype=np.uint8)
+    old, new = ~b.new_mask, b.new_mask
+    oracle.cache_write(od, ocache, b.k_hist[old], b.v_hist[old], b.slots_hist[old], b.k_scale, b.v_scale)
+    nk, nv, ns = (np.ascontiguousarray(x[new]) for x in (b.k_hist, b.v_hist, b.slots_hist))
+    kv_bytes = W.kv_read_bytes(w, per_token_head=False)
+    steps, elapsed = 0, 0.0
+    while elapsed < target_seconds:
+        t0 = time.perf_counter()
+        oracle.cache_write(od, ocache, nk, nv, ns, b.k_scale, b.v_scale)
+        oracle.attention(od, ocache, b.q, b.block_tables, b.seq_lens, b.query_start_loc, w.num_q_heads,
+                         k_scale=b.k_scale, v_scale=b.v_scale)
+        elapsed += time.perf_counter() - t0
+        steps += 1
+    return {"value": round(kv_bytes * steps / elapsed / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{steps} full steps of the same decode batch (cache write of its 64 new tokens + attention "
+                      f"over {kv_bytes / 1e6:.1f} MB of KV per step) in {elapsed:.1f} s; fp64 attention over the "
+                      f"dequantised, gathered cache"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the path has no multi-GPU "
+                                   "component (sharding by sequence or KV head needs no exchange)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    if args.copy_probe:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
+                          "GBps_read_plus_write": round(2 * n / ms / 1e6, 1)}))
+        return
+    import attention_quantized_paged_amd as aqp
+    import workloads as W
+
+    log(args, "[bench] setting up decode batch")
+    s = setup_decode(torch, aqp, W, args)
+    w = s["w"]
+    kv_bytes = W.kv_read_bytes(w, per_token_head=False)
+    for _ in range(args.warmup):
+        decode_step(torch, aqp, s)
+    torch.cuda.synchronize()
+    log(args, f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        sch = decode_step(torch, aqp, s)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # kernel time: the same steps again, each attention launch bracketed by HIP events on the
+    # stream it runs on (timing events serialise the stream, so they stay out of the step timing)
+    log(args, f"[bench] timing {args.steps} attention launches")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        decode_step(torch, aqp, s, evs[i])
+    torch.cuda.synchronize()
+    attn_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    ms_per_step = elapsed / args.steps * 1e3
+    value = kv_bytes * args.steps / elapsed / 1e9
+    h = sch.header
+    achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
+    result = {
+        "metric": "decode KV-read HBM GB/s (% of peak) + prefill TFLOP/s, paged attn over fp8/int8 KV",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": len(w.seqs), "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size, "kv_cache_dtype": w.kv_dtype,
+                   "context": "uniform[512,8192] seeded", "kv_bytes_per_step": kv_bytes,
+                   "new_tokens_per_step": int(s["b"].new_mask.sum()), "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(kv_bytes),
+                     "kernel": "decode_kernel + split-KV merge (one attention launch)",
+                     "launch_ms": round(attn_ms, 4), "decode_workgroups": h["num_dec_wgs"],
+                     "partials": h["num_parts"]},
+    }
+    if not args.no_prefill:
+        log(args, "[bench] prefill figure")
+        result["prefill"] = run_prefill(torch, aqp, W, args)
+    if not args.no_cpu_baseline:
+        log(args, "[bench] oracle CPU baseline")
+        result["cpu_baseline"] = cpu_baseline(W, s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

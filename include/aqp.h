@@ -93,7 +93,8 @@ typedef struct {
   int32_t max_blocks_per_seq; /* row stride of block_tables */
   float sm_scale;             /* logit scale; 0 means 1/sqrt(head_dim) */
   float softcap;              /* 0: none; c > 0: logit z -> c * tanh(z / c), applied after sm_scale */
-  int32_t decode_parallelism; /* waves the decode work is split across; 0 = default (4096) */
+  int32_t decode_parallelism; /* work-groups the decode work is split across; 0 = one resident wave of
+                                 work-groups on the current device (CUs x 3 for head_dim <= 128, x 2 above) */
   int32_t reserved;
 } aqp_attn_params;
 

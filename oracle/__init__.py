@@ -52,6 +52,7 @@ def _load():
         P = ctypes.c_void_p
         i32, i64, f32, f64, u32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_uint32
         D = ctypes.POINTER(_Desc)
+        lib.orc_num_threads.argtypes = []; lib.orc_num_threads.restype = ctypes.c_int
         lib.orc_decode.argtypes = [ctypes.c_int, u32]; lib.orc_decode.restype = f64
         lib.orc_encode.argtypes = [ctypes.c_int, f32]; lib.orc_encode.restype = u32
         lib.orc_encode_array.argtypes = [ctypes.c_int, P, i64, P]; lib.orc_encode_array.restype = None
@@ -102,6 +103,10 @@ class CacheDesc:
 
     def page_offset(self, block, kv, head):
         return _load().orc_page_offset(ctypes.byref(self.c), block, kv, head)
+
+
+def num_threads() -> int:
+    return _load().orc_num_threads()
 
 
 def decode(fmt: int, code: int) -> float:

@@ -44,6 +44,8 @@ typedef struct {
   int32_t mode; /* ORC_MODE_* */
 } orc_cache_desc;
 
+int orc_num_threads(void);                          /* OpenMP threads the oracle runs with */
+
 /* ---- codec ---- */
 double orc_decode(int fmt, uint32_t code);          /* value of one code (NaN / inf where the format has them) */
 uint32_t orc_encode(int fmt, float y);              /* fp8: RNE + satfinite; int8: RNE + clamp (two's complement byte) */

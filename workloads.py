@@ -14,9 +14,11 @@ soft_cap, kv_cache_dtype) and the KV modes of the per-token-head page
 need datasets and trained weights, so these seeded inputs stand in for them.
 
 Recipe (per workload, seed fixed below):
-  * values: fp32 draws from N(0, sigma^2) with numpy's default_rng, optional
-    outliers (a seeded Bernoulli mask multiplies entries by a factor), then
-    rounded to bf16 (nearest, ties to even);
+  * values: fp32 draws from N(0, sigma^2) with numpy's PCG64 generators
+    (one child seed per tensor and per fixed 1/16 chunk of its rows, so the
+    values do not depend on the thread count), optional outliers (a seeded
+    Bernoulli mask multiplies entries by a factor), then rounded to bf16
+    (nearest, ties to even);
   * block tables: a seeded permutation of the block pool; sequence b takes the
     next ceil(L_b / block_size) entries; unused entries are -1;
   * slot of token j of sequence b: table[b][j // bs] * bs + j % bs;
@@ -26,9 +28,10 @@ Recipe (per workload, seed fixed below):
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
-import math
-from typing import List, Optional, Tuple
+import os
+from typing import Tuple
 
 import numpy as np
 
@@ -90,17 +93,21 @@ def scaled(w: Workload, **kw) -> Workload:
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
-    """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even (finite inputs)."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    bias = ((u >> 16) & 1) + np.uint32(0x7FFF)
-    return ((u + bias) >> 16).astype(np.uint16)
+    """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even (torch's CPU cast)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 def bf16_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def _draw(rng: np.random.Generator, shape, w: Workload) -> np.ndarray:
+_CHUNKS = 16
+
+
+def _draw_chunk(seed_seq: np.random.SeedSequence, shape, w: Workload) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(seed_seq))
     x = rng.standard_normal(shape, dtype=np.float32)
     if w.sigma != 1.0:
         x *= np.float32(w.sigma)
@@ -108,6 +115,25 @@ def _draw(rng: np.random.Generator, shape, w: Workload) -> np.ndarray:
         mask = rng.random(shape, dtype=np.float32) < np.float32(w.outlier_frac)
         x[mask] *= np.float32(w.outlier_factor)
     return bf16_round(x)
+
+
+def _draw(seed_seq: np.random.SeedSequence, shape, w: Workload) -> np.ndarray:
+    """bf16 bits of the given shape; rows split into _CHUNKS fixed pieces with their own child seeds."""
+    n = shape[0]
+    out = np.empty(shape, dtype=np.uint16)
+    if n == 0:
+        return out
+    bounds = np.linspace(0, n, _CHUNKS + 1).astype(np.int64)
+    kids = seed_seq.spawn(_CHUNKS)
+
+    def fill(i):
+        lo, hi = int(bounds[i]), int(bounds[i + 1])
+        if hi > lo:
+            out[lo:hi] = _draw_chunk(kids[i], (hi - lo,) + tuple(shape[1:]), w)
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(_CHUNKS, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(_CHUNKS)))
+    return out
 
 
 @dataclasses.dataclass
@@ -130,7 +156,8 @@ class Batch:
 
 
 def make_batch(w: Workload, with_kv: bool = True) -> Batch:
-    rng = np.random.default_rng(w.seed)
+    ss_tables, ss_q, ss_k, ss_v = np.random.SeedSequence(w.seed).spawn(4)
+    rng = np.random.Generator(np.random.PCG64(ss_tables))
     B = len(w.seqs)
     qlens = w.query_lens
     lens = w.seq_lens
@@ -146,7 +173,7 @@ def make_batch(w: Workload, with_kv: bool = True) -> Batch:
         pos += int(need[b])
     qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
     Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_dim
-    q = _draw(rng, (int(qsl[-1]), Hq, D), w)
+    q = _draw(ss_q, (int(qsl[-1]), Hq, D), w)
     total = int(lens.sum())
     slots = np.empty(total, dtype=np.int64)
     new_mask = np.zeros(total, dtype=bool)
@@ -157,8 +184,8 @@ def make_batch(w: Workload, with_kv: bool = True) -> Batch:
         new_mask[off + lens[b] - qlens[b]: off + lens[b]] = True
         off += int(lens[b])
     if with_kv:
-        k = _draw(rng, (total, Hkv, D), w)
-        v = _draw(rng, (total, Hkv, D), w)
+        k = _draw(ss_k, (total, Hkv, D), w)
+        v = _draw(ss_v, (total, Hkv, D), w)
     else:
         k = v = np.zeros((0, Hkv, D), dtype=np.uint16)
     k_scale = v_scale = 1.0
