@@ -69,8 +69,9 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
   const int32_t dec_stage = kDecWaves * kDecIterKeys * (d.head_dim * g->staged_elem_bytes + kDecVRowPad);
   const int32_t dec_merge = (kDecWaves - 1) * kMaxHeadsPerUnit * (d.head_dim + 2) * 4;
   g->dec_lds_bytes = std::max(dec_stage, dec_merge);
-  // Prefill work-group: double-buffered K and V tiles of codes plus their row scales.
-  g->pf_lds_bytes = 2 * (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes + 2 * kPfKvTile * 4);
+  // Prefill work-group: a ring of kPfStages steps, each the K and V codes of kPfKvTile keys
+  // plus their row scales.
+  g->pf_lds_bytes = kPfStages * (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes + 2 * kPfKvTile * 4);
   return AQP_OK;
 }
 

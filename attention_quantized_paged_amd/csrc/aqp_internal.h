@@ -29,6 +29,7 @@ constexpr int kPfRowsPerWave = 32;   // prefill: query rows (token, head) per wa
 constexpr int kPfWaves = 4;          // prefill: waves per work-group
 constexpr int kPfRows = kPfRowsPerWave * kPfWaves;  // query rows per prefill work item
 constexpr int kPfKvTile = 32;        // prefill: keys staged in LDS per step
+constexpr int kPfStages = 4;         // prefill: LDS ring stages (three steps of copies in flight)
 constexpr int kMinDecodeKeysPerWG = 512;
 // Decode work-groups resident per CU for each head_dim (registers of the
 // compiled kernel: 3, 3 and 2 waves per SIMD). The default decode split uses

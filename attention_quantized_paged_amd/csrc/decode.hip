@@ -86,12 +86,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
   // second four 16 columns further, so one read yields the operands of two head-dim tiles
   const int tr_i = r16 >> 1;
   const int tr_off = (4 * kg + (tr_i & 3)) * VROW + (tr_i >> 2) * 16 + (r16 & 1) * 8;
-  const int s_begin = a.wg_start[blockIdx.x], s_end = a.wg_start[blockIdx.x + 1];
+  const int s_begin = as_const(a.wg_start)[blockIdx.x], s_end = as_const(a.wg_start)[blockIdx.x + 1];
   // without a soft-cap, log2(e) folds into the logit scale
   const float xscale = a.softcap > 0.0f ? a.logit_scale : a.logit_scale * kLog2e;
 
   for (int si = s_begin; si < s_end; ++si) {
-    const DecSeg sg = a.segs[si];
+    const DecSeg sg = load_const(as_const(a.segs) + si);
     const int head = sg.head0 + r16;
     const bool head_ok = r16 < sg.nheads;
     const int hq = sg.kvh * a.group + head;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
         qb[st] = __builtin_bit_cast(bf16x8, u);
       }
     }
-    const int32_t* bt = a.block_tables + (int64_t)sg.seq * a.max_blocks;
+    const cptr<int32_t> bt = as_const(a.block_tables) + (int64_t)sg.seq * a.max_blocks;
     const uint8_t* kbase = a.cache + (int64_t)sg.kvh * a.page_bytes;
     const uint8_t* vbase = a.cache + (int64_t)(a.num_kv_heads + sg.kvh) * a.page_bytes;
     const int it_base = (sg.k_lo / kTileKeys) * kTileKeys;
@@ -179,9 +179,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
           if (ok) vmask |= 0xFFu << (8 * r);
         }
       }
-      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      // rows outside the range may hold unwritten bytes: their V codes are masked to zero and
+      // (per token-head) their scale is replaced, so no NaN pattern reaches the sums
+      const float mx = max_over_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
       // lazy rescaling: the reference max moves (and O, l are rescaled) only when some head's
       // max exceeds it by more than 2^8, so probabilities stay <= 256 and the common case
       // leaves the accumulators alone
@@ -199,7 +199,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
       for (int r = 0; r < 4; ++r) p4[r] = fast_exp2(x[r] - m_use);
       l += (p4[0] + p4[1]) + (p4[2] + p4[3]);
       if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
-        p4[0] *= R.vs.x; p4[1] *= R.vs.y; p4[2] *= R.vs.z; p4[3] *= R.vs.w;
+        float4 vs = R.vs;
+        if (!full) {
+          vs.x = (vmask & 0xFFu) ? vs.x : 0.0f;
+          vs.y = (vmask & 0xFF00u) ? vs.y : 0.0f;
+          vs.z = (vmask & 0xFF0000u) ? vs.z : 0.0f;
+          vs.w = (vmask & 0xFF000000u) ? vs.w : 0.0f;
+        }
+        p4[0] *= vs.x; p4[1] *= vs.y; p4[2] *= vs.z; p4[3] *= vs.w;
       }
       bf16x4 pb;
 #pragma unroll
@@ -244,8 +251,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
     }
 
     // ---- merge the four waves: l over the lanes of a head, then across waves in LDS
-    l += shfl_xor_f(l, 16);
-    l += shfl_xor_f(l, 32);
+    l = sum_over_rows(l);
     __syncthreads();  // every wave is done with its V staging buffer
     float* mg = (float*)smem;  // [wave-1][head][D + 2]
     if (wave > 0) {
@@ -320,7 +326,7 @@ template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(const CombItem* items, const float* scratch, uint16_t* out,
                                                      int32_t num_q_heads, int32_t group, int32_t group_heads,
                                                      int32_t num_parts) {
-  const CombItem it = items[blockIdx.x];
+  const CombItem it = load_const(as_const(items) + blockIdx.x);
   const int h = blockIdx.y;
   if (h >= it.nheads) return;
   const int lane = threadIdx.x;

@@ -82,6 +82,64 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const void* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane l's
+// 16 bytes from `g` land at LDS byte address lds_base + 16 * l. lds_base must be wave-uniform.
+// Issued by hand so that the waits below can be exact: the compiler's own tracking of these
+// copies waits for every outstanding one before any LDS read, which would drain a multi-stage
+// pipeline.
+__device__ __forceinline__ void dma16_to_lds(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory");
+}
+
+// Wait until at most n of this wave's vector memory operations are outstanding (n < 16).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+    case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+  }
+}
+
+// LDS byte address of a pointer into the dynamic shared allocation.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Read-only view in the constant address space: uniform indexes then compile to scalar loads
+// (block tables, schedule items), which leave the vector memory counter to the KV traffic.
+template <typename T>
+using cptr = const __attribute__((address_space(4))) T*;
+template <typename T>
+__device__ __forceinline__ cptr<T> as_const(const T* p) {
+  return (cptr<T>)(p);
+}
+
+// Copy a record (a multiple of 16 bytes) out of the constant address space.
+template <typename T>
+__device__ __forceinline__ T load_const(cptr<T> p) {
+  static_assert(sizeof(T) % 16 == 0, "records are whole 16-byte words");
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  v4i w[sizeof(T) / 16];
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 16); ++i) w[i] = ((cptr<v4i>)p)[i];
+  T r;
+  __builtin_memcpy(&r, w, sizeof(T));
+  return r;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // tanh from its definition via exp: tanh(t) = sign(t) * (1 - e^{-2|t|}) / (1 + e^{-2|t|}),
@@ -93,6 +151,21 @@ __device__ __forceinline__ float tanh_via_exp2(float t) {
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows of a wave), in VALU:
+// v_permlane16_swap exchanges rows 0<->1 and 2<->3, v_permlane32_swap the two halves.
+__device__ __forceinline__ float max_over_rows(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), false, false);
+  v = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), false, false);
+  v = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), false, false);
+  return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
+}
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -39,26 +39,45 @@ struct PfArgs {
   float v_scale;
 };
 
+// 16-byte chunk swizzle of a staged row: chunk c of row `row` is stored at chunk
+// c ^ swz(row). Rows are D bytes; 256 bytes span all LDS banks, so rows that share banks
+// (same row / (256 / D) residue) get different chunk offsets, and the second 16-key tile gets
+// the upper half of the offsets. This keeps the K-operand reads (16 rows, one chunk) and the
+// transposed V reads (8 rows of two tiles, one chunk) free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  constexpr int CPR = D / 16;                  // chunks per row
+  constexpr int RPL = D >= 256 ? 1 : 256 / D;  // rows per 256 bytes
+  return ((row / RPL) % CPR) ^ (((row >> 4) & 1) * (CPR / 2));
+}
+
 template <int D, int DT, int MODE>
-__global__ __launch_bounds__(256) void prefill_kernel(PfArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : (D <= 128 ? 2 : 1)))) void prefill_kernel(PfArgs a) {
   constexpr int NT = D / 16;
   constexpr int QS = D / 32;
-  constexpr int KT = kPfKvTile;                // keys per step
-  constexpr int CHUNKS = KT * D / 16;          // 16-byte chunks per K (or V) step
-  constexpr int CPT = (CHUNKS + 255) / 256;    // chunks per thread
-  constexpr int BUF = 2 * KT * D + 2 * KT * 4; // bytes per LDS buffer: K, V codes, K, V scales
+  constexpr int KT = kPfKvTile;                   // keys per step (two 16-key tiles)
+  constexpr int NS = kPfStages;                   // LDS ring stages
+  constexpr int CPR = D / 16;                     // 16-byte chunks per row
+  constexpr int STAGE = 2 * KT * D + 2 * KT * 4;  // K codes, V codes, K scales, V scales
+  constexpr int KV_INSTR = KT * CPR / 64;         // 1 KB copies per K (or V) step
+  constexpr int IPW = 2 * KV_INSTR / 4;           // K+V copies per wave per step
+  static_assert(IPW >= 1 && (2 * KV_INSTR) % 4 == 0, "copies must split evenly over 4 waves");
+  constexpr int PTH = MODE == AQP_SCALE_PER_TOKEN_HEAD ? 1 : 0;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int r16 = lane & 15;
   const int kg = lane >> 4;
-  const PfItem it = a.items[blockIdx.x];
+  const PfItem it = load_const(as_const(a.items) + blockIdx.x);
   const int G = a.group;
   const int ntok = it.q_hi - it.q_lo;
-  const int32_t* bt = a.block_tables + (int64_t)it.seq * a.max_blocks;
+  const cptr<int32_t> bt = as_const(a.block_tables) + (int64_t)it.seq * a.max_blocks;
   const uint8_t* kbase = a.cache + (int64_t)it.kvh * a.page_bytes;
   const uint8_t* vbase = a.cache + (int64_t)(a.num_kv_heads + it.kvh) * a.page_bytes;
+  const uint32_t lds0 = lds_addr(smem);
+  // copies this wave issues per step: its share of K/V, plus the scale copy on wave 3
+  const int ipw_me = IPW + ((PTH && wave == 3) ? 1 : 0);
 
   // ---- rows of this lane (as MFMA column r16 of row tiles 0, 1)
   int lo_r[2], hi_r[2];
@@ -84,12 +103,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PfArgs a) {
       qb[rt][st] = __builtin_bit_cast(bf16x8, u);
     }
   }
+  // the wave's rows cover tokens [tw0, tw1]: keys in [vis_lo, vis_hi) are visible to all of them
+  const int tw0 = min(ntok - 1, (wave * kPfRowsPerWave) / G);
+  const int tw1 = min(ntok - 1, (wave * kPfRowsPerWave + kPfRowsPerWave - 1) / G);
+  const bool wave_rows_full = (wave * kPfRowsPerWave + kPfRowsPerWave - 1) / G < ntok;
+  const int pw0 = it.L - it.ql + it.q_lo + tw0, pw1 = it.L - it.ql + it.q_lo + tw1;
+  const int vis_hi = a.causal ? pw0 + 1 : it.L;
+  const int vis_lo = (a.window > 0 && pw1 - a.window + 1 > 0) ? pw1 - a.window + 1 : 0;
   // ---- key range of the whole item: first token's window start .. last token's end
   const int p_first = it.L - it.ql + it.q_lo;
   const int k_first = (a.window > 0 && p_first - a.window + 1 > 0) ? p_first - a.window + 1 : 0;
   const int k_begin = (k_first / kTileKeys) * kTileKeys;
   const int k_end = it.k_hi_max;
   const int n_steps = (k_end - k_begin + KT - 1) / KT;
+  const float xscale = a.softcap > 0.0f ? a.logit_scale : a.logit_scale * kLog2e;
+  const int last_tile = ((it.L - 1) / kTileKeys) * kTileKeys;  // first key of the tile holding key L-1
 
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
   f32x4 acc[2][NT];
@@ -98,147 +126,163 @@ __global__ __launch_bounds__(256) void prefill_kernel(PfArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // cooperative staging registers
-  uint4 kreg[CPT], vreg[CPT];
-  float sreg = 0.0f;
-  auto gload = [&](int step) {
+  // ---- issue the copies of one step into its ring stage. Copy ii (0 .. 2*KV_INSTR-1) fills
+  // 64 chunks of K (ii < KV_INSTR) or V; lane l takes LDS chunk q = 64*(ii % KV_INSTR) + l,
+  // row q / CPR, stored chunk q % CPR, which holds logical chunk (q % CPR) ^ swz(row). The 64
+  // chunks lie in one 16-key tile. Keys at or past L (never visible) read key L-1's row so that
+  // only finite codes reach LDS.
+  auto issue = [&](int step) {
     const int kb0 = k_begin + step * KT;
+    const uint32_t sbase = lds0 + (uint32_t)((step % NS) * STAGE);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * 256;
-      kreg[c] = make_uint4(0, 0, 0, 0);
-      vreg[c] = make_uint4(0, 0, 0, 0);
-      if (ch < CHUNKS) {
-        const int key = ch / (D / 16), col = (ch % (D / 16)) * 16;
-        const int j = kb0 + key;
-        if (j < it.L) {
-          const int32_t blk = bt[j / a.block_size];
-          if ((uint32_t)blk < (uint32_t)a.num_blocks) {
-            const int64_t off = (int64_t)blk * a.block_bytes + (int64_t)(j % a.block_size) * D + col;
-            kreg[c] = *(const uint4*)(kbase + off);
-            vreg[c] = *(const uint4*)(vbase + off);
-          }
-        }
-      }
+    for (int j = 0; j < IPW; ++j) {
+      const int ii = wave + 4 * j;
+      const int kv = ii / KV_INSTR;
+      const int q0 = 64 * (ii % KV_INSTR);
+      const int q = q0 + lane;
+      const int row = q / CPR;
+      const int lc = (q % CPR) ^ swz<D>(row);
+      // tile of this copy (uniform), clamped to the tile of key L-1
+      const int tile_k0 = min(kb0 + ((q0 / CPR) & ~15), last_tile);
+      const int tbi = tile_k0 / a.block_size;
+      const int tr0 = tile_k0 - tbi * a.block_size;
+      int32_t blk = bt[tbi];
+      if ((uint32_t)blk >= (uint32_t)a.num_blocks) blk = 0;  // invalid table entry: stay in the pool
+      const int key = min(kb0 + row, it.L - 1);
+      const uint8_t* src = (kv ? vbase : kbase) + (int64_t)blk * a.block_bytes +
+                           (int64_t)(tr0 + (key - tile_k0)) * D + lc * 16;
+      dma16_to_lds(src, sbase + (uint32_t)(kv * KT * D + q0 * 16));
     }
-    if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
-      sreg = 0.0f;
-      if (tid < 2 * KT) {
-        const int j = kb0 + (tid % KT);
-        if (j < it.L) {
-          const int32_t blk = bt[j / a.block_size];
-          if ((uint32_t)blk < (uint32_t)a.num_blocks) {
-            const uint8_t* base = tid < KT ? kbase : vbase;
-            sreg = *(const float*)(base + (int64_t)blk * a.block_bytes + (int64_t)a.block_size * D + 4 * (j % a.block_size));
-          }
-        }
+    if constexpr (PTH) {
+      if (wave == 3) {
+        // 16 lanes x 16 bytes: [K scales of the 32 keys][V scales], 4 scales per lane
+        const int tl = (lane >> 2) & 1, part = lane & 3, kv = lane >> 3;
+        const int t0 = min(kb0, last_tile), t1 = min(kb0 + 16, last_tile);
+        const int bi0 = t0 / a.block_size, bi1 = t1 / a.block_size;
+        int32_t b0 = bt[bi0], b1 = bt[bi1];
+        if ((uint32_t)b0 >= (uint32_t)a.num_blocks) b0 = 0;
+        if ((uint32_t)b1 >= (uint32_t)a.num_blocks) b1 = 0;
+        const int tk0 = tl ? t1 : t0;
+        const int32_t blk = tl ? b1 : b0;
+        const int r0 = tk0 - (tl ? bi1 : bi0) * a.block_size;
+        const uint8_t* src = (kv ? vbase : kbase) + (int64_t)blk * a.block_bytes + (int64_t)a.block_size * D +
+                             4 * (r0 + 4 * part);
+        if (lane < 16) dma16_to_lds(src, sbase + (uint32_t)(2 * KT * D));
       }
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint8_t* b = smem + buf * BUF;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * 256;
-      if (ch < CHUNKS) {
-        *(uint4*)(b + ch * 16) = kreg[c];
-        *(uint4*)(b + KT * D + ch * 16) = vreg[c];
-      }
-    }
-    if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
-      if (tid < 2 * KT) *(float*)(b + 2 * KT * D + 4 * tid) = sreg;
     }
   };
 
-  if (n_steps > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
+  // transposed V read: row i of lane group kg is key (i < 4 ? 4kg + i : 16 + 4kg + i - 4)
+  const int tr_i = r16 >> 1;
+  const int tr_row = (tr_i < 4) ? (4 * kg + tr_i) : (16 + 4 * kg + tr_i - 4);
+  const int tr_swz = swz<D>(tr_row);
+
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0)
+    if (s0 < n_steps) issue(s0);
+
   for (int step = 0; step < n_steps; ++step) {
-    const int buf = step & 1;
-    if (step + 1 < n_steps) gload(step + 1);
-    const uint8_t* kl = smem + buf * BUF;
+    // this step's copies are done once only the later stages' copies are outstanding
+    wait_vmcnt(min(NS - 2, n_steps - 1 - step) * ipw_me);
+    __syncthreads();  // every wave's copies of this step landed; every wave left the previous step
+    if (step + NS - 1 < n_steps) issue(step + NS - 1);  // into the stage the previous step used
+    const uint8_t* kl = smem + (step % NS) * STAGE;
     const uint8_t* vl = kl + KT * D;
     const float* ksl = (const float*)(kl + 2 * KT * D);
     const float* vsl = ksl + KT;
     const int kb0 = k_begin + step * KT;
+    // ---- operand reads of the whole step are issued before any use, so the LDS latency of
+    // one overlaps the conversion and MFMAs of the others
+    uint2 kw[2][QS];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int krow = kt * 16 + r16;
+      const uint8_t* kp = kl + krow * D;
+      const int ksw = swz<D>(krow);
+#pragma unroll
+      for (int st = 0; st < QS; ++st) {
+        const int dbyte = kg * (D / 4) + st * 8;
+        kw[kt][st] = *(const uint2*)(kp + ((((dbyte >> 4) ^ ksw) << 4) | (dbyte & 8)));
+      }
+    }
     // ---- S^T = K Q^T: [key tile kt][row tile rt]
     f32x4 s[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) s[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint8_t* kp = kl + (kt * 16 + r16) * D + kg * (D / 4);
 #pragma unroll
       for (int st = 0; st < QS; ++st) {
-        const uint2 w = *(const uint2*)(kp + st * 8);
-        const bf16x8 ka = widen8<DT>(w.x, w.y);
+        const bf16x8 ka = widen8<DT>(kw[kt][st].x, kw[kt][st].y);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) s[kt][rt] = mfma16x16x32(ka, qb[rt][st], s[kt][rt]);
       }
     }
-    // ---- online softmax per row tile
+    // V^T operands: transposed reads issued now, used after the softmax
+    i32x2 vw[NT];
+    {
+      const uint8_t* rp = vl + tr_row * D + (r16 & 1) * 8;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) vw[t] = lds_read_tr8(rp + ((t ^ tr_swz) << 4));
+    }
+    // ---- online softmax per row tile (lazy rescaling as in decode)
+    const bool full = wave_rows_full && kb0 >= vis_lo && kb0 + KT <= vis_hi && kb0 + KT <= it.L;
     bf16x8 pb[2];
-    float alpha[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kt = e >> 2, r = e & 3;
-        float v = s[kt][rt][r] * a.logit_scale;
-        if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) v *= ksl[kt * 16 + 4 * kg + r];
-        if (a.softcap > 0.0f) v = a.softcap * tanh_via_exp2(v * a.inv_softcap);
-        const int j = kb0 + kt * 16 + 4 * kg + r;
-        x[e] = (j >= lo_r[rt] && j < hi_r[rt]) ? v * kLog2e : -INFINITY;
+        float v = s[kt][rt][r] * xscale;
+        if constexpr (PTH) v *= ksl[kt * 16 + 4 * kg + r];
+        if (a.softcap > 0.0f) v = a.softcap * kLog2e * tanh_via_exp2(v * a.inv_softcap);
+        x[e] = v;
+      }
+      if (!full) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = kb0 + (e >> 2) * 16 + 4 * kg + (e & 3);
+          if (!(j >= lo_r[rt] && j < hi_r[rt])) x[e] = -INFINITY;
+        }
       }
       float mx = x[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float m_new = fmaxf(m[rt], mx);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      alpha[rt] = fast_exp2(m[rt] - m_use);
+      mx = max_over_rows(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > m[rt] + 8.0f) != 0) {
+        const float m_new = fmaxf(m[rt], mx);
+        const float alpha = fast_exp2(m[rt] - (m_new == -INFINITY ? 0.0f : m_new));
+        l[rt] *= alpha;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[rt][t] *= alpha;
+        m[rt] = m_new;
+      }
+      const float m_use = m[rt] == -INFINITY ? 0.0f : m[rt];
       float psum = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float pe = fast_exp2(x[e] - m_use);
         psum += pe;
-        if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) pe *= vsl[(e >> 2) * 16 + 4 * kg + (e & 3)];
+        // a masked key may have an unwritten scale slot: select, do not multiply, its zero
+        if constexpr (PTH) pe = x[e] == -INFINITY ? 0.0f : pe * vsl[(e >> 2) * 16 + 4 * kg + (e & 3)];
         pb[rt][e] = (__bf16)pe;
       }
-      l[rt] = l[rt] * alpha[rt] + psum;
-      m[rt] = m_new;
+      l[rt] += psum;
     }
+    // ---- O^T += V^T P^T
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[rt][t] *= alpha[rt];
-    // ---- O^T += V^T P^T; transposed row i of the read is key (i < 4 ? 4kg + i : 16 + 4kg + i - 4)
-    {
-      const int i = r16 >> 1;
-      const int row = (i < 4) ? (4 * kg + i) : (16 + 4 * kg + i - 4);
-      const uint8_t* rp = vl + row * D + (r16 & 1) * 8;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const i32x2 v = lds_read_tr8(rp + t * 16);
-        const bf16x8 va = widen8<DT>((uint32_t)v.x, (uint32_t)v.y);
-        acc[0][t] = mfma16x16x32(va, pb[0], acc[0][t]);
-        acc[1][t] = mfma16x16x32(va, pb[1], acc[1][t]);
-      }
+    for (int t = 0; t < NT; ++t) {
+      const bf16x8 va = widen8<DT>((uint32_t)vw[t].x, (uint32_t)vw[t].y);
+      acc[0][t] = mfma16x16x32(va, pb[0], acc[0][t]);
+      acc[1][t] = mfma16x16x32(va, pb[1], acc[1][t]);
     }
-    if (step + 1 < n_steps) lstore(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- normalise and write the rows
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    float lt = l[rt];
-    lt += shfl_xor_f(lt, 16);
-    lt += shfl_xor_f(lt, 32);
+    const float lt = sum_over_rows(l[rt]);
     if (!row_ok[rt]) continue;
     const float norm = a.v_scale / lt;
     uint16_t* op = a.out + orow[rt];

@@ -53,6 +53,27 @@ def test_small_parity(aqp, w):
     compare(out[rows], ref, w.name)
 
 
+NAN_FILL = [
+    W.Workload("nanfill_decode_pth", "fp8_per_token_head", ((1, 37), (1, 100), (1, 16)), 8, 2, 128, 16, 24, seed=91),
+    W.Workload("nanfill_mixed_int8", "int8_per_token_head", ((1, 50), (21, 45)), 8, 2, 64, 32, 12, seed=92),
+    W.Workload("nanfill_prefill_e4m3", "fp8_e4m3", ((19, 19), (40, 70)), 8, 2, 256, 32, 12, seed=93),
+    W.Workload("nanfill_prefill_e4m3_pth_w", "fp8_per_token_head", ((33, 33), (9, 60)), 4, 1, 128, 16, 16, window=20,
+               seed=94),
+]
+
+
+@pytest.mark.parametrize("w", NAN_FILL, ids=[w.name for w in NAN_FILL])
+def test_unwritten_cache_bytes_do_not_leak(aqp, w):
+    """Every byte of the cache that the batch does not write holds 0xFF (a NaN pattern for the fp8
+    codes and for fp32 scales); rows past each sequence's end share pages with real keys. The
+    outputs must not see them."""
+    r = Run(w, torch, aqp, fill=0xFF)
+    r.cache_matches()
+    out = r.gpu_attention()
+    ref, rows = r.oracle_attention()
+    compare(out[rows], ref, w.name)
+
+
 @pytest.mark.parametrize("par", [1, 3, 64, 4096])
 def test_decode_split_counts(aqp, par):
     """The same decode batch cut into 1 .. many work-groups gives the same result."""

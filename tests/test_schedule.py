@@ -184,5 +184,5 @@ def test_large_block_size_geometry_is_consistent():
     s, *_ = _sched(((1024, 1024),) * 4, 16, 2, 256, 2176)
     h = s.header
     assert h["pf_kv_tile"] == 32 and h["staged_elem_bytes"] == 1
-    assert h["pf_lds_bytes"] == 2 * (2 * 32 * 256 * 1 + 2 * 32 * 4)
-    assert h["dec_lds_bytes"] == max(4 * 32 * 256, 3 * 16 * (256 + 2) * 4)
+    assert h["pf_lds_bytes"] == 4 * (2 * 32 * 256 * 1 + 2 * 32 * 4)
+    assert h["dec_lds_bytes"] == max(4 * 16 * (256 + 32), 3 * 16 * (256 + 2) * 4)
