@@ -64,11 +64,6 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
   g->page_bytes = round_up((int64_t)d.block_size * d.head_dim * g->kv_elem_bytes + (int64_t)d.block_size * g->scale_bytes, 128);
   g->block_bytes = 2 * (int64_t)d.num_kv_heads * g->page_bytes;
   g->total_bytes = (int64_t)d.num_blocks * g->block_bytes;
-  // Decode work-group: each wave stages one iteration of V codes; at the end
-  // waves 1..3 hand their (O, m, l) for up to 16 heads to wave 0.
-  const int32_t dec_stage = kDecWaves * kDecIterKeys * (d.head_dim * g->staged_elem_bytes + kDecVRowPad);
-  const int32_t dec_merge = (kDecWaves - 1) * kMaxHeadsPerUnit * (d.head_dim + 2) * 4;
-  g->dec_lds_bytes = std::max(dec_stage, dec_merge);
   // Prefill work-group: a ring of kPfStages steps, each the K and V codes of kPfKvTile keys
   // plus their row scales.
   g->pf_lds_bytes = kPfStages * (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes + 2 * kPfKvTile * 4);
@@ -167,7 +162,6 @@ static int check_params(const aqp_attn_params& p, const aqp_cache_desc& d, const
   if (p.num_kv_heads != d.num_kv_heads) { *why = "params.num_kv_heads differs from the cache's"; return AQP_ERR_INVALID; }
   if (p.head_dim != d.head_dim) { *why = "params.head_dim differs from the cache's"; return AQP_ERR_INVALID; }
   if (p.num_q_heads <= 0 || p.num_q_heads % p.num_kv_heads != 0) { *why = "num_q_heads must be a positive multiple of num_kv_heads"; return AQP_ERR_INVALID; }
-  if (p.num_q_heads / p.num_kv_heads > kPfRows) { *why = "q heads per KV head above 128 are not supported"; return AQP_ERR_UNSUPPORTED; }
   if (p.causal != 0 && p.causal != 1) { *why = "causal must be 0 or 1"; return AQP_ERR_INVALID; }
   if (p.window < 0) { *why = "negative window"; return AQP_ERR_INVALID; }
   if (p.window > 0 && !p.causal) { *why = "a sliding window needs causal attention"; return AQP_ERR_UNSUPPORTED; }
@@ -208,8 +202,8 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   const int64_t total_q = num_seqs > 0 ? qsl[num_seqs] : 0;
   if (total_q > INT32_MAX / 2) return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: too many query tokens");
 
-  // ---- decode: units (sequence, KV head, head group) over their visible keys,
-  // cut into equal runs of 16-key tiles, one run per work-group.
+  // ---- decode: units (sequence, KV head, head group) over their visible keys, laid end to end
+  // and cut into equal runs of 16-key tiles, one run per work-group (one resident wave of them).
   struct Unit { int32_t seq, kvh, head0, nheads, lo, hi, q_tok; int64_t t0, ntiles; };
   // per-thread work buffers, reused across calls (the schedule is rebuilt every batch)
   static thread_local std::vector<Unit> units;
@@ -224,6 +218,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   comb.clear();
   pf.clear();
   const int32_t hpu = std::min<int32_t>(G, kMaxHeadsPerUnit);
+  const int32_t dec_lds = dec_lds_bytes(desc->head_dim, desc->mode, hpu);
   int64_t total_tiles = 0, dec_keys = 0;
   for (int32_t b = 0; b < num_seqs; ++b) {
     const int32_t L = seq_lens[b], ql = qsl[b + 1] - qsl[b];
@@ -244,8 +239,8 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   int32_t num_wgs = 0;
   if (total_tiles > 0) {
     const int64_t target = p.decode_parallelism > 0 ? p.decode_parallelism
-                                                    : (int64_t)device_cu_count() * decode_wgs_per_cu(desc->head_dim);
-    const int64_t by_size = (total_tiles * kTileKeys + kMinDecodeKeysPerWG - 1) / kMinDecodeKeysPerWG;
+                                                    : (int64_t)device_cu_count() * decode_wgs_per_cu(desc->head_dim, dec_lds);
+    const int64_t by_size = (total_tiles + kMinRunTiles - 1) / kMinRunTiles;
     int64_t P = std::max<int64_t>(1, std::min(target, by_size));
     const int64_t per = (total_tiles + P - 1) / P;
     P = (total_tiles + per - 1) / per;
@@ -300,8 +295,10 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
     while (w_cur < P) wg_start[++w_cur] = (int32_t)segs.size();
   }
 
-  // ---- prefill items: (sequence, KV head, run of query tokens), all G heads of
-  // the KV head in one item; heaviest (most keys) first.
+  // ---- prefill items: (sequence, KV head, run of query tokens, run of its q heads): all G
+  // heads of the KV head when G <= kPfRows, else one token and kPfRows heads at a time;
+  // heaviest (most keys) first.
+  const int32_t hpi = std::min<int32_t>(G, kPfRows);
   const int32_t tpi = std::max<int32_t>(1, kPfRows / G);
   for (int32_t b = 0; b < num_seqs; ++b) {
     const int32_t L = seq_lens[b], ql = qsl[b + 1] - qsl[b];
@@ -309,7 +306,9 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
     for (int32_t q0 = 0; q0 < ql; q0 += tpi) {
       const int32_t q1 = std::min(ql, q0 + tpi);
       const int32_t khi = p.causal ? (L - ql + q1) : L;  // exclusive end of the last row's keys
-      for (int32_t h = 0; h < p.num_kv_heads; ++h) pf.push_back({b, h, q0, q1, L, ql, qsl[b], khi});
+      for (int32_t h = 0; h < p.num_kv_heads; ++h)
+        for (int32_t h0 = 0; h0 < G; h0 += hpi)
+          pf.push_back({b, h, q0, q1, L, ql, qsl[b], khi, h0, std::min(hpi, G - h0), 0, 0});
     }
   }
   if (pf.size() > 1) std::stable_sort(pf.begin(), pf.end(), [&](const PfItem& x, const PfItem& y) {
@@ -376,7 +375,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   h.pf_rows = kPfRows;
   h.pf_kv_tile = kPfKvTile;
   h.heads_per_unit = kMaxHeadsPerUnit;
-  h.dec_lds_bytes = g.dec_lds_bytes;
+  h.dec_lds_bytes = dec_lds;
   h.pf_lds_bytes = g.pf_lds_bytes;
   h.num_dec_wgs = num_wgs;
   h.num_dec_segs = (int32_t)segs.size();
@@ -432,7 +431,8 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
   MISMATCH_IF(h.causal != params->causal || h.window != params->window || h.max_blocks_per_seq != params->max_blocks_per_seq, "mask / block-table shape");
   MISMATCH_IF(h.sm_scale != effective_sm_scale(*params) || h.softcap != params->softcap, "logit scale / soft-cap");
   MISMATCH_IF(h.tile_keys != kTileKeys || h.dec_iter_keys != kDecIterKeys || h.dec_waves != kDecWaves || h.pf_rows != kPfRows ||
-              h.pf_kv_tile != kPfKvTile || h.heads_per_unit != kMaxHeadsPerUnit || h.dec_lds_bytes != g.dec_lds_bytes ||
+              h.pf_kv_tile != kPfKvTile || h.heads_per_unit != kMaxHeadsPerUnit ||
+              h.dec_lds_bytes != dec_lds_bytes(desc->head_dim, desc->mode, std::min<int32_t>(params->num_q_heads / params->num_kv_heads, kMaxHeadsPerUnit)) ||
               h.pf_lds_bytes != g.pf_lds_bytes, "tile geometry");
   if ((int64_t)scratch_bytes < h.scratch_bytes)
     return fail(AQP_ERR_SCRATCH_TOO_SMALL, "aqp_paged_attention: scratch of %zu bytes, schedule needs %lld", scratch_bytes, (long long)h.scratch_bytes);

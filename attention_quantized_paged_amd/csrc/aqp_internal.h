@@ -17,24 +17,44 @@
 namespace aqp {
 
 constexpr uint32_t kMagic = 0x53505141u;  // "AQPS"
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 2;
 
 // ---- compile-time tile geometry of the kernels ----------------------------
 constexpr int kTileKeys = 16;        // keys per KV tile: one 16-row MFMA operand; block_size % 16 == 0
 constexpr int kDecIterKeys = 16;     // keys per decode iteration (one tile; PV on 16x16x16 MFMA)
-constexpr int kDecVRowPad = 32;      // bytes of padding per staged V row (spreads transposed LDS reads over banks)
-constexpr int kDecWaves = 4;         // waves per decode work-group (they split a segment's iterations)
+constexpr int kDecWaves = 4;         // compute waves per decode work-group (they split a segment's iterations)
 constexpr int kMaxHeadsPerUnit = 16; // q heads per MFMA column block
-constexpr int kPfRowsPerWave = 32;   // prefill: query rows (token, head) per wave
-constexpr int kPfWaves = 4;          // prefill: waves per work-group
-constexpr int kPfRows = kPfRowsPerWave * kPfWaves;  // query rows per prefill work item
+constexpr int kPfRows = 128;         // prefill: query rows (token, q head) per work item
+// Prefill waves per work-group: head_dim 256 gives each of 8 waves 16 rows (so a wave's
+// 16 x 256 fp32 output tile and its Q rows stay in ordinary registers at two waves per SIMD);
+// smaller head dims give each of 4 waves 32 rows, which halves the code widening per MFMA.
+constexpr int pf_waves(int head_dim) { return head_dim >= 256 ? 8 : 4; }
 constexpr int kPfKvTile = 32;        // prefill: keys staged in LDS per step
 constexpr int kPfStages = 4;         // prefill: LDS ring stages (three steps of copies in flight)
-constexpr int kMinDecodeKeysPerWG = 512;
-// Decode work-groups resident per CU for each head_dim (registers of the
-// compiled kernel: 3, 3 and 2 waves per SIMD). The default decode split uses
-// exactly one resident wave of equal work-groups.
-constexpr int decode_wgs_per_cu(int head_dim) { return head_dim <= 128 ? 3 : 2; }
+constexpr int kMinRunTiles = 32;     // decode: fewest 16-key tiles a work-group is given
+constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per compute unit (gfx950)
+
+// Decode LDS: per compute wave, a ring of dec_stages tiles (each the K and V codes of 16 keys plus
+// their per-token-head scales) and one Q slot (the q rows of one segment); then the merge area
+// where the compute waves hand their (O, m, l) to the merging wave.
+constexpr int dec_stages(int head_dim) { return head_dim >= 256 ? 2 : 3; }
+constexpr int dec_slot_bytes(int head_dim, int mode) {
+  return 2 * kDecIterKeys * head_dim + (mode == AQP_SCALE_PER_TOKEN_HEAD ? 2 * kDecIterKeys * 4 : 0);
+}
+constexpr int32_t dec_lds_bytes(int head_dim, int mode, int group_heads) {
+  return kDecWaves * (dec_stages(head_dim) * dec_slot_bytes(head_dim, mode) + group_heads * head_dim * 2) +
+         kDecWaves * group_heads * (head_dim + 2) * 4;
+}
+// Waves per SIMD the decode kernel's registers are sized for; a work-group is kDecWaves compute
+// waves and one merging wave.
+constexpr int dec_waves_per_simd(int head_dim) { return head_dim <= 128 ? 3 : 2; }
+// Decode work-groups resident per CU: the smaller of the register limit of the compiled kernel
+// and the LDS limit. The decode grid is exactly one resident wave of work-groups.
+constexpr int decode_wgs_per_cu(int head_dim, int32_t lds_bytes) {
+  return 4 * dec_waves_per_simd(head_dim) / (kDecWaves + 1) < kLdsPerCu / lds_bytes
+             ? 4 * dec_waves_per_simd(head_dim) / (kDecWaves + 1)
+             : kLdsPerCu / lds_bytes;
+}
 // Compute units of the current device (256 on MI355X; 256 when no device is visible).
 int device_cu_count();
 
@@ -50,7 +70,6 @@ struct Geometry {
   int64_t page_bytes;
   int64_t block_bytes;
   int64_t total_bytes;
-  int32_t dec_lds_bytes;      // LDS per decode work-group
   int32_t pf_lds_bytes;       // LDS per prefill work-group
 };
 
@@ -58,7 +77,7 @@ struct Geometry {
 int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why);
 
 // ---- schedule metadata -----------------------------------------------------
-// Layout: [SchedHeader][DecSeg x num_dec_segs][int32 dec_wg_start x (num_dec_wgs+1)]
+// Layout: [SchedHeader][DecSeg x num_dec_segs][int32 dec_wg_start x (num_dec_wgs + 1)]
 //         [CombItem x num_comb][PfItem x num_pf_items], each array 256-byte aligned.
 struct SchedHeader {
   uint32_t magic, version;
@@ -99,8 +118,10 @@ struct CombItem {
 // Prefill item: query tokens [q_lo, q_hi) (indices within the sequence) of
 // sequence seq, all G q heads of KV head kvh. The sequence has L keys and ql
 // queries; its first query is token q_start of q / out.
+// Prefill item: query tokens [q_lo, q_hi) of sequence seq times q heads [head0, head0 + nheads)
+// of KV head kvh; row r is token q_lo + r / nheads, head head0 + r % nheads.
 struct PfItem {
-  int32_t seq, kvh, q_lo, q_hi, L, ql, q_start, k_hi_max;
+  int32_t seq, kvh, q_lo, q_hi, L, ql, q_start, k_hi_max, head0, nheads, pad0, pad1;
 };
 
 // Scratch of a partial slot: nh = min(G, 16) heads x (D floats of O, then m, l).

@@ -11,30 +11,29 @@
 //
 // gfx950 mapping, per work-group of 4 waves and per schedule segment
 // (keys [k_lo, k_hi) of one (sequence, KV head, group of <= 16 q heads)):
-//  * a wave takes 16-key tiles w, w+4, ... of the segment;
-//  * K: each lane loads D/4 contiguous code bytes of one key straight from HBM
-//    (16 keys x D bytes of a page per tile); the codes are widened to bf16 in
-//    registers and fed to v_mfma_f32_16x16x32_bf16 as S^T = K * Q^T with the
-//    group's q heads as the 16 MFMA columns;
+//  * a wave takes 16-key tiles w, w+4, ... of each of the work-group's segments, one
+//    stream of tiles across segment boundaries;
+//  * each tile's K and V codes (and per-token-head scales) are copied straight from HBM
+//    into the wave's own LDS ring with global_load_lds (16-byte chunks, XOR-swizzled
+//    per row so the operand reads below are free of bank conflicts), dec_stages(D) - 1
+//    tiles ahead of the one being computed; the stream does not drain at segment ends,
+//    so the copies of the next segment overlap the merge of the current one. The
+//    segment's Q rows travel the same way, into a per-wave Q slot;
+//  * K: each lane reads D/4 code bytes of one key, widens them to bf16 in registers and
+//    feeds v_mfma_f32_16x16x32_bf16 as S^T = K * Q^T with the group's q heads as the
+//    16 MFMA columns;
 //  * scale folding: per tensor, k_scale goes into the logit scale and v_scale
 //    into the final normalisation; per token-head, each key's scale multiplies
 //    its logit and each value's scale its probability;
-//  * softmax: running max / sum in the exp2 domain, the max reduced across the
-//    four lanes that share a head with two xor shuffles;
-//  * V: the tile's codes are staged in the wave's own LDS buffer and read back
-//    with ds_read_b64_tr_b8, which hands each lane 4 keys of one head-dim column
-//    for two column tiles at once: the key-contiguous operand that
-//    O^T = V^T * P^T on v_mfma_f32_16x16x16_bf16 needs, so the probabilities
-//    stay in the registers the QK^T product left them in;
+//  * softmax: running max / sum in the exp2 domain, reduced across the four lanes that
+//    share a head with lane permutes; lazy rescaling;
+//  * V: ds_read_b64_tr_b8 hands each lane 4 keys of one head-dim column for two column
+//    tiles at once: the key-contiguous operand that O^T = V^T * P^T on
+//    v_mfma_f32_16x16x16_bf16 needs, so the probabilities stay in the registers the
+//    QK^T product left them in;
 //  * the four waves' (m, l, O) are merged in LDS; the result is either the
 //    output row (bf16) or a partial slot for the split-KV merge kernel.
 #include "device_common.h"
-
-// Decode waves per SIMD the register allocation targets for head_dim <= 128
-// (head_dim 256 targets 2).
-#ifndef AQP_DECODE_WAVES_PER_EU
-#define AQP_DECODE_WAVES_PER_EU 3
-#endif
 
 namespace aqp {
 
@@ -43,7 +42,7 @@ struct DecArgs {
   const uint16_t* q;
   const int32_t* block_tables;
   const DecSeg* segs;
-  const int32_t* wg_start;
+  const int32_t* wg_start;  // segments of work-group b: [wg_start[b], wg_start[b + 1])
   float* scratch;
   uint16_t* out;
   int64_t page_bytes, block_bytes;
@@ -53,64 +52,238 @@ struct DecArgs {
   float v_scale;      // per tensor; 1 per token-head
 };
 
-template <int D, int MODE>
-struct TileRegs {
-  static constexpr int KV4 = D / 64;  // uint4 per lane per 16-key tile (D/4 bytes)
-  uint4 k[KV4];                       // K codes: one key row slice per lane (MFMA A layout)
-  uint4 v[KV4];                       // V codes: coalesced slices of the tile
-  float4 ks, vs;                      // per token-head scales of the lane's 4 keys
-  bool ok;                            // the tile's block id is inside the pool
-};
+// Stored 16-byte chunk of logical chunk c in staged row `row` (rows of D bytes): c ^ dec_swz(row).
+// Rows that fall on the same LDS banks (same row / (256 / D) residue) get distinct offsets, so the
+// 16 rows of a K operand read and the 4 x 2 rows of a transposed V read hit distinct banks.
+template <int D>
+__device__ __forceinline__ int dec_swz(int row) {
+  constexpr int CPR = D / 16;
+  constexpr int RPB = D >= 256 ? 1 : 256 / D;
+  return (row / RPB) % CPR;
+}
 
-template <int D, int DT, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? AQP_DECODE_WAVES_PER_EU : 2))) void decode_kernel(DecArgs a) {
-  constexpr int KV4 = D / 64;
+// LDS barrier for the work-group that orders LDS traffic only (the global stores of the merge
+// need no ordering against the other waves, and the copies in flight must not be waited for).
+__device__ __forceinline__ void block_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Merge of the four compute waves' (O, m, l) of one segment, left in LDS as [wave][head][D + 2],
+// into the output rows (bf16) or the segment's partial slot. Lane (r16, kg) handles head r16 and
+// head-dim elements t * 16 + 4 kg + r, the layout the waves' accumulators have.
+template <int D>
+__device__ __forceinline__ void merge_store(const DecArgs& a, const float* mg, int gh, const DecSeg& sg, int r16, int kg) {
+  constexpr int NT = D / 16;
+  if (r16 >= sg.nheads) return;
+  float mw[kDecWaves], lw[kDecWaves];
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) {
+    const float* src = mg + (w * gh + r16) * (D + 2);
+    mw[w] = src[D];
+    lw[w] = src[D + 1];
+  }
+  float M = mw[0];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, mw[w]);
+  const float M_use = M == -INFINITY ? 0.0f : M;
+  float f[kDecWaves], L = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) {
+    f[w] = fast_exp2(mw[w] - M_use);
+    L += f[w] * lw[w];
+  }
+  f32x4 o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float* src = mg + (w * gh + r16) * (D + 2) + t * 16 + 4 * kg;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[t][r] += f[w] * src[r];
+    }
+  }
+  const int hq = sg.kvh * a.group + sg.head0 + r16;
+  if (sg.part < 0) {
+    const float norm = a.v_scale / L;
+    uint16_t* op = a.out + ((int64_t)sg.q_tok * a.num_q_heads + hq) * D;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint2 w;
+      w.x = (uint32_t)f32_to_bf16_rne(o[t][0] * norm) | ((uint32_t)f32_to_bf16_rne(o[t][1] * norm) << 16);
+      w.y = (uint32_t)f32_to_bf16_rne(o[t][2] * norm) | ((uint32_t)f32_to_bf16_rne(o[t][3] * norm) << 16);
+      *(uint2*)(op + t * 16 + 4 * kg) = w;
+    }
+  } else {
+    // partial slot: O at [part][head][D], (m, l) at [part][head][2] after all O slots
+    float* pp = a.scratch + ((int64_t)sg.part * a.group_heads + r16) * D;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      *(float4*)(pp + t * 16 + 4 * kg) = make_float4(o[t][0] * a.v_scale, o[t][1] * a.v_scale, o[t][2] * a.v_scale,
+                                                     o[t][3] * a.v_scale);
+    if (kg == 0) {
+      float* ml = a.scratch + (int64_t)a.num_parts * a.group_heads * D + ((int64_t)sg.part * a.group_heads + r16) * 2;
+      ml[0] = M;
+      ml[1] = L;
+    }
+  }
+}
+
+template <int D, int DT, int MODE, bool CAP>
+__global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_per_eu(dec_waves_per_simd(D)))) void decode_kernel(DecArgs a) {
   constexpr int NT = D / 16;   // 16-wide head-dim tiles of the output
   constexpr int QS = D / 32;   // 32-deep MFMA steps of QK^T
-  constexpr int VROW = D + kDecVRowPad;  // staged V row stride in LDS
+  constexpr int CPR = D / 16;  // 16-byte chunks per staged row
   constexpr int STEP = kDecWaves * kDecIterKeys;  // keys between a wave's consecutive tiles
+  constexpr int PTH = MODE == AQP_SCALE_PER_TOKEN_HEAD ? 1 : 0;
+  constexpr int NS = dec_stages(D);               // ring slots per wave
+  constexpr int NQ = 1;                           // Q slots per wave
+  constexpr int TB = kDecIterKeys * D;            // bytes of one K (or V) tile
+  constexpr int KI = TB / 1024;                   // 1 KB copies per K (or V) tile
+  constexpr int SLOT = dec_slot_bytes(D, MODE);   // K tile, V tile, K scales, V scales
+  constexpr int IPT = 2 * KI + PTH;               // copies per tile
+  static_assert(KI >= 1 && IPT * (NS - 1) <= 15, "tile copies and waits");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
   const int kg = lane >> 4;
-  uint8_t* vbuf = smem + wave * (kDecIterKeys * VROW);
-  // where this lane's V chunks go in the padded staging rows
-  int vdst[KV4];
-#pragma unroll
-  for (int c = 0; c < KV4; ++c) {
-    const int o = lane * 16 + c * 1024;
-    vdst[c] = (o / D) * VROW + (o % D);
-  }
-  // transposed-read address of this lane: rows i = 0..3 and 4..7 are keys 4kg + (i & 3), the
-  // second four 16 columns further, so one read yields the operands of two head-dim tiles
-  const int tr_i = r16 >> 1;
-  const int tr_off = (4 * kg + (tr_i & 3)) * VROW + (tr_i >> 2) * 16 + (r16 & 1) * 8;
+  const int gh = a.group_heads;
+  const int QB = gh * D * 2;  // bytes of a Q slot: the group's q rows, bf16
+  uint8_t* ring = smem + wave * (NS * SLOT);
+  uint8_t* qslots = smem + kDecWaves * NS * SLOT + wave * (NQ * QB);
+  float* mg = (float*)(smem + kDecWaves * NS * SLOT + kDecWaves * NQ * QB);  // [wave][head][D + 2]
+  const uint32_t ring_lds = lds_addr(ring), q_lds = lds_addr(qslots);
   const int s_begin = as_const(a.wg_start)[blockIdx.x], s_end = as_const(a.wg_start)[blockIdx.x + 1];
-  // without a soft-cap, log2(e) folds into the logit scale
-  const float xscale = a.softcap > 0.0f ? a.logit_scale : a.logit_scale * kLog2e;
 
-  for (int si = s_begin; si < s_end; ++si) {
-    const DecSeg sg = load_const(as_const(a.segs) + si);
-    const int head = sg.head0 + r16;
-    const bool head_ok = r16 < sg.nheads;
-    const int hq = sg.kvh * a.group + head;
-    // Q^T operand: lane (column head r16, group kg) holds q[head][kg*D/4 + 8*st + 0..7] for step st.
-    bf16x8 qb[QS];
-    {
-      const uint16_t* qp = a.q + ((int64_t)sg.q_tok * a.num_q_heads + (head_ok ? hq : sg.kvh * a.group)) * D + kg * (D / 4);
-#pragma unroll
-      for (int st = 0; st < QS; ++st) {
-        uint4 u = *(const uint4*)(qp + st * 8);
-        if (!head_ok) u = make_uint4(0, 0, 0, 0);
-        qb[st] = __builtin_bit_cast(bf16x8, u);
-      }
+  if (wave == kDecWaves) {
+    // ---- the merging wave: takes part in the two barriers of every segment, merges the compute
+    // waves' (O, m, l) and writes the result while they go on with the next segment (so the
+    // stores never hold up a wave that has copies in flight)
+    for (int si = s_begin; si < s_end; ++si) {
+      const DecSeg sg = load_const(as_const(a.segs) + si);
+      block_sync_lds();
+      block_sync_lds();
+      merge_store<D>(a, mg, gh, sg, r16, kg);
     }
-    const cptr<int32_t> bt = as_const(a.block_tables) + (int64_t)sg.seq * a.max_blocks;
-    const uint8_t* kbase = a.cache + (int64_t)sg.kvh * a.page_bytes;
-    const uint8_t* vbase = a.cache + (int64_t)(a.num_kv_heads + sg.kvh) * a.page_bytes;
+    return;
+  }
+
+  // transposed-read address of this lane: rows i = 0..3 and 4..7 are keys 4kg + (i & 3) at
+  // logical chunks 2 t2 and 2 t2 + 1, so one read yields the operands of two head-dim tiles
+  const int tr_i = r16 >> 1;
+  const int tr_row = 4 * kg + (tr_i & 3);
+  const int tr_hi = tr_i >> 2;
+  const int tr_base = tr_row * D + (r16 & 1) * 8;
+  const int tr_swz = dec_swz<D>(tr_row);
+  const int k_swz = dec_swz<D>(r16);
+  // byte offset, within a tile's 16 rows of a page, of this lane's 16-byte chunk in copy i:
+  // LDS chunk q = 64 i + lane holds logical chunk (q % CPR) ^ dec_swz(row) of row q / CPR
+  int dma_off[KI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int q = 64 * i + lane;
+    dma_off[i] = (q / CPR) * D + (((q % CPR) ^ dec_swz<D>(q / CPR)) << 4);
+  }
+
+  // without a soft-cap, log2(e) folds into the logit scale
+  const float xscale = CAP ? a.logit_scale : a.logit_scale * kLog2e;
+
+  struct Pos { int k0, bi, r0; };
+  auto advance = [&](Pos p) {
+    p.k0 += STEP;
+    p.r0 += STEP;
+    while (p.r0 >= a.block_size) { p.r0 -= a.block_size; ++p.bi; }
+    return p;
+  };
+  // the wave's first tile of a segment and its tile count there (iterations it = w, w+4, ...)
+  auto first_pos = [&](const DecSeg& sg, Pos& p) {
     const int it_base = (sg.k_lo / kTileKeys) * kTileKeys;
     const int n_iter = (sg.k_hi - it_base + kDecIterKeys - 1) / kDecIterKeys;
+    p.k0 = it_base + wave * kDecIterKeys;
+    p.bi = p.k0 / a.block_size;
+    p.r0 = p.k0 - p.bi * a.block_size;
+    return wave < n_iter ? (n_iter - wave + kDecWaves - 1) / kDecWaves : 0;
+  };
+  // ---- issue side: the wave's tile stream, walked ahead of the compute side
+  int is_si = s_begin, is_left = 0, q_issued = 0, n_issued = 0;
+  Pos is_p = {0, 0, 0};
+  DecSeg is_sg = {};
+  cptr<int32_t> is_bt = as_const(a.block_tables);
+  const uint8_t* is_kv = a.cache;  // K page of the segment's KV head in block 0
+  int32_t is_blk = 0;              // block-table entry of the next tile (read one tile ahead)
+  bool is_new = false;             // the next tile opens a segment: its Q rows go first
+  uint32_t is_slot = 0;            // ring byte offset of the next tile
+  uint64_t ok_bits = 0;            // bit (n & 63): tile n lies in a valid block
+  // moves the cursor to this wave's first tile at or after segment si
+  auto seek = [&](int si) {
+    for (; si < s_end; ++si) {
+      is_sg = load_const(as_const(a.segs) + si);
+      is_left = first_pos(is_sg, is_p);
+      if (is_left > 0) {
+        is_si = si;
+        is_new = true;
+        is_bt = as_const(a.block_tables) + (int64_t)is_sg.seq * a.max_blocks;
+        is_kv = a.cache + (int64_t)is_sg.kvh * a.page_bytes;
+        is_blk = is_bt[is_p.bi];
+        return;
+      }
+    }
+    is_si = s_end;
+    is_left = 0;
+  };
+  // issues the next tile if its ring slot (and, for a new segment, a Q slot) is free
+  auto issue_next = [&](int n_done, int q_read) {
+    if (is_left <= 0 || n_issued - n_done >= NS) return;
+    if (is_new) {
+      if (q_issued - q_read >= NQ) return;
+      // the segment's q rows, contiguous: [nheads][D] bf16 into Q slot q_issued % NQ
+      const int nbytes = is_sg.nheads * D * 2;
+      const uint8_t* src = (const uint8_t*)(a.q + ((int64_t)is_sg.q_tok * a.num_q_heads + is_sg.kvh * a.group + is_sg.head0) * D);
+      const uint32_t dst = q_lds + (uint32_t)((q_issued % NQ) * QB);
+      for (int o = 0; o < nbytes; o += 1024)
+        if (o + lane * 16 < nbytes) dma16_to_lds(src + o + lane * 16, dst + (uint32_t)o);
+      ++q_issued;
+      is_new = false;
+    }
+    // an entry outside the pool masks its tile instead of reading outside the cache
+    const bool ok = (uint32_t)is_blk < (uint32_t)a.num_blocks;
+    ok_bits |= (uint64_t)ok << (n_issued & 63);
+    const uint8_t* kpage = is_kv + (uint64_t)(ok ? (uint32_t)is_blk : 0u) * (uint64_t)a.block_bytes +
+                           (int64_t)is_p.r0 * D;
+    const uint8_t* vpage = kpage + (int64_t)a.num_kv_heads * a.page_bytes;
+    const uint32_t slot = ring_lds + is_slot;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      dma16_to_lds(kpage + dma_off[i], slot + (uint32_t)(1024 * i));
+      dma16_to_lds(vpage + dma_off[i], slot + (uint32_t)(TB + 1024 * i));
+    }
+    if constexpr (PTH) {
+      // lanes 0..3: the 16 K scales, lanes 4..7: the 16 V scales
+      const uint8_t* sp = ((lane & 4) ? vpage : kpage) + (int64_t)(a.block_size - is_p.r0) * D + 4 * (is_p.r0 + 4 * (lane & 3));
+      if (lane < 8) dma16_to_lds(sp, slot + (uint32_t)(2 * TB));
+    }
+    ++n_issued;
+    is_slot = is_slot + SLOT == NS * SLOT ? 0u : is_slot + SLOT;
+    if (--is_left > 0) {
+      is_p = advance(is_p);
+      is_blk = is_bt[is_p.bi];  // needed only at the next issue: its latency hides behind a tile
+    } else {
+      seek(is_si + 1);
+    }
+  };
+
+  seek(s_begin);
+#pragma unroll
+  for (int k = 0; k < NS; ++k) issue_next(0, 0);
+
+  // ---- compute side
+  int n_done = 0, q_read = 0;
+  uint32_t c_slot = 0;
+  bf16x8 qb[QS];
+  for (int si = s_begin; si < s_end; ++si) {
+    const DecSeg sg = load_const(as_const(a.segs) + si);
+    const bool head_ok = r16 < sg.nheads;
+    Pos pc;
+    const int n_my = first_pos(sg, pc);
 
     float m = -INFINITY;  // reference max (log2 domain) of this lane's head
     float l = 0.0f;       // sum of this lane's probabilities relative to m
@@ -118,69 +291,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // position of a tile: logical block index and first row, advanced incrementally
-    struct Pos { int k0, bi, r0; };
-    auto advance = [&](Pos p) {
-      p.k0 += STEP;
-      p.r0 += STEP;
-      while (p.r0 >= a.block_size) { p.r0 -= a.block_size; ++p.bi; }
-      return p;
-    };
-
-    auto load = [&](TileRegs<D, MODE>& R, const Pos& p) {
-      int32_t blk = bt[p.bi];
-      // an entry outside the pool masks its tile instead of reading outside the cache
-      R.ok = (uint32_t)blk < (uint32_t)a.num_blocks;
-      if (!R.ok) blk = 0;
-      const int64_t pb = (int64_t)blk * a.block_bytes;
-      const uint8_t* kp = kbase + pb + (int64_t)(p.r0 + r16) * D + kg * (D / 4);
-      const uint8_t* vp = vbase + pb + (int64_t)p.r0 * D + lane * 16;
+    for (int k = 0; k < n_my; ++k) {
+      // this tile's copies are done once only the later tiles' copies are outstanding (the Q
+      // copies and merge stores are not counted, which only makes the wait longer)
+      wait_tiles_ahead<IPT, NS>(n_issued - n_done - 1);
+      if (k == 0) {
+        // Q^T operand: lane (column head r16, group kg) holds q[head][kg*D/4 + 8*st + 0..7]
+        const uint8_t* qp = qslots + (q_read % NQ) * QB + r16 * (D * 2) + kg * (D / 2);
 #pragma unroll
-      for (int c = 0; c < KV4; ++c) {
-        R.k[c] = *(const uint4*)(kp + c * 16);
-        R.v[c] = *(const uint4*)(vp + c * 1024);
+        for (int st = 0; st < QS; ++st) {
+          uint4 u = *(const uint4*)(qp + st * 16);
+          if (!head_ok) u = make_uint4(0, 0, 0, 0);
+          qb[st] = __builtin_bit_cast(bf16x8, u);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        ++q_read;
+        issue_next(n_done, q_read);  // a copy held back for want of a Q slot
       }
-      if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
-        const int64_t so = (int64_t)a.block_size * D + 4 * (p.r0 + 4 * kg);
-        R.ks = *(const float4*)(kbase + pb + so);
-        R.vs = *(const float4*)(vbase + pb + so);
-      }
-    };
+      const uint8_t* kl = ring + c_slot;
+      const uint8_t* vl = kl + TB;
+      const bool ok = (ok_bits >> (n_done & 63)) & 1;
 
-    auto compute = [&](const TileRegs<D, MODE>& R, const Pos& p) {
       // ---- S^T = K * Q^T: lane holds keys k0 + 4kg + r of head r16
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < QS; ++st) {
-        const uint4 w = R.k[st / 2];
-        const uint32_t w0 = (st & 1) ? w.z : w.x, w1 = (st & 1) ? w.w : w.y;
-        s = mfma16x16x32(widen8<DT>(w0, w1), qb[st], s);
+      for (int c2 = 0; c2 < QS / 2; ++c2) {
+        const uint4 w = *(const uint4*)(kl + r16 * D + (((kg * (QS / 2) + c2) ^ k_swz) << 4));
+        s = mfma16x16x32(widen8<DT>(w.x, w.y), qb[2 * c2], s);
+        s = mfma16x16x32(widen8<DT>(w.z, w.w), qb[2 * c2 + 1], s);
+      }
+      // V^T operands: transposed reads issued now, used after the softmax
+      i32x2 vw[NT / 2];
+#pragma unroll
+      for (int t2 = 0; t2 < NT / 2; ++t2) vw[t2] = lds_read_tr8(vl + tr_base + (((2 * t2 + tr_hi) ^ tr_swz) << 4));
+      float4 ks, vs;
+      if constexpr (PTH) {
+        ks = *(const float4*)(kl + 2 * TB + 16 * kg);
+        vs = *(const float4*)(kl + 2 * TB + 64 + 16 * kg);
       }
       float x[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[r] = s[r] * xscale;
-      if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
-        x[0] *= R.ks.x; x[1] *= R.ks.y; x[2] *= R.ks.z; x[3] *= R.ks.w;
+      if constexpr (PTH) {
+        x[0] *= ks.x; x[1] *= ks.y; x[2] *= ks.z; x[3] *= ks.w;
       }
-      if (a.softcap > 0.0f) {
+      if constexpr (CAP) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] = a.softcap * kLog2e * tanh_via_exp2(x[r] * a.inv_softcap);
       }
-      // masking is needed only on the segment's edge tiles (and tiles of an invalid block)
-      const bool full = R.ok && p.k0 >= sg.k_lo && p.k0 + kTileKeys <= sg.k_hi;
+      // masking is needed only on the segment's edge tiles (and tiles of an invalid block); rows
+      // outside the range may hold unwritten bytes: their logits are replaced, their V codes
+      // masked to zero and (per token-head) their scales replaced, so no NaN reaches the sums
+      const bool full = ok && pc.k0 >= sg.k_lo && pc.k0 + kTileKeys <= sg.k_hi;
       uint32_t vmask = 0xFFFFFFFFu;
       if (!full) {
         vmask = 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = p.k0 + 4 * kg + r;
-          const bool ok = R.ok && key >= sg.k_lo && key < sg.k_hi;
-          x[r] = ok ? x[r] : -INFINITY;
-          if (ok) vmask |= 0xFFu << (8 * r);
+          const int key = pc.k0 + 4 * kg + r;
+          const bool kok = ok && key >= sg.k_lo && key < sg.k_hi;
+          x[r] = kok ? x[r] : -INFINITY;
+          if (kok) vmask |= 0xFFu << (8 * r);
         }
       }
-      // rows outside the range may hold unwritten bytes: their V codes are masked to zero and
-      // (per token-head) their scale is replaced, so no NaN pattern reaches the sums
       const float mx = max_over_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
       // lazy rescaling: the reference max moves (and O, l are rescaled) only when some head's
       // max exceeds it by more than 2^8, so probabilities stay <= 256 and the common case
@@ -198,8 +371,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
 #pragma unroll
       for (int r = 0; r < 4; ++r) p4[r] = fast_exp2(x[r] - m_use);
       l += (p4[0] + p4[1]) + (p4[2] + p4[3]);
-      if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
-        float4 vs = R.vs;
+      if constexpr (PTH) {
         if (!full) {
           vs.x = (vmask & 0xFFu) ? vs.x : 0.0f;
           vs.y = (vmask & 0xFF00u) ? vs.y : 0.0f;
@@ -211,113 +383,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
       bf16x4 pb;
 #pragma unroll
       for (int r = 0; r < 4; ++r) pb[r] = (__bf16)p4[r];
-      // ---- stage the V tile, read it transposed: O^T[d][head] += V^T[d][keys] P^T[keys][head]
-#pragma unroll
-      for (int c = 0; c < KV4; ++c) *(uint4*)(vbuf + vdst[c]) = R.v[c];
-      wave_lds_sync();
+      // ---- O^T[d][head] += V^T[d][keys] P^T[keys][head]
 #pragma unroll
       for (int t2 = 0; t2 < NT / 2; ++t2) {
-        const i32x2 v = lds_read_tr8(vbuf + tr_off + t2 * 32);
-        acc[2 * t2] = mfma16x16x16(widen4v<DT>((uint32_t)v.x & vmask), pb, acc[2 * t2]);
-        acc[2 * t2 + 1] = mfma16x16x16(widen4v<DT>((uint32_t)v.y & vmask), pb, acc[2 * t2 + 1]);
+        acc[2 * t2] = mfma16x16x16(widen4v<DT>((uint32_t)vw[t2].x & vmask), pb, acc[2 * t2]);
+        acc[2 * t2 + 1] = mfma16x16x16(widen4v<DT>((uint32_t)vw[t2].y & vmask), pb, acc[2 * t2 + 1]);
       }
-      wave_lds_sync();
-    };
-
-    // software pipeline: the loads of the wave's next tile are in flight while
-    // the current one is computed
-    if (wave < n_iter) {
-      Pos p0, p1;
-      p0.k0 = it_base + wave * kDecIterKeys;
-      p0.bi = p0.k0 / a.block_size;
-      p0.r0 = p0.k0 - p0.bi * a.block_size;
-      TileRegs<D, MODE> R0, R1;
-      load(R0, p0);
-      int it = wave;
-      while (true) {
-        p1 = advance(p0);
-        const bool more1 = it + kDecWaves < n_iter;
-        if (more1) load(R1, p1);
-        compute(R0, p0);
-        if (!more1) break;
-        it += kDecWaves;
-        p0 = advance(p1);
-        const bool more0 = it + kDecWaves < n_iter;
-        if (more0) load(R0, p0);
-        compute(R1, p1);
-        if (!more0) break;
-        it += kDecWaves;
-      }
+      ++n_done;
+      c_slot = c_slot + SLOT == NS * SLOT ? 0u : c_slot + SLOT;
+      pc = advance(pc);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue_next(n_done, q_read);  // into the slot this tile used: every read of it is complete
     }
 
-    // ---- merge the four waves: l over the lanes of a head, then across waves in LDS
+    // ---- hand (O, m, l) to the fetching wave, which merges the four waves and writes the
+    // result while these waves go on with the next segment
     l = sum_over_rows(l);
-    __syncthreads();  // every wave is done with its V staging buffer
-    float* mg = (float*)smem;  // [wave-1][head][D + 2]
-    if (wave > 0) {
-      float* dst = mg + ((wave - 1) * kMaxHeadsPerUnit + r16) * (D + 2);
+    block_sync_lds();  // the fetching wave has read the previous segment's values
+    if (r16 < gh) {
+      float* dst = mg + (wave * gh + r16) * (D + 2);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) dst[t * 16 + 4 * kg + r] = acc[t][r];
       if (kg == 0) { dst[D] = m; dst[D + 1] = l; }
     }
-    __syncthreads();
-    if (wave == 0) {
-      float mw[kDecWaves], lw[kDecWaves];
-      mw[0] = m; lw[0] = l;
-#pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) {
-        const float* src = mg + ((w - 1) * kMaxHeadsPerUnit + r16) * (D + 2);
-        mw[w] = src[D]; lw[w] = src[D + 1];
-      }
-      float M = mw[0];
-#pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, mw[w]);
-      const float M_use = M == -INFINITY ? 0.0f : M;
-      float f[kDecWaves], L = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) { f[w] = fast_exp2(mw[w] - M_use); L += f[w] * lw[w]; }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        acc[t] *= f[0];
-#pragma unroll
-        for (int w = 1; w < kDecWaves; ++w) {
-          const float* src = mg + ((w - 1) * kMaxHeadsPerUnit + r16) * (D + 2) + t * 16 + 4 * kg;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[t][r] += f[w] * src[r];
-        }
-      }
-      if (head_ok) {
-        if (sg.part < 0) {
-          const float norm = a.v_scale / L;
-          uint16_t* op = a.out + ((int64_t)sg.q_tok * a.num_q_heads + hq) * D;
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            uint2 w;
-            w.x = (uint32_t)f32_to_bf16_rne(acc[t][0] * norm) | ((uint32_t)f32_to_bf16_rne(acc[t][1] * norm) << 16);
-            w.y = (uint32_t)f32_to_bf16_rne(acc[t][2] * norm) | ((uint32_t)f32_to_bf16_rne(acc[t][3] * norm) << 16);
-            *(uint2*)(op + t * 16 + 4 * kg) = w;
-          }
-        } else {
-          // partial slot: O at [part][head][D], (m, l) at [part][head][2] after all O slots
-          float* pp = a.scratch + ((int64_t)sg.part * a.group_heads + r16) * D;
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            float4 w = make_float4(acc[t][0] * a.v_scale, acc[t][1] * a.v_scale, acc[t][2] * a.v_scale,
-                                   acc[t][3] * a.v_scale);
-            *(float4*)(pp + t * 16 + 4 * kg) = w;
-          }
-          if (kg == 0) {
-            float* ml = a.scratch + (int64_t)a.num_parts * a.group_heads * D + ((int64_t)sg.part * a.group_heads + r16) * 2;
-            ml[0] = M;
-            ml[1] = L;
-          }
-        }
-      }
-    }
-    __syncthreads();  // the merge area is reused as staging by the next segment
+    block_sync_lds();
   }
+  // every copy this wave issued has landed before it exits
+  wait_vmcnt(0);
 }
 
 // Split-KV merge: one wave per (item, head). M = max_s m_s;
@@ -378,7 +472,10 @@ static int launch_dec(const AttnArgs& a, hipStream_t st) {
   d.softcap = a.softcap;
   d.inv_softcap = a.softcap > 0.0f ? 1.0f / a.softcap : 0.0f;
   d.v_scale = MODE == AQP_SCALE_PER_TENSOR ? a.v_scale : 1.0f;
-  hipLaunchKernelGGL((decode_kernel<D, DT, MODE>), dim3(h.num_dec_wgs), dim3(256), h.dec_lds_bytes, st, d);
+  if (a.softcap > 0.0f)
+    hipLaunchKernelGGL((decode_kernel<D, DT, MODE, true>), dim3(h.num_dec_wgs), dim3((kDecWaves + 1) * 64), h.dec_lds_bytes, st, d);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, DT, MODE, false>), dim3(h.num_dec_wgs), dim3((kDecWaves + 1) * 64), h.dec_lds_bytes, st, d);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("aqp_paged_attention: decode launch failed: %s", hipGetErrorString(e));

@@ -52,8 +52,9 @@ __device__ __forceinline__ void widen4(uint32_t w, uint32_t& lo, uint32_t& hi) {
     const float f1 = (float)(((int32_t)(w << 16)) >> 24);
     const float f2 = (float)(((int32_t)(w << 8)) >> 24);
     const float f3 = (float)(((int32_t)w) >> 24);
-    lo = (__builtin_bit_cast(uint32_t, f0) >> 16) | (__builtin_bit_cast(uint32_t, f1) & 0xFFFF0000u);
-    hi = (__builtin_bit_cast(uint32_t, f2) >> 16) | (__builtin_bit_cast(uint32_t, f3) & 0xFFFF0000u);
+    // one byte permute packs the upper halves of two floats
+    lo = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1), __builtin_bit_cast(uint32_t, f0), 0x07060302u);
+    hi = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f3), __builtin_bit_cast(uint32_t, f2), 0x07060302u);
   }
 }
 
@@ -114,6 +115,23 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 
 // LDS byte address of a pointer into the dynamic shared allocation.
+// Compile-time form of the wait above.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_c() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait for the oldest of this wave's tile copies when `ahead` later tiles (ipt copies each) may
+// stay in flight; ahead < ns.
+template <int IPT, int NS>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  static_assert(NS >= 2 && NS <= 3, "ring depth");
+  if (NS == 3 && ahead >= 2) wait_vmcnt_c<IPT * (NS - 1)>();
+  else if (ahead >= 1) wait_vmcnt_c<IPT>();
+  else wait_vmcnt_c<0>();
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

@@ -7,16 +7,17 @@
 // case the "Fix CPU FP8 attention scheduler scratch sizing" page, vllm PR
 // 50194, stresses with block_size 2176 and head_size 256).
 //
-// gfx950 mapping: one work-group of 4 waves per schedule item (a run of query
-// tokens of one sequence times the q heads of one KV head = up to 128 query
-// rows, token-major, so all rows share the K/V tiles). Each step stages the
-// codes of 32 keys of K and V (and their per-token-head scales) in LDS,
-// double-buffered, with one cooperative 16-byte load per chunk; every wave
-// then runs, for its 32 rows (two 16-row MFMA column blocks):
+// gfx950 mapping: one work-group per schedule item (a run of query tokens of
+// one sequence times a run of the q heads of one KV head = up to 128 query rows,
+// token-major, so all rows share the K/V tiles); 4 waves of 32 rows, or 8 waves
+// of 16 rows at head_dim 256 (two waves per SIMD). Each step copies
+// the codes of 32 keys of K and V (and their per-token-head scales) straight
+// from HBM into a 4-stage LDS ring (global_load_lds, XOR-swizzled 16-byte
+// chunks); every wave then runs, for its rows (16-row MFMA column blocks):
 //   S^T = K * Q^T   (A = K codes read from LDS and widened to bf16; B = Q^T in
 //                    registers for the whole item)
 //   online softmax per row (4 keys per lane per 16-key tile, max over the
-//                    4 lanes of a row with xor shuffles)
+//                    4 lanes of a row with lane permutes)
 //   O^T += V^T * P^T (A = V codes via ds_read_b64_tr_b8, B = the
 //                    probabilities exactly where S^T left them)
 // The 32-key step is the kernel's compile-time tile; the schedule records it
@@ -51,17 +52,20 @@ __device__ __forceinline__ int swz(int row) {
   return ((row / RPL) % CPR) ^ (((row >> 4) & 1) * (CPR / 2));
 }
 
-template <int D, int DT, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : (D <= 128 ? 2 : 1)))) void prefill_kernel(PfArgs a) {
+template <int D, int DT, int MODE, bool CAP>
+__global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 2))) void prefill_kernel(PfArgs a) {
   constexpr int NT = D / 16;
   constexpr int QS = D / 32;
+  constexpr int WAVES = pf_waves(D);
+  constexpr int RT = kPfRows / (16 * WAVES);      // 16-row MFMA column blocks per wave
+  constexpr int RPW = 16 * RT;                    // query rows per wave
   constexpr int KT = kPfKvTile;                   // keys per step (two 16-key tiles)
   constexpr int NS = kPfStages;                   // LDS ring stages
   constexpr int CPR = D / 16;                     // 16-byte chunks per row
   constexpr int STAGE = 2 * KT * D + 2 * KT * 4;  // K codes, V codes, K scales, V scales
   constexpr int KV_INSTR = KT * CPR / 64;         // 1 KB copies per K (or V) step
-  constexpr int IPW = 2 * KV_INSTR / 4;           // K+V copies per wave per step
-  static_assert(IPW >= 1 && (2 * KV_INSTR) % 4 == 0, "copies must split evenly over 4 waves");
+  constexpr int IPW = 2 * KV_INSTR / WAVES;       // K+V copies per wave per step
+  static_assert(IPW >= 1 && (2 * KV_INSTR) % WAVES == 0, "copies must split evenly over the waves");
   constexpr int PTH = MODE == AQP_SCALE_PER_TOKEN_HEAD ? 1 : 0;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
@@ -71,23 +75,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
   const int kg = lane >> 4;
   const PfItem it = load_const(as_const(a.items) + blockIdx.x);
   const int G = a.group;
+  const int nh = it.nheads;  // q heads per token in this item
   const int ntok = it.q_hi - it.q_lo;
   const cptr<int32_t> bt = as_const(a.block_tables) + (int64_t)it.seq * a.max_blocks;
   const uint8_t* kbase = a.cache + (int64_t)it.kvh * a.page_bytes;
   const uint8_t* vbase = a.cache + (int64_t)(a.num_kv_heads + it.kvh) * a.page_bytes;
   const uint32_t lds0 = lds_addr(smem);
-  // copies this wave issues per step: its share of K/V, plus the scale copy on wave 3
-  const int ipw_me = IPW + ((PTH && wave == 3) ? 1 : 0);
+  // copies this wave issues per step: its share of K/V, plus the scale copy on the last wave
+  const int ipw_me = IPW + ((PTH && wave == WAVES - 1) ? 1 : 0);
 
-  // ---- rows of this lane (as MFMA column r16 of row tiles 0, 1)
-  int lo_r[2], hi_r[2];
-  bool row_ok[2];
-  int64_t orow[2];
-  bf16x8 qb[2][QS];
+  // ---- rows of this lane (as MFMA column r16 of the wave's row tiles)
+  int lo_r[RT], hi_r[RT];
+  bool row_ok[RT];
+  int64_t orow[RT];
+  bf16x8 qb[RT][QS];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int row = wave * kPfRowsPerWave + rt * 16 + r16;
-    const int tl = row / G, g = row - (row / G) * G;
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = wave * RPW + rt * 16 + r16;
+    const int tl = row / nh, g = it.head0 + row - (row / nh) * nh;
     row_ok[rt] = tl < ntok;
     const int t = it.q_lo + (row_ok[rt] ? tl : 0);
     const int p = it.L - it.ql + t;
@@ -104,9 +109,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
     }
   }
   // the wave's rows cover tokens [tw0, tw1]: keys in [vis_lo, vis_hi) are visible to all of them
-  const int tw0 = min(ntok - 1, (wave * kPfRowsPerWave) / G);
-  const int tw1 = min(ntok - 1, (wave * kPfRowsPerWave + kPfRowsPerWave - 1) / G);
-  const bool wave_rows_full = (wave * kPfRowsPerWave + kPfRowsPerWave - 1) / G < ntok;
+  const int tw0 = min(ntok - 1, (wave * RPW) / nh);
+  const int tw1 = min(ntok - 1, (wave * RPW + RPW - 1) / nh);
+  const bool wave_rows_full = (wave * RPW + RPW - 1) / nh < ntok;
   const int pw0 = it.L - it.ql + it.q_lo + tw0, pw1 = it.L - it.ql + it.q_lo + tw1;
   const int vis_hi = a.causal ? pw0 + 1 : it.L;
   const int vis_lo = (a.window > 0 && pw1 - a.window + 1 > 0) ? pw1 - a.window + 1 : 0;
@@ -116,13 +121,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
   const int k_begin = (k_first / kTileKeys) * kTileKeys;
   const int k_end = it.k_hi_max;
   const int n_steps = (k_end - k_begin + KT - 1) / KT;
-  const float xscale = a.softcap > 0.0f ? a.logit_scale : a.logit_scale * kLog2e;
+  const float xscale = CAP ? a.logit_scale : a.logit_scale * kLog2e;
   const int last_tile = ((it.L - 1) / kTileKeys) * kTileKeys;  // first key of the tile holding key L-1
 
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  f32x4 acc[2][NT];
+  float m[RT], l[RT];
+  f32x4 acc[RT][NT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = -INFINITY;
+    l[rt] = 0.0f;
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -136,7 +146,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
     const uint32_t sbase = lds0 + (uint32_t)((step % NS) * STAGE);
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-      const int ii = wave + 4 * j;
+      const int ii = wave + WAVES * j;
       const int kv = ii / KV_INSTR;
       const int q0 = 64 * (ii % KV_INSTR);
       const int q = q0 + lane;
@@ -154,7 +164,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
       dma16_to_lds(src, sbase + (uint32_t)(kv * KT * D + q0 * 16));
     }
     if constexpr (PTH) {
-      if (wave == 3) {
+      if (wave == WAVES - 1) {
         // 16 lanes x 16 bytes: [K scales of the 32 keys][V scales], 4 scales per lane
         const int tl = (lane >> 2) & 1, part = lane & 3, kv = lane >> 3;
         const int t0 = min(kb0, last_tile), t1 = min(kb0 + 16, last_tile);
@@ -206,16 +216,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
       }
     }
     // ---- S^T = K Q^T: [key tile kt][row tile rt]
-    f32x4 s[2][2];
+    f32x4 s[2][RT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) s[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < RT; ++rt) s[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < QS; ++st) {
         const bf16x8 ka = widen8<DT>(kw[kt][st].x, kw[kt][st].y);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) s[kt][rt] = mfma16x16x32(ka, qb[rt][st], s[kt][rt]);
+        for (int rt = 0; rt < RT; ++rt) s[kt][rt] = mfma16x16x32(ka, qb[rt][st], s[kt][rt]);
       }
     }
     // V^T operands: transposed reads issued now, used after the softmax
@@ -227,16 +237,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
     }
     // ---- online softmax per row tile (lazy rescaling as in decode)
     const bool full = wave_rows_full && kb0 >= vis_lo && kb0 + KT <= vis_hi && kb0 + KT <= it.L;
-    bf16x8 pb[2];
+    bf16x8 pb[RT];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kt = e >> 2, r = e & 3;
         float v = s[kt][rt][r] * xscale;
         if constexpr (PTH) v *= ksl[kt * 16 + 4 * kg + r];
-        if (a.softcap > 0.0f) v = a.softcap * kLog2e * tanh_via_exp2(v * a.inv_softcap);
+        if constexpr (CAP) v = a.softcap * kLog2e * tanh_via_exp2(v * a.inv_softcap);
         x[e] = v;
       }
       if (!full) {
@@ -274,14 +284,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const bf16x8 va = widen8<DT>((uint32_t)vw[t].x, (uint32_t)vw[t].y);
-      acc[0][t] = mfma16x16x32(va, pb[0], acc[0][t]);
-      acc[1][t] = mfma16x16x32(va, pb[1], acc[1][t]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt][t] = mfma16x16x32(va, pb[rt], acc[rt][t]);
     }
   }
 
   // ---- normalise and write the rows
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     const float lt = sum_over_rows(l[rt]);
     if (!row_ok[rt]) continue;
     const float norm = a.v_scale / lt;
@@ -319,7 +329,10 @@ static int launch_pf(const AttnArgs& a, hipStream_t st) {
   p.softcap = a.softcap;
   p.inv_softcap = a.softcap > 0.0f ? 1.0f / a.softcap : 0.0f;
   p.v_scale = MODE == AQP_SCALE_PER_TENSOR ? a.v_scale : 1.0f;
-  hipLaunchKernelGGL((prefill_kernel<D, DT, MODE>), dim3(h.num_pf_items), dim3(256), h.pf_lds_bytes, st, p);
+  if (a.softcap > 0.0f)
+    hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, true>), dim3(h.num_pf_items), dim3(pf_waves(D) * 64), h.pf_lds_bytes, st, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, false>), dim3(h.num_pf_items), dim3(pf_waves(D) * 64), h.pf_lds_bytes, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("aqp_paged_attention: prefill launch failed: %s", hipGetErrorString(e));

@@ -95,19 +95,24 @@ class Run:
         bad = np.nonzero(g != self.ocache)[0]
         assert bad.size == 0, f"{bad.size} cache bytes differ, first at {bad[:8]}"
 
-    def gpu_attention(self):
+    def gpu_attention(self, calls=1):
+        """Output of the last of `calls` attention calls that reuse one device copy of the schedule."""
         torch, aqp, b = self.torch, self.aqp, self.b
         sch = aqp.get_schedule(self.params, self.desc, b.seq_lens, b.query_start_loc)
         meta_dev = torch.from_numpy(sch.meta).cuda()
         scratch = torch.empty(max(sch.scratch_bytes, 4), dtype=torch.uint8, device="cuda")
         q = to_dev(b.q, torch)
-        out = torch.full(q.shape, -1, dtype=torch.int16, device="cuda")  # NaN pattern: every row must be written
         bt = to_dev(b.block_tables, torch)
-        aqp.paged_attention(self.params, self.desc, self.gcache, q, bt, sch.meta, meta_dev, b.k_scale, b.v_scale,
-                            scratch, sch.scratch_bytes, out)
+        self.outs = []
+        for _ in range(calls):
+            out = torch.full(q.shape, -1, dtype=torch.int16, device="cuda")  # NaN pattern: every row must be written
+            aqp.paged_attention(self.params, self.desc, self.gcache, q, bt, sch.meta, meta_dev, b.k_scale, b.v_scale,
+                                scratch, sch.scratch_bytes, out)
+            self.outs.append(out)
         torch.cuda.synchronize()
         self.sched = sch
-        return out.cpu().numpy().view(np.uint16)
+        self.meta_after = meta_dev.cpu().numpy()
+        return self.outs[-1].cpu().numpy().view(np.uint16)
 
     def oracle_attention(self, seqs=None):
         """Oracle output rows of the chosen sequences (default all), on the oracle's own cache."""

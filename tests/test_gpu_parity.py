@@ -41,6 +41,10 @@ SMALL = [
     W.Workload("d64_int8_mixed", "int8_per_token_head", ((1, 100), (12, 12), (1, 3)), 8, 4, 64, 16, 20, seed=79),
     W.Workload("d256_e5m2_decode", "fp8_e5m2", ((1, 333), (1, 1024)), 16, 2, 256, 64, 40, softcap=20.0, seed=80),
     W.Workload("noncausal_prefill", "fp8_e4m3", ((40, 40), (7, 7)), 8, 2, 128, 16, 10, causal=False, seed=81),
+    # G = 160: a prefill item holds one token and at most 128 of its q heads; D = 256 with softcap at prefill
+    W.Workload("g160_mixed_e5m2", "fp8_e5m2", ((3, 40), (1, 70), (20, 33)), 160, 1, 64, 16, 16, seed=82),
+    W.Workload("prefill_d256_cap_pth", "fp8_per_token_head", ((37, 37), (5, 80)), 16, 2, 256, 16, 12,
+               softcap=8.0, seed=83),
 ]
 
 
@@ -82,6 +86,20 @@ def test_decode_split_counts(aqp, par):
     out = r.gpu_attention()
     ref, rows = r.oracle_attention()
     compare(out[rows], ref, w.name)
+
+
+def test_reused_schedule_copy_gives_identical_results(aqp):
+    """Calls reusing one device copy of the schedule give bit-identical outputs and leave the copy
+    unchanged, at several work-group counts."""
+    w = W.scaled(W.CFG3, name="reuse_meta", seqs=((1, 3000), (1, 129), (1, 2047), (1, 700)) * 3, num_blocks=1200)
+    for par in (0, 3, 40):
+        r = Run(w, torch, aqp, par=par)
+        last = r.gpu_attention(calls=4)
+        first = r.outs[0].cpu().numpy().view(np.uint16)
+        assert np.array_equal(first, last), f"par={par}"
+        assert np.array_equal(r.meta_after, r.sched.meta), f"par={par}: schedule copy changed"
+    ref, rows = r.oracle_attention()
+    compare(last[rows], ref, w.name)
 
 
 def test_block_permutation_bit_identical(aqp):

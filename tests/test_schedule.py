@@ -13,7 +13,11 @@ import workloads
 
 SEG = np.dtype([(n, "<i4") for n in "seq kvh head0 nheads k_lo k_hi q_tok part".split()])
 COMB = np.dtype([(n, "<i4") for n in "kvh head0 nheads q_tok first_part num_parts pad0 pad1".split()])
-PF = np.dtype([(n, "<i4") for n in "seq kvh q_lo q_hi L ql q_start k_hi_max".split()])
+PF = np.dtype([(n, "<i4") for n in "seq kvh q_lo q_hi L ql q_start k_hi_max head0 nheads pad0 pad1".split()])
+
+
+def h_rows(s):
+    return s.header["pf_rows"]
 
 
 def _arrays(s):
@@ -21,7 +25,7 @@ def _arrays(s):
     segs = m[h["off_dec_segs"]: h["off_dec_segs"] + 32 * h["num_dec_segs"]].view(SEG)
     wgs = m[h["off_dec_wg_start"]: h["off_dec_wg_start"] + 4 * (h["num_dec_wgs"] + 1)].view(np.int32)
     comb = m[h["off_comb"]: h["off_comb"] + 32 * h["num_comb"]].view(COMB)
-    pf = m[h["off_pf_items"]: h["off_pf_items"] + 32 * h["num_pf_items"]].view(PF)
+    pf = m[h["off_pf_items"]: h["off_pf_items"] + PF.itemsize * h["num_pf_items"]].view(PF)
     return segs, wgs, comb, pf
 
 
@@ -42,6 +46,7 @@ CASES = [
     (workloads.CFG4.seqs, 32, 8, 128, 16, 0, 0),
     (workloads.CFG5A.seqs, 64, 8, 128, 16, 4096, 0),
     (workloads.CFG2.seqs, 16, 2, 256, 2176, 0, 0),
+    (((3, 40), (70, 70), (1, 90)), 192, 1, 64, 16, 0, 0),  # G = 192 > 128: prefill items split the heads
 ]
 
 
@@ -89,8 +94,9 @@ def test_decode_coverage_exact(seqs, hq, hkv, d, bs, window, par):
             t = 0
             for sg in segs[wgs[w]: wgs[w + 1]]:
                 t += (sg["k_hi"] - 1) // 16 - sg["k_lo"] // 16 + 1
-            tiles.append(t // max(1, (G + 15) // 16 if False else 1))
+            tiles.append(t)
         assert len(tiles) == h["num_dec_wgs"] and min(tiles) > 0
+        assert len(set(tiles[:-1])) <= 1 and tiles[-1] <= tiles[0]
 
 
 @pytest.mark.parametrize("seqs,hq,hkv,d,bs,window,par", CASES)
@@ -101,13 +107,16 @@ def test_prefill_coverage_and_order(seqs, hq, hkv, d, bs, window, par):
     seen = {}
     for it in pf:
         assert 0 <= it["q_lo"] < it["q_hi"] <= it["ql"]
-        assert (it["q_hi"] - it["q_lo"]) * G <= 128
+        assert 0 <= it["head0"] < it["head0"] + it["nheads"] <= G
+        assert (it["q_hi"] - it["q_lo"]) * it["nheads"] <= h_rows(s)
         for t in range(it["q_lo"], it["q_hi"]):
-            key = (it["seq"], it["kvh"], t)
-            assert key not in seen
-            seen[key] = 1
+            for hh in range(it["head0"], it["head0"] + it["nheads"]):
+                key = (it["seq"], it["kvh"], t, hh)
+                assert key not in seen
+                seen[key] = 1
         assert it["k_hi_max"] == it["L"] - it["ql"] + it["q_hi"]
-    expect = {(b, k, t) for b, (ql, L) in enumerate(seqs) if ql > 1 for k in range(hkv) for t in range(ql)}
+    expect = {(b, k, t, hh) for b, (ql, L) in enumerate(seqs) if ql > 1 for k in range(hkv) for t in range(ql)
+              for hh in range(G)}
     assert set(seen) == expect
     work = [it["k_hi_max"] - (max(0, it["L"] - it["ql"] + it["q_lo"] - window + 1) if window else 0) for it in pf]
     assert work == sorted(work, reverse=True)
@@ -185,4 +194,5 @@ def test_large_block_size_geometry_is_consistent():
     h = s.header
     assert h["pf_kv_tile"] == 32 and h["staged_elem_bytes"] == 1
     assert h["pf_lds_bytes"] == 4 * (2 * 32 * 256 * 1 + 2 * 32 * 4)
-    assert h["dec_lds_bytes"] == max(4 * 16 * (256 + 32), 3 * 16 * (256 + 2) * 4)
+    # decode: per wave 2 ring slots of 16 keys of K and V, one Q slot of 8 heads; merge area of 4 waves
+    assert h["dec_lds_bytes"] == 4 * (2 * (2 * 16 * 256) + 8 * 256 * 2) + 4 * 8 * (256 + 2) * 4
