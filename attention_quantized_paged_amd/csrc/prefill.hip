@@ -187,22 +187,10 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   const int tr_row = (tr_i < 4) ? (4 * kg + tr_i) : (16 + 4 * kg + tr_i - 4);
   const int tr_swz = swz<D>(tr_row);
 
-#pragma unroll
-  for (int s0 = 0; s0 < NS - 1; ++s0)
-    if (s0 < n_steps) issue(s0);
-
-  for (int step = 0; step < n_steps; ++step) {
-    // this step's copies are done once only the later stages' copies are outstanding
-    wait_vmcnt(min(NS - 2, n_steps - 1 - step) * ipw_me);
-    __syncthreads();  // every wave's copies of this step landed; every wave left the previous step
-    if (step + NS - 1 < n_steps) issue(step + NS - 1);  // into the stage the previous step used
+  // ---- S^T = K Q^T of one step: [key tile kt][row tile rt]. The operand reads of the whole step
+  // are issued before any use, so the LDS latency of one overlaps the work on the others.
+  auto qk = [&](int step, f32x4 (&s)[2][RT]) {
     const uint8_t* kl = smem + (step % NS) * STAGE;
-    const uint8_t* vl = kl + KT * D;
-    const float* ksl = (const float*)(kl + 2 * KT * D);
-    const float* vsl = ksl + KT;
-    const int kb0 = k_begin + step * KT;
-    // ---- operand reads of the whole step are issued before any use, so the LDS latency of
-    // one overlaps the conversion and MFMAs of the others
     uint2 kw[2][QS];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -215,8 +203,6 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
         kw[kt][st] = *(const uint2*)(kp + ((((dbyte >> 4) ^ ksw) << 4) | (dbyte & 8)));
       }
     }
-    // ---- S^T = K Q^T: [key tile kt][row tile rt]
-    f32x4 s[2][RT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -228,14 +214,33 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
         for (int rt = 0; rt < RT; ++rt) s[kt][rt] = mfma16x16x32(ka, qb[rt][st], s[kt][rt]);
       }
     }
-    // V^T operands: transposed reads issued now, used after the softmax
+  };
+
+  // ---- online softmax of one step's S (lazy rescaling as in decode), then O^T += V^T P^T
+  auto softmax_pv = [&](int step, const f32x4 (&s)[2][RT]) {
+    const uint8_t* kl = smem + (step % NS) * STAGE;
+    const uint8_t* vl = kl + KT * D;
+    const float* ksl = (const float*)(kl + 2 * KT * D);
+    const float* vsl = ksl + KT;
+    const int kb0 = k_begin + step * KT;
+    // V^T operands: transposed reads issued first, used after the softmax
     i32x2 vw[NT];
     {
       const uint8_t* rp = vl + tr_row * D + (r16 & 1) * 8;
 #pragma unroll
       for (int t = 0; t < NT; ++t) vw[t] = lds_read_tr8(rp + ((t ^ tr_swz) << 4));
     }
-    // ---- online softmax per row tile (lazy rescaling as in decode)
+    // per-token-head scales of the lane's 8 keys (4kg + r of each 16-key tile), one vector read each
+    float ks[8], vs[8];
+    if constexpr (PTH) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const float4 k4 = *(const float4*)(ksl + kt * 16 + 4 * kg);
+        const float4 v4 = *(const float4*)(vsl + kt * 16 + 4 * kg);
+        ks[4 * kt] = k4.x; ks[4 * kt + 1] = k4.y; ks[4 * kt + 2] = k4.z; ks[4 * kt + 3] = k4.w;
+        vs[4 * kt] = v4.x; vs[4 * kt + 1] = v4.y; vs[4 * kt + 2] = v4.z; vs[4 * kt + 3] = v4.w;
+      }
+    }
     const bool full = wave_rows_full && kb0 >= vis_lo && kb0 + KT <= vis_hi && kb0 + KT <= it.L;
     bf16x8 pb[RT];
 #pragma unroll
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       for (int e = 0; e < 8; ++e) {
         const int kt = e >> 2, r = e & 3;
         float v = s[kt][rt][r] * xscale;
-        if constexpr (PTH) v *= ksl[kt * 16 + 4 * kg + r];
+        if constexpr (PTH) v *= ks[e];
         if constexpr (CAP) v = a.softcap * kLog2e * tanh_via_exp2(v * a.inv_softcap);
         x[e] = v;
       }
@@ -275,18 +280,46 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
         float pe = fast_exp2(x[e] - m_use);
         psum += pe;
         // a masked key may have an unwritten scale slot: select, do not multiply, its zero
-        if constexpr (PTH) pe = x[e] == -INFINITY ? 0.0f : pe * vsl[(e >> 2) * 16 + 4 * kg + (e & 3)];
+        if constexpr (PTH) pe = x[e] == -INFINITY ? 0.0f : pe * vs[e];
         pb[rt][e] = (__bf16)pe;
       }
       l[rt] += psum;
     }
-    // ---- O^T += V^T P^T
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const bf16x8 va = widen8<DT>((uint32_t)vw[t].x, (uint32_t)vw[t].y);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) acc[rt][t] = mfma16x16x32(va, pb[rt], acc[rt][t]);
     }
+  };
+
+  // ---- software pipeline: step t's softmax and PV product run while the QK^T product of step
+  // t + 1 is in the matrix cores. Stages t and t + 1 are read during iteration t; the copies of
+  // stages t + 2 .. t + NS - 1 are in flight.
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0)
+    if (s0 < n_steps) issue(s0);
+  f32x4 s_cur[2][RT];
+  if (n_steps > 0) {
+    wait_vmcnt(min(NS - 2, n_steps - 1) * ipw_me);
+    __syncthreads();  // stage 0 landed for every wave
+    qk(0, s_cur);
+  }
+  for (int step = 0; step < n_steps; ++step) {
+    f32x4 s_next[2][RT];
+    if (step + 1 < n_steps) {
+      // stage step + 1 is done once only the copies of later stages are outstanding
+      const int issued = min(n_steps, step + NS - 1);
+      wait_vmcnt((issued - step - 2) * ipw_me);
+      __syncthreads();  // every wave's copies of stage step + 1 landed; every wave left step - 1
+      if (step + NS - 1 < n_steps) issue(step + NS - 1);  // into the stage step - 1 used
+      qk(step + 1, s_next);
+    }
+    softmax_pv(step, s_cur);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) s_cur[kt][rt] = s_next[kt][rt];
   }
 
   // ---- normalise and write the rows
