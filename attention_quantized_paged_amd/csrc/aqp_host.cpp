@@ -217,8 +217,10 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   wg_start.clear();
   comb.clear();
   pf.clear();
-  const int32_t hpu = std::min<int32_t>(G, kMaxHeadsPerUnit);
+  const int32_t max_hpu = heads_per_unit(desc->head_dim);
+  const int32_t hpu = std::min<int32_t>(G, max_hpu);
   const int32_t dec_lds = dec_lds_bytes(desc->head_dim, desc->mode, hpu);
+  if (dec_lds > kLdsPerCu) return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: decode needs %d bytes of LDS", dec_lds);
   int64_t total_tiles = 0, dec_keys = 0;
   for (int32_t b = 0; b < num_seqs; ++b) {
     const int32_t L = seq_lens[b], ql = qsl[b + 1] - qsl[b];
@@ -229,8 +231,8 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
     const int64_t t0 = lo / kTileKeys, t1 = (hi + kTileKeys - 1) / kTileKeys;
     for (int32_t h = 0; h < p.num_kv_heads; ++h) {
       dec_keys += hi - lo;
-      for (int32_t h0 = 0; h0 < G; h0 += kMaxHeadsPerUnit) {
-        units.push_back({b, h, h0, std::min<int32_t>(kMaxHeadsPerUnit, G - h0), lo, hi, qsl[b], t0, t1 - t0});
+      for (int32_t h0 = 0; h0 < G; h0 += max_hpu) {
+        units.push_back({b, h, h0, std::min<int32_t>(max_hpu, G - h0), lo, hi, qsl[b], t0, t1 - t0});
         total_tiles += t1 - t0;
       }
     }
@@ -374,7 +376,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   h.dec_waves = kDecWaves;
   h.pf_rows = kPfRows;
   h.pf_kv_tile = kPfKvTile;
-  h.heads_per_unit = kMaxHeadsPerUnit;
+  h.heads_per_unit = max_hpu;
   h.dec_lds_bytes = dec_lds;
   h.pf_lds_bytes = g.pf_lds_bytes;
   h.num_dec_wgs = num_wgs;
@@ -431,8 +433,8 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
   MISMATCH_IF(h.causal != params->causal || h.window != params->window || h.max_blocks_per_seq != params->max_blocks_per_seq, "mask / block-table shape");
   MISMATCH_IF(h.sm_scale != effective_sm_scale(*params) || h.softcap != params->softcap, "logit scale / soft-cap");
   MISMATCH_IF(h.tile_keys != kTileKeys || h.dec_iter_keys != kDecIterKeys || h.dec_waves != kDecWaves || h.pf_rows != kPfRows ||
-              h.pf_kv_tile != kPfKvTile || h.heads_per_unit != kMaxHeadsPerUnit ||
-              h.dec_lds_bytes != dec_lds_bytes(desc->head_dim, desc->mode, std::min<int32_t>(params->num_q_heads / params->num_kv_heads, kMaxHeadsPerUnit)) ||
+              h.pf_kv_tile != kPfKvTile || h.heads_per_unit != heads_per_unit(desc->head_dim) ||
+              h.dec_lds_bytes != dec_lds_bytes(desc->head_dim, desc->mode, std::min<int32_t>(params->num_q_heads / params->num_kv_heads, heads_per_unit(desc->head_dim))) ||
               h.pf_lds_bytes != g.pf_lds_bytes, "tile geometry");
   if ((int64_t)scratch_bytes < h.scratch_bytes)
     return fail(AQP_ERR_SCRATCH_TOO_SMALL, "aqp_paged_attention: scratch of %zu bytes, schedule needs %lld", scratch_bytes, (long long)h.scratch_bytes);

@@ -23,7 +23,9 @@ constexpr uint32_t kVersion = 2;
 constexpr int kTileKeys = 16;        // keys per KV tile: one 16-row MFMA operand; block_size % 16 == 0
 constexpr int kDecIterKeys = 16;     // keys per decode iteration (one tile; PV on 16x16x16 MFMA)
 constexpr int kDecWaves = 4;         // compute waves per decode work-group (they split a segment's iterations)
-constexpr int kMaxHeadsPerUnit = 16; // q heads per MFMA column block
+// q heads per decode unit (MFMA column block): 16, or 8 at head_dim 256 so the work-group's LDS
+// (Q rows and the merge area grow with the heads) stays within one CU's
+constexpr int heads_per_unit(int head_dim) { return head_dim >= 256 ? 8 : 16; }
 constexpr int kPfRows = 128;         // prefill: query rows (token, q head) per work item
 // Prefill waves per work-group: head_dim 256 gives each of 8 waves 16 rows (so a wave's
 // 16 x 256 fp32 output tile and its Q rows stay in ordinary registers at two waves per SIMD);

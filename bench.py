@@ -169,6 +169,32 @@ def run_prefill(torch, aqp, W, args):
             "ms_per_call": round(ms, 4), "flops": flops, "timing": "median of 20 HIP-event pairs, L2 warm"}
 
 
+def run_cache_write(torch, aqp, W, s):
+    """Quantise-and-scatter of the decode batch's whole history (every token of every sequence)
+    into its cache: algorithmic bytes = bf16 K and V read + one code byte each written + the slot
+    index, per (token, KV head)."""
+    w, b, desc = s["w"], s["b"], s["desc"]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
+    k, v, slots = dev(b.k_hist), dev(b.v_hist), dev(b.slots_hist)
+    call = lambda: aqp.cache_write(desc, s["cache"], k, v, slots, b.k_scale, b.v_scale)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+    n = int(slots.numel())
+    byts = n * w.num_kv_heads * w.head_dim * 2 * (2 + 1) + n * 8
+    del k, v, slots
+    return {"workload": f"history of {w.name}", "tokens": n, "gbs": round(byts / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "ms_per_call": round(ms, 4),
+            "bytes": byts, "timing": "median of 10 HIP-event pairs"}
+
+
 def cpu_baseline(W, s, target_seconds=10.0):
     """The oracle (plain C, OpenMP) running the same step on the host: quantised cache write of
     the step's new tokens into its own cache, then attention for every sequence of the batch.
@@ -279,6 +305,8 @@ def main():
     if not args.no_prefill:
         log(args, "[bench] prefill figure")
         result["prefill"] = run_prefill(torch, aqp, W, args)
+        log(args, "[bench] cache-write figure")
+        result["cache_write"] = run_cache_write(torch, aqp, W, s)
     if not args.no_cpu_baseline:
         log(args, "[bench] oracle CPU baseline")
         result["cpu_baseline"] = cpu_baseline(W, s)

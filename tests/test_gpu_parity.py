@@ -45,6 +45,9 @@ SMALL = [
     W.Workload("g160_mixed_e5m2", "fp8_e5m2", ((3, 40), (1, 70), (20, 33)), 160, 1, 64, 16, 16, seed=82),
     W.Workload("prefill_d256_cap_pth", "fp8_per_token_head", ((37, 37), (5, 80)), 16, 2, 256, 16, 12,
                softcap=8.0, seed=83),
+    # head_dim 256 with 16 q heads per KV head: decode units of 8 heads (two per KV head)
+    W.Workload("d256_g16_pth_mixed", "fp8_per_token_head", ((1, 300), (1, 77), (3, 40)), 32, 2, 256, 16, 40,
+               seed=84),
 ]
 
 

@@ -86,7 +86,7 @@ def test_decode_coverage_exact(seqs, hq, hkv, d, bs, window, par):
     assert parts == list(range(h["num_parts"]))
     from_comb = sorted(p for c in comb for p in range(c["first_part"], c["first_part"] + c["num_parts"]))
     assert from_comb == parts
-    assert h["scratch_bytes"] == h["num_parts"] * min(G, 16) * (d + 2) * 4 == s.scratch_bytes
+    assert h["scratch_bytes"] == h["num_parts"] * min(G, 16 if d <= 128 else 8) * (d + 2) * 4 == s.scratch_bytes
     # balance: work-groups get equal numbers of 16-key tiles (the last may get fewer)
     if len(segs):
         tiles = []
