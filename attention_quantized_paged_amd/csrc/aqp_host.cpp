@@ -65,8 +65,10 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
   g->block_bytes = 2 * (int64_t)d.num_kv_heads * g->page_bytes;
   g->total_bytes = (int64_t)d.num_blocks * g->block_bytes;
   // Prefill work-group: a ring of kPfStages steps, each the K and V codes of kPfKvTile keys
-  // plus their row scales.
-  g->pf_lds_bytes = kPfStages * (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes + 2 * kPfKvTile * 4);
+  // plus their row scales; then two K and two V operand images of a step in bf16 (the codes
+  // widened once per work-group), each V image followed by a copy of its step's scales.
+  g->pf_lds_bytes = kPfStages * (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes + 2 * kPfKvTile * 4) +
+                    4 * kPfKvTile * d.head_dim * kPfOperandBytes + 2 * (2 * kPfKvTile * 4);
   return AQP_OK;
 }
 

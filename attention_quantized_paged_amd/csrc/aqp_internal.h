@@ -29,10 +29,11 @@ constexpr int heads_per_unit(int head_dim) { return head_dim >= 256 ? 8 : 16; }
 constexpr int kPfRows = 128;         // prefill: query rows (token, q head) per work item
 // Prefill waves per work-group: head_dim 256 gives each of 8 waves 16 rows (so a wave's
 // 16 x 256 fp32 output tile and its Q rows stay in ordinary registers at two waves per SIMD);
-// smaller head dims give each of 4 waves 32 rows, which halves the code widening per MFMA.
+// smaller head dims give each of 4 waves 32 rows, which halves the LDS operand reads per MFMA.
 constexpr int pf_waves(int head_dim) { return head_dim >= 256 ? 8 : 4; }
 constexpr int kPfKvTile = 32;        // prefill: keys staged in LDS per step
-constexpr int kPfStages = 4;         // prefill: LDS ring stages (three steps of copies in flight)
+constexpr int kPfStages = 4;         // prefill: LDS ring stages of codes (two steps ahead of the widening)
+constexpr int kPfOperandBytes = 2;   // prefill: bf16 operand images in LDS
 constexpr int kMinRunTiles = 32;     // decode: fewest 16-key tiles a work-group is given
 constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per compute unit (gfx950)
 

@@ -66,6 +66,16 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   constexpr int KV_INSTR = KT * CPR / 64;         // 1 KB copies per K (or V) step
   constexpr int IPW = 2 * KV_INSTR / WAVES;       // K+V copies per wave per step
   static_assert(IPW >= 1 && (2 * KV_INSTR) % WAVES == 0, "copies must split evenly over the waves");
+  // bf16 operand images: the MFMA A operands of one step, 64 lanes x 16 bytes per 1 KB block,
+  // written once per work-group and read by every wave
+  constexpr int IMG = KT * D * 2;                 // one K (or V) image of a step
+  constexpr int KIMG = NS * STAGE;                // two K images after the ring
+  constexpr int VSLOT = IMG + 2 * KT * 4;         // V image + the step's K and V scales
+  constexpr int VIMG = KIMG + 2 * IMG;            // two V slots
+  constexpr int KBLK = 2 * QS;                    // K blocks per image: [key tile][depth slice]
+  constexpr int KB_PW = KBLK / WAVES;             // K blocks each wave converts
+  constexpr int VB_PW = NT / WAVES;               // V blocks each wave converts
+  static_assert(KB_PW >= 1 && KBLK % WAVES == 0 && VB_PW >= 1 && NT % WAVES == 0, "blocks must split evenly");
   constexpr int PTH = MODE == AQP_SCALE_PER_TOKEN_HEAD ? 1 : 0;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
@@ -187,52 +197,96 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   const int tr_row = (tr_i < 4) ? (4 * kg + tr_i) : (16 + 4 * kg + tr_i - 4);
   const int tr_swz = swz<D>(tr_row);
 
-  // ---- S^T = K Q^T of one step: [key tile kt][row tile rt]. The operand reads of the whole step
-  // are issued before any use, so the LDS latency of one overlaps the work on the others.
-  auto qk = [&](int step, f32x4 (&s)[2][RT]) {
+  // ---- widen the K codes of one step into its K image: block kt * QS + st holds, for lane l,
+  // the 8 depth values kg * D/4 + 8 st .. +7 of key kt * 16 + l % 16 (the A operand of S^T = K Q^T)
+  auto convert_k = [&](int step) {
     const uint8_t* kl = smem + (step % NS) * STAGE;
-    uint2 kw[2][QS];
+    uint8_t* img = smem + KIMG + (step & 1) * IMG + lane * 16;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int j = 0; j < KB_PW; ++j) {
+      const int blk = wave * KB_PW + j;
+      const int kt = blk / QS, st = blk - (blk / QS) * QS;
       const int krow = kt * 16 + r16;
-      const uint8_t* kp = kl + krow * D;
-      const int ksw = swz<D>(krow);
-#pragma unroll
-      for (int st = 0; st < QS; ++st) {
-        const int dbyte = kg * (D / 4) + st * 8;
-        kw[kt][st] = *(const uint2*)(kp + ((((dbyte >> 4) ^ ksw) << 4) | (dbyte & 8)));
-      }
+      const int dbyte = kg * (D / 4) + st * 8;
+      const uint2 c = *(const uint2*)(kl + krow * D + ((((dbyte >> 4) ^ swz<D>(krow)) << 4) | (dbyte & 8)));
+      *(bf16x8*)(img + blk * 1024) = widen8<DT>(c.x, c.y);
     }
+  };
+  // ---- widen the V codes of one step into its V image: block t holds, for lane l, dim
+  // t * 16 + l % 16 of the 8 keys of lane group kg (the A operand of O^T += V^T P^T); the step's
+  // K and V scales are copied next to it, so they outlive the ring stage
+  auto convert_v = [&](int step) {
+    const uint8_t* kl = smem + (step % NS) * STAGE;
+    uint8_t* slot = smem + VIMG + (step & 1) * VSLOT;
+    const uint8_t* rp = kl + KT * D + tr_row * D + (r16 & 1) * 8;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) s[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < QS; ++st) {
-        const bf16x8 ka = widen8<DT>(kw[kt][st].x, kw[kt][st].y);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) s[kt][rt] = mfma16x16x32(ka, qb[rt][st], s[kt][rt]);
-      }
+    for (int j = 0; j < VB_PW; ++j) {
+      const int t = wave * VB_PW + j;
+      const i32x2 c = lds_read_tr8(rp + ((t ^ tr_swz) << 4));
+      *(bf16x8*)(slot + t * 1024 + lane * 16) = widen8<DT>((uint32_t)c.x, (uint32_t)c.y);
+    }
+    if constexpr (PTH) {
+      if (wave == WAVES - 1 && lane < 16) *(uint4*)(slot + IMG + lane * 16) = *(const uint4*)(kl + 2 * KT * D + lane * 16);
     }
   };
 
-  // ---- online softmax of one step's S (lazy rescaling as in decode), then O^T += V^T P^T
-  auto softmax_pv = [&](int step, const f32x4 (&s)[2][RT]) {
-    const uint8_t* kl = smem + (step % NS) * STAGE;
-    const uint8_t* vl = kl + KT * D;
-    const float* ksl = (const float*)(kl + 2 * KT * D);
-    const float* vsl = ksl + KT;
-    const int kb0 = k_begin + step * KT;
-    // V^T operands: transposed reads issued first, used after the softmax
-    i32x2 vw[NT];
-    {
-      const uint8_t* rp = vl + tr_row * D + (r16 & 1) * 8;
+  // ---- K operands of one step from its K image: [key tile][depth slice]
+  auto read_k = [&](int step, bf16x8 (&kw)[2][QS]) {
+    const uint8_t* img = smem + KIMG + (step & 1) * IMG + lane * 16;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) vw[t] = lds_read_tr8(rp + ((t ^ tr_swz) << 4));
-    }
-    // per-token-head scales of the lane's 8 keys (4kg + r of each 16-key tile), one vector read each
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int st = 0; st < QS; ++st) kw[kt][st] = *(const bf16x8*)(img + (kt * QS + st) * 1024);
+  };
+  // ---- half h of the depth slices of S^T = K Q^T: [key tile kt][row tile rt]
+  auto qk_half = [&](int h, const bf16x8 (&kw)[2][QS], f32x4 (&s)[2][RT]) {
+#pragma unroll
+    for (int st = h * (QS / 2); st < (h + 1) * (QS / 2); ++st)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          s[kt][rt] = mfma16x16x32(kw[kt][st], qb[rt][st], st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kt][rt]);
+  };
+
+  // ---- prologue: stages 0 and 1 widened, S of step 0
+  // (the software pipeline below: iteration t, after one barrier, puts the copies of step t + NS
+  // into the ring stage step t left, computes S of step t + 1 in the matrix cores while the
+  // softmax of step t runs, then the PV product of step t while K of step t + 2 and V of step
+  // t + 1 are widened into their images. Each image is written one iteration before it is read,
+  // so one barrier per step orders both. The last iteration computes an S it does not use.)
+#pragma unroll
+  for (int s0 = 0; s0 < NS; ++s0)
+    if (s0 < n_steps) issue(s0);
+  f32x4 s_cur[2][RT];
+  if (n_steps > 0) {
+    wait_vmcnt(max(0, min(NS, n_steps) - 2) * ipw_me);
+    __syncthreads();  // stages 0 and 1 landed for every wave
+    convert_k(0);
+    convert_k(1);
+    convert_v(0);
+    __syncthreads();
+    bf16x8 kw[2][QS];
+    read_k(0, kw);
+    qk_half(0, kw, s_cur);
+    qk_half(1, kw, s_cur);
+  }
+  for (int step = 0; step < n_steps; ++step) {
+    // stage step + 2 landed once only the copies of later stages are outstanding
+    const int issued = min(n_steps, step + NS);
+    wait_vmcnt(max(0, issued - step - 3) * ipw_me);
+    __syncthreads();  // every wave's copies of stage step + 2 landed; every wave left iteration step - 1
+    if (step + NS < n_steps) issue(step + NS);  // into the stage of step, whose codes are widened
+    bf16x8 kw[2][QS];
+    read_k(step + 1, kw);
+
+    const uint8_t* slot = smem + VIMG + (step & 1) * VSLOT;
+    const int kb0 = k_begin + step * KT;
+    // logits of step (log2 domain), masked where a step is not visible to all of the wave's rows
     float ks[8], vs[8];
     if constexpr (PTH) {
+      const float* ksl = (const float*)(slot + IMG);
+      const float* vsl = ksl + KT;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const float4 k4 = *(const float4*)(ksl + kt * 16 + 4 * kg);
@@ -241,81 +295,103 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
         vs[4 * kt] = v4.x; vs[4 * kt + 1] = v4.y; vs[4 * kt + 2] = v4.z; vs[4 * kt + 3] = v4.w;
       }
     }
-    const bool full = wave_rows_full && kb0 >= vis_lo && kb0 + KT <= vis_hi && kb0 + KT <= it.L;
-    bf16x8 pb[RT];
+    float x[RT][8];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float x[8];
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int kt = e >> 2, r = e & 3;
-        float v = s[kt][rt][r] * xscale;
+        float v = s_cur[e >> 2][rt][e & 3] * xscale;
         if constexpr (PTH) v *= ks[e];
         if constexpr (CAP) v = a.softcap * kLog2e * tanh_via_exp2(v * a.inv_softcap);
-        x[e] = v;
+        x[rt][e] = v;
       }
-      if (!full) {
+    const bool full = wave_rows_full && kb0 >= vis_lo && kb0 + KT <= vis_hi && kb0 + KT <= it.L;
+    if (!full) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = kb0 + (e >> 2) * 16 + 4 * kg + (e & 3);
-          if (!(j >= lo_r[rt] && j < hi_r[rt])) x[e] = -INFINITY;
+          if (!(j >= lo_r[rt] && j < hi_r[rt])) x[rt][e] = -INFINITY;
         }
-      }
-      float mx = x[0];
+    }
+
+    // first half of S of step + 1 while the row maxima of step are taken
+    f32x4 s_next[2][RT];
+    qk_half(0, kw, s_next);
+    float mx[RT];
+    bool grow = false;
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-      mx = max_over_rows(mx);
-      if (__builtin_amdgcn_ballot_w64(mx > m[rt] + 8.0f) != 0) {
-        const float m_new = fmaxf(m[rt], mx);
+    for (int rt = 0; rt < RT; ++rt) {
+      float v = x[rt][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) v = fmaxf(v, x[rt][e]);
+      mx[rt] = max_over_rows(v);
+      grow = grow || (mx[rt] > m[rt] + 8.0f);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * RT * (QS / 2); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+    // lazy rescaling: the reference maximum moves only when a row's logits exceed it by 8
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float m_new = fmaxf(m[rt], mx[rt]);
         const float alpha = fast_exp2(m[rt] - (m_new == -INFINITY ? 0.0f : m_new));
         l[rt] *= alpha;
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[rt][t] *= alpha;
         m[rt] = m_new;
       }
+    }
+
+    // second half of S of step + 1 while the probabilities of step are formed; the V operands
+    // of step are read meanwhile
+    const uint8_t* vimg = slot + lane * 16;
+    bf16x8 vw[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) vw[t] = *(const bf16x8*)(vimg + t * 1024);
+    qk_half(1, kw, s_next);
+    bf16x8 pb[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
       const float m_use = m[rt] == -INFINITY ? 0.0f : m[rt];
       float psum = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float pe = fast_exp2(x[e] - m_use);
+        float pe = fast_exp2(x[rt][e] - m_use);
         psum += pe;
         // a masked key may have an unwritten scale slot: select, do not multiply, its zero
-        if constexpr (PTH) pe = x[e] == -INFINITY ? 0.0f : pe * vs[e];
+        if constexpr (PTH) pe = x[rt][e] == -INFINITY ? 0.0f : pe * vs[e];
         pb[rt][e] = (__bf16)pe;
       }
       l[rt] += psum;
     }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const bf16x8 va = widen8<DT>((uint32_t)vw[t].x, (uint32_t)vw[t].y);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[rt][t] = mfma16x16x32(va, pb[rt], acc[rt][t]);
-    }
-  };
 
-  // ---- software pipeline: step t's softmax and PV product run while the QK^T product of step
-  // t + 1 is in the matrix cores. Stages t and t + 1 are read during iteration t; the copies of
-  // stages t + 2 .. t + NS - 1 are in flight.
+    // O^T += V^T P^T of step while K of step + 2 and V of step + 1 are widened
 #pragma unroll
-  for (int s0 = 0; s0 < NS - 1; ++s0)
-    if (s0 < n_steps) issue(s0);
-  f32x4 s_cur[2][RT];
-  if (n_steps > 0) {
-    wait_vmcnt(min(NS - 2, n_steps - 1) * ipw_me);
-    __syncthreads();  // stage 0 landed for every wave
-    qk(0, s_cur);
-  }
-  for (int step = 0; step < n_steps; ++step) {
-    f32x4 s_next[2][RT];
-    if (step + 1 < n_steps) {
-      // stage step + 1 is done once only the copies of later stages are outstanding
-      const int issued = min(n_steps, step + NS - 1);
-      wait_vmcnt((issued - step - 2) * ipw_me);
-      __syncthreads();  // every wave's copies of stage step + 1 landed; every wave left step - 1
-      if (step + NS - 1 < n_steps) issue(step + NS - 1);  // into the stage step - 1 used
-      qk(step + 1, s_next);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt][t] = mfma16x16x32(vw[t], pb[rt], acc[rt][t]);
+    convert_k(step + 2);
+    convert_v(step + 1);
+    // issue order of this block: half the V reads, then each matrix op of S with four vector ops
+    // of the softmax, then each PV matrix op with one LDS read and one vector op
+    __builtin_amdgcn_sched_group_barrier(0x100, NT / 2, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * RT * (QS / 2); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
-    softmax_pv(step, s_cur);
+#pragma unroll
+    for (int i = 0; i < NT * RT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+    }
+
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll

@@ -193,6 +193,7 @@ def test_large_block_size_geometry_is_consistent():
     s, *_ = _sched(((1024, 1024),) * 4, 16, 2, 256, 2176)
     h = s.header
     assert h["pf_kv_tile"] == 32 and h["staged_elem_bytes"] == 1
-    assert h["pf_lds_bytes"] == 4 * (2 * 32 * 256 * 1 + 2 * 32 * 4)
+    # prefill: 4 ring stages of codes and scales, two K and two V bf16 images, two scale copies
+    assert h["pf_lds_bytes"] == 4 * (2 * 32 * 256 * 1 + 2 * 32 * 4) + 4 * 32 * 256 * 2 + 2 * 2 * 32 * 4
     # decode: per wave 2 ring slots of 16 keys of K and V, one Q slot of 8 heads; merge area of 4 waves
     assert h["dec_lds_bytes"] == 4 * (2 * (2 * 16 * 256) + 8 * 256 * 2) + 4 * 8 * (256 + 2) * 4
