@@ -35,6 +35,8 @@ constexpr int kPfKvTile = 32;        // prefill: keys staged in LDS per step
 constexpr int kPfStages = 4;         // prefill: LDS ring stages of codes (two steps ahead of the widening)
 constexpr int kPfOperandBytes = 2;   // prefill: bf16 operand images in LDS
 constexpr int kMinRunTiles = 32;     // decode: fewest 16-key tiles a work-group is given
+constexpr int kCwRowsPerLane = 4;    // cache write: rows each lane loads before converting
+constexpr int kCwWgsPerCu = 16;      // cache write: resident work-groups per CU (grid cap)
 constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per compute unit (gfx950)
 
 // Decode LDS: per compute wave, a ring of dec_stages tiles (each the K and V codes of 16 keys plus

@@ -10,8 +10,11 @@
 // Work split: a row is (K or V, token, KV head) of head_dim values; D/8
 // lanes take 8 values each (one 16-byte load, one 8-byte store), so one
 // wave covers 64*8/D rows of consecutive heads of one token range and both
-// the loads and the page stores are contiguous per row. The per-token-head
-// absmax is a butterfly over the row's lanes.
+// the loads and the page stores are contiguous per row. Each lane loads
+// several rows before it converts any, so enough bytes are in flight per CU
+// to cover HBM latency; the grid is one resident wave of work-groups that
+// strides over the rows. The per-token-head absmax is a butterfly over the
+// row's lanes.
 //
 // Rounding: the hardware fp32 -> fp8 conversions of gfx950 round to nearest
 // even; values are first clamped to the largest finite code (v_med3) so that
@@ -54,46 +57,57 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast
 template <int D, int DT, int MODE>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
   constexpr int TPR = D / 8;          // lanes per row
-  constexpr int RPB = 256 / TPR;      // rows per work-group pass
+  constexpr int RPB = 256 / TPR;      // rows per work-group and sub-pass
+  constexpr int U = kCwRowsPerLane;   // rows per lane per pass, loaded together
   constexpr float QMAX = DT == AQP_KV_INT8 ? 127.0f : (DT == AQP_KV_FP8_E4M3 ? 448.0f : 57344.0f);
   const int64_t per_kv = a.num_tokens * a.num_kv_heads;
   const int64_t rows = 2 * per_kv;
   const int sub = threadIdx.x % TPR;
-  for (int64_t r0 = (int64_t)blockIdx.x * RPB; r0 < rows; r0 += (int64_t)gridDim.x * RPB) {
-    const int64_t r = r0 + threadIdx.x / TPR;
-    const bool active = r < rows;
-    const int64_t rr = active ? r : rows - 1;  // keep every lane in the row's butterfly
-    const int kv = rr >= per_kv ? 1 : 0;
-    const int64_t rem = rr - kv * per_kv;
-    const int64_t t = rem / a.num_kv_heads;
-    const int h = (int)(rem - t * a.num_kv_heads);
-    const uint16_t* src = (kv ? a.v : a.k) + t * a.token_stride + (int64_t)h * D + sub * 8;
-    const uint4 in = *(const uint4*)src;
-    float x[8] = {bf16_lo(in.x), bf16_hi(in.x), bf16_lo(in.y), bf16_hi(in.y),
-                  bf16_lo(in.z), bf16_hi(in.z), bf16_lo(in.w), bf16_hi(in.w)};
-    float s;
-    if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
-      float amax = 0.0f;
+  for (int64_t r0 = (int64_t)blockIdx.x * RPB * U; r0 < rows; r0 += (int64_t)gridDim.x * RPB * U) {
+    // issue the U rows' loads (16 bytes of values, 8 bytes of slot each) before using any
+    uint4 in[U];
+    int64_t slot[U];
+    int kv[U], h[U];
+    bool active[U];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-#pragma unroll
-      for (int o = TPR / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-      s = amax / QMAX;  // correctly rounded fp32 division
-    } else {
-      s = kv ? a.v_scale : a.k_scale;
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = r0 + u * RPB + threadIdx.x / TPR;
+      active[u] = r < rows;
+      const int64_t rr = active[u] ? r : rows - 1;  // keep every lane in the row's butterfly
+      kv[u] = rr >= per_kv ? 1 : 0;
+      const int64_t rem = rr - kv[u] * per_kv;
+      const int64_t t = rem / a.num_kv_heads;
+      h[u] = (int)(rem - t * a.num_kv_heads);
+      in[u] = *(const uint4*)((kv[u] ? a.v : a.k) + t * a.token_stride + (int64_t)h[u] * D + sub * 8);
+      slot[u] = a.slots[t];
     }
-    const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
-    const int64_t slot = a.slots[t];
-    if (!active || slot < 0 || slot >= a.total_slots) continue;
-    const int64_t blk = slot / a.block_size;
-    const int off = (int)(slot - blk * a.block_size);
-    uint8_t* page = a.cache + blk * a.block_bytes + (int64_t)(kv * a.num_kv_heads + h) * a.page_bytes;
-    uint2 codes;
-    codes.x = encode4<DT>(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
-    codes.y = encode4<DT>(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
-    *(uint2*)(page + (int64_t)off * D + sub * 8) = codes;
-    if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
-      if (sub == 0) *(float*)(page + (int64_t)a.block_size * D + 4 * off) = s;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[8] = {bf16_lo(in[u].x), bf16_hi(in[u].x), bf16_lo(in[u].y), bf16_hi(in[u].y),
+                    bf16_lo(in[u].z), bf16_hi(in[u].z), bf16_lo(in[u].w), bf16_hi(in[u].w)};
+      float s;
+      if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+        for (int o = TPR / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        s = amax / QMAX;  // correctly rounded fp32 division
+      } else {
+        s = kv[u] ? a.v_scale : a.k_scale;
+      }
+      const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+      if (!active[u] || slot[u] < 0 || slot[u] >= a.total_slots) continue;
+      const int64_t blk = slot[u] / a.block_size;
+      const int off = (int)(slot[u] - blk * a.block_size);
+      uint8_t* page = a.cache + blk * a.block_bytes + (int64_t)(kv[u] * a.num_kv_heads + h[u]) * a.page_bytes;
+      uint2 codes;
+      codes.x = encode4<DT>(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+      codes.y = encode4<DT>(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
+      *(uint2*)(page + (int64_t)off * D + sub * 8) = codes;
+      if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
+        if (sub == 0) *(float*)(page + (int64_t)a.block_size * D + 4 * off) = s;
+      }
     }
   }
 }
@@ -102,8 +116,9 @@ template <int D, int DT, int MODE>
 static int launch_cw(const CacheWriteArgs& a, hipStream_t st) {
   constexpr int RPB = 256 / (D / 8);
   const int64_t rows = 2 * a.num_tokens * a.num_kv_heads;
-  int64_t grid = (rows + RPB - 1) / RPB;
-  if (grid > 256 * 16) grid = 256 * 16;
+  int64_t grid = (rows + RPB * kCwRowsPerLane - 1) / (RPB * kCwRowsPerLane);
+  const int64_t resident = (int64_t)device_cu_count() * kCwWgsPerCu;
+  if (grid > resident) grid = resident;
   hipLaunchKernelGGL((cache_write_kernel<D, DT, MODE>), dim3((unsigned)grid), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

@@ -251,10 +251,11 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
 
   // ---- prologue: stages 0 and 1 widened, S of step 0
   // (the software pipeline below: iteration t, after one barrier, puts the copies of step t + NS
-  // into the ring stage step t left, computes S of step t + 1 in the matrix cores while the
-  // softmax of step t runs, then the PV product of step t while K of step t + 2 and V of step
-  // t + 1 are widened into their images. Each image is written one iteration before it is read,
-  // so one barrier per step orders both. The last iteration computes an S it does not use.)
+  // into the ring stage step t left (half the waves at once, the other half mid-step), computes
+  // S of step t + 1 in the matrix cores while the softmax of step t runs, then the PV product of
+  // step t while K of step t + 2 and V of step t + 1 are widened into their images. Each image is
+  // written one iteration before it is read, so one barrier per step orders both. The last
+  // iteration computes an S it does not use.)
 #pragma unroll
   for (int s0 = 0; s0 < NS; ++s0)
     if (s0 < n_steps) issue(s0);
@@ -276,7 +277,10 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
     const int issued = min(n_steps, step + NS);
     wait_vmcnt(max(0, issued - step - 3) * ipw_me);
     __syncthreads();  // every wave's copies of stage step + 2 landed; every wave left iteration step - 1
-    if (step + NS < n_steps) issue(step + NS);  // into the stage of step, whose codes are widened
+    // the copies of step + NS go into the stage of step, whose codes are widened: even waves issue
+    // theirs here, odd waves before the PV product, so the memory pipeline takes them in two
+    // bursts and fewer waves stall on a full request queue at once
+    if ((wave & 1) == 0 && step + NS < n_steps) issue(step + NS);
     bf16x8 kw[2][QS];
     read_k(step + 1, kw);
 
@@ -370,6 +374,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       l[rt] += psum;
     }
 
+    if ((wave & 1) == 1 && step + NS < n_steps) issue(step + NS);
     // O^T += V^T P^T of step while K of step + 2 and V of step + 1 are widened
 #pragma unroll
     for (int t = 0; t < NT; ++t)
