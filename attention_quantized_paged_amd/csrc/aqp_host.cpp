@@ -43,8 +43,6 @@ static int check_dtype_mode(int32_t dtype, int32_t mode, const char** why) {
   if (mode != AQP_SCALE_PER_TENSOR && mode != AQP_SCALE_PER_TOKEN_HEAD) { *why = "unknown scale mode"; return AQP_ERR_INVALID; }
   if (dtype == AQP_KV_AUTO) { *why = "kv dtype 'auto' (unquantised cache) is not supported by this build"; return AQP_ERR_UNSUPPORTED; }
   if (dtype != AQP_KV_FP8_E4M3 && dtype != AQP_KV_FP8_E5M2 && dtype != AQP_KV_INT8) { *why = "unknown kv dtype"; return AQP_ERR_INVALID; }
-  if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_INT8) { *why = "int8 with per-tensor scales is not supported"; return AQP_ERR_UNSUPPORTED; }
-  if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_FP8_E5M2) { *why = "fp8_e5m2 with per-token-head scales is not supported"; return AQP_ERR_UNSUPPORTED; }
   return AQP_OK;
 }
 
@@ -99,6 +97,9 @@ extern "C" int aqp_parse_kv_dtype(const char* s, int32_t* dtype, int32_t* mode) 
       {"fp8_e5m2", AQP_KV_FP8_E5M2, AQP_SCALE_PER_TENSOR},
       {"int8_per_token_head", AQP_KV_INT8, AQP_SCALE_PER_TOKEN_HEAD},
       {"fp8_per_token_head", AQP_KV_FP8_E4M3, AQP_SCALE_PER_TOKEN_HEAD},
+      // the remaining codec x scale-mode pairs, named after the ones above
+      {"int8", AQP_KV_INT8, AQP_SCALE_PER_TENSOR},
+      {"fp8_e5m2_per_token_head", AQP_KV_FP8_E5M2, AQP_SCALE_PER_TOKEN_HEAD},
   };
   for (auto& e : table) {
     if (std::strcmp(s, e.name) == 0) { *dtype = e.dt; *mode = e.md; return AQP_OK; }

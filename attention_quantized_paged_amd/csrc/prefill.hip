@@ -472,6 +472,8 @@ int launch_prefill(int dtype, int mode, const AttnArgs& a, void* stream) {
   if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_FP8_E5M2) return pf_d<AQP_KV_FP8_E5M2, AQP_SCALE_PER_TENSOR>(a, st);
   if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_INT8) return pf_d<AQP_KV_INT8, AQP_SCALE_PER_TOKEN_HEAD>(a, st);
   if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_FP8_E4M3) return pf_d<AQP_KV_FP8_E4M3, AQP_SCALE_PER_TOKEN_HEAD>(a, st);
+  if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_INT8) return pf_d<AQP_KV_INT8, AQP_SCALE_PER_TENSOR>(a, st);
+  if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_FP8_E5M2) return pf_d<AQP_KV_FP8_E5M2, AQP_SCALE_PER_TOKEN_HEAD>(a, st);
   set_error("aqp_paged_attention: dtype %d with scale mode %d is not built", dtype, mode);
   return AQP_ERR_UNSUPPORTED;
 }

@@ -105,6 +105,11 @@ typedef struct {
  *   "fp8_e5m2"              -> FP8_E5M2, PER_TENSOR
  *   "int8_per_token_head"   -> INT8,     PER_TOKEN_HEAD
  *   "fp8_per_token_head"    -> FP8_E4M3, PER_TOKEN_HEAD
+ * The two remaining codec x scale-mode pairs ([P38378] Risk/Impact: other
+ * scale granularities are left as a later addition) have names of this
+ * library's own:
+ *   "int8"                  -> INT8,     PER_TENSOR
+ *   "fp8_e5m2_per_token_head" -> FP8_E5M2, PER_TOKEN_HEAD
  *   "auto"                  -> AUTO, PER_TENSOR, returns AQP_ERR_UNSUPPORTED
  * Anything else: AQP_ERR_INVALID. Outputs are written only on AQP_OK (and for
  * "auto"). */

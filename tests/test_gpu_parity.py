@@ -48,6 +48,13 @@ SMALL = [
     # head_dim 256 with 16 q heads per KV head: decode units of 8 heads (two per KV head)
     W.Workload("d256_g16_pth_mixed", "fp8_per_token_head", ((1, 300), (1, 77), (3, 40)), 32, 2, 256, 16, 40,
                seed=84),
+    # the codec x scale-mode pairs beyond the pages' four: int8 per tensor, e5m2 per token-head
+    W.Workload("int8_pt_mixed_d128", "int8", ((1, 900), (1, 31), (48, 200), (1, 257)), 32, 8, 128, 16, 120, seed=85),
+    W.Workload("e5m2_pth_mixed_w_cap", "fp8_e5m2_per_token_head", ((1, 1200), (17, 90), (1, 64)), 16, 2, 128, 16, 100,
+               window=300, softcap=30.0, seed=86),
+    W.Workload("int8_pt_prefill_d256", "int8", ((70, 70), (9, 130)), 16, 2, 256, 32, 12, seed=87),
+    W.Workload("e5m2_pth_prefill_d64", "fp8_e5m2_per_token_head", ((45, 45), (3, 99), (1, 20)), 8, 2, 64, 16, 16,
+               seed=88),
 ]
 
 
@@ -122,7 +129,8 @@ def test_block_permutation_bit_identical(aqp):
     assert np.array_equal(o1, o2)
 
 
-@pytest.mark.parametrize("dtype_str", ["fp8_e4m3", "fp8_e5m2", "int8_per_token_head", "fp8_per_token_head"])
+@pytest.mark.parametrize("dtype_str", ["fp8_e4m3", "fp8_e5m2", "int8_per_token_head", "fp8_per_token_head", "int8",
+                                       "fp8_e5m2_per_token_head"])
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_cache_write_bit_exact(aqp, dtype_str, D):
     """Random slots (some negative), a fused-QKV token stride, specials (zero rows, huge and tiny

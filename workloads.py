@@ -190,8 +190,8 @@ def make_batch(w: Workload, with_kv: bool = True) -> Batch:
         k = v = np.zeros((0, Hkv, D), dtype=np.uint16)
     k_scale = v_scale = 1.0
     fmt = w.kv_dtype
-    if fmt in ("fp8_e4m3", "fp8_e5m2", "fp8") and with_kv:
-        qm = np.float32(QMAX["fp8_e5m2" if fmt == "fp8_e5m2" else "fp8_e4m3"])
+    if fmt in ("fp8_e4m3", "fp8_e5m2", "fp8", "int8") and with_kv:
+        qm = np.float32(QMAX[{"fp8_e5m2": "fp8_e5m2", "int8": "int8"}.get(fmt, "fp8_e4m3")])
         k_scale = float(np.float32(np.abs(bf16_to_f32(k)).max()) / qm)
         v_scale = float(np.float32(np.abs(bf16_to_f32(v)).max()) / qm)
     return Batch(w, lens, qsl, bt, q, k, v, slots, new_mask, k_scale, v_scale)
