@@ -69,6 +69,12 @@ def _load():
         lib.orc_attention_weights.argtypes = [D, P, P, P, i32, P, P, i32, i32, i32, i32, f64, f64, f32, f32,
                                               i32, i32, i32, P]
         lib.orc_attention_weights.restype = ctypes.c_int
+        lib.orc_attention_ext.argtypes = [D, P, P, P, i32, P, P, i32, i32, i32, P, i32, f64, f64, P, P, f32, f32,
+                                          P, P]
+        lib.orc_attention_ext.restype = ctypes.c_int
+        lib.orc_attention_weights_ext.argtypes = [D, P, P, P, i32, P, P, i32, i32, i32, i32, f64, f64, f64, f64,
+                                                  f32, f32, i32, i32, i32, P]
+        lib.orc_attention_weights_ext.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -161,18 +167,24 @@ def read_row(desc: CacheDesc, cache: np.ndarray, kv: int, block: int, head: int,
 def attention(desc: CacheDesc, cache: np.ndarray, q: np.ndarray, block_tables: np.ndarray,
               seq_lens: np.ndarray, query_start_loc: np.ndarray, num_q_heads: int, causal: bool = True,
               window: int = 0, sm_scale: float = 0.0, softcap: float = 0.0, k_scale: float = 1.0,
-              v_scale: float = 1.0, want_f64: bool = False):
+              v_scale: float = 1.0, want_f64: bool = False, causal_per_seq=None, alibi_slopes=None,
+              sinks=None):
     """Plain fp64 attention over the dequantised cache. Returns bf16 bits ``[T_q, Hq, D]`` (uint16)
-    and, if ``want_f64``, the fp64 values before rounding."""
+    and, if ``want_f64``, the fp64 values before rounding. ``causal_per_seq`` (int per sequence),
+    ``alibi_slopes`` and ``sinks`` (one float per q head) follow ``orc_attention_ext``."""
     q = np.ascontiguousarray(q, dtype=np.uint16)
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
     sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
     qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
     out = np.zeros(q.shape, dtype=np.uint16)
     o64 = np.zeros(q.shape, dtype=np.float64) if want_f64 else None
-    rc = _load().orc_attention(ctypes.byref(desc.c), _ptr(cache), _ptr(q), _ptr(bt), bt.shape[1], _ptr(sl),
-                               _ptr(qsl), sl.shape[0], num_q_heads, int(causal), int(window), float(sm_scale),
-                               float(softcap), float(k_scale), float(v_scale), _ptr(out), _ptr(o64))
+    cps = None if causal_per_seq is None else np.ascontiguousarray(causal_per_seq, dtype=np.int32)
+    al = None if alibi_slopes is None else np.ascontiguousarray(alibi_slopes, dtype=np.float64)
+    sk = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.float64)
+    rc = _load().orc_attention_ext(ctypes.byref(desc.c), _ptr(cache), _ptr(q), _ptr(bt), bt.shape[1], _ptr(sl),
+                                   _ptr(qsl), sl.shape[0], num_q_heads, int(causal), _ptr(cps), int(window),
+                                   float(sm_scale), float(softcap), _ptr(al), _ptr(sk), float(k_scale),
+                                   float(v_scale), _ptr(out), _ptr(o64))
     if rc != 0:
         raise ValueError("oracle attention: invalid arguments")
     return (out, o64) if want_f64 else out
@@ -181,16 +193,17 @@ def attention(desc: CacheDesc, cache: np.ndarray, q: np.ndarray, block_tables: n
 def attention_weights(desc: CacheDesc, cache: np.ndarray, q: np.ndarray, block_tables: np.ndarray,
                       seq_lens: np.ndarray, query_start_loc: np.ndarray, num_q_heads: int, b: int, i: int,
                       hq: int, causal: bool = True, window: int = 0, sm_scale: float = 0.0,
-                      softcap: float = 0.0, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+                      softcap: float = 0.0, k_scale: float = 1.0, v_scale: float = 1.0, alibi_slope: float = 0.0,
+                      sink: float = float("-inf")) -> np.ndarray:
     q = np.ascontiguousarray(q, dtype=np.uint16)
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
     sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
     qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
     w = np.zeros(max(int(sl[b]), 1), dtype=np.float64)
-    rc = _load().orc_attention_weights(ctypes.byref(desc.c), _ptr(cache), _ptr(q), _ptr(bt), bt.shape[1], _ptr(sl),
-                                       _ptr(qsl), sl.shape[0], num_q_heads, int(causal), int(window),
-                                       float(sm_scale), float(softcap), float(k_scale), float(v_scale), b, i, hq,
-                                       _ptr(w))
+    rc = _load().orc_attention_weights_ext(ctypes.byref(desc.c), _ptr(cache), _ptr(q), _ptr(bt), bt.shape[1],
+                                           _ptr(sl), _ptr(qsl), sl.shape[0], num_q_heads, int(causal), int(window),
+                                           float(sm_scale), float(softcap), float(alibi_slope), float(sink),
+                                           float(k_scale), float(v_scale), b, i, hq, _ptr(w))
     if rc != 0:
         raise ValueError("oracle attention_weights: invalid arguments")
     return w[: int(sl[b])]

@@ -265,10 +265,11 @@ typedef struct {
 } orc_ctx;
 
 static int check_args(const orc_cache_desc* d, const int32_t* seq_lens, const int32_t* qsl, int32_t num_seqs,
-                      int32_t Hq, int32_t causal, int32_t window, int32_t max_blocks) {
+                      int32_t Hq, int32_t causal, const int32_t* causal_per_seq, int32_t window, int32_t max_blocks) {
   if (d->num_kv_heads <= 0 || Hq <= 0 || Hq % d->num_kv_heads != 0) return -1;
   if (window < 0 || (window > 0 && !causal)) return -1;
   for (int b = 0; b < num_seqs; ++b) {
+    if (causal_per_seq && window > 0 && !causal_per_seq[b]) return -1;
     int32_t L = seq_lens[b], ql = qsl[b + 1] - qsl[b];
     if (ql < 0 || L < ql || (ql > 0 && L == 0)) return -1;
     if (((int64_t)L + d->block_size - 1) / d->block_size > max_blocks) return -1;
@@ -295,10 +296,15 @@ static void key_range(int32_t L, int32_t ql, int32_t i, int32_t causal, int32_t 
   *lo = (window > 0 && p - window + 1 > 0) ? p - window + 1 : 0;
 }
 
-/* Weights of one row over the gathered keys [lo0, ...): w has (L - lo0) entries. */
+/* Weights of one row (query at position p) over the gathered keys [lo0, ...): w has (L - lo0)
+ * entries. Logit of key j: z = sm_scale * q.k_j, soft-capped (cap * tanh(z / cap)) if cap > 0,
+ * plus the linear position bias slope * (j - p) (ALiBi; slope 0 = none). The softmax runs over
+ * the visible keys and, if sink is finite, one more logit `sink` that has no value row: it only
+ * adds exp(sink - m) to the normaliser, so the key weights sum to less than one. */
 static void row_weights(const double* qrow, const double* kk, int32_t lo0, int32_t lo, int32_t hi, int D,
-                        double sm_scale, double softcap, double* w, int32_t n) {
-  double m = -INFINITY;
+                        double sm_scale, double softcap, double slope, int32_t p, double sink, double* w,
+                        int32_t n) {
+  double m = sink;  /* -inf when there is no sink */
   for (int32_t j = 0; j < n; ++j) w[j] = 0.0;
   for (int32_t j = lo; j <= hi; ++j) {
     const double* kr = kk + (int64_t)(j - lo0) * D;
@@ -306,10 +312,11 @@ static void row_weights(const double* qrow, const double* kk, int32_t lo0, int32
     for (int dd = 0; dd < D; ++dd) dot += qrow[dd] * kr[dd];
     double z = sm_scale * dot;
     if (softcap > 0.0) z = softcap * tanh(z / softcap);
+    z += slope * (double)(j - p);
     w[j - lo0] = z;
     if (z > m) m = z;
   }
-  double l = 0.0;
+  double l = isinf(sink) ? 0.0 : exp(sink - m);
   for (int32_t j = lo; j <= hi; ++j) { w[j - lo0] = exp(w[j - lo0] - m); l += w[j - lo0]; }
   for (int32_t j = lo; j <= hi; ++j) w[j - lo0] /= l;
 }
@@ -319,7 +326,19 @@ int orc_attention(const orc_cache_desc* d, const uint8_t* cache, const uint16_t*
                   const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
                   int32_t num_q_heads, int32_t causal, int32_t window, double sm_scale, double softcap,
                   float k_scale, float v_scale, uint16_t* out, double* out_f64) {
-  if (check_args(d, seq_lens, query_start_loc, num_seqs, num_q_heads, causal, window, max_blocks_per_seq)) return -1;
+  return orc_attention_ext(d, cache, q, block_tables, max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+                           num_q_heads, causal, NULL, window, sm_scale, softcap, NULL, NULL, k_scale, v_scale, out,
+                           out_f64);
+}
+
+int orc_attention_ext(const orc_cache_desc* d, const uint8_t* cache, const uint16_t* q,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t causal, const int32_t* causal_per_seq, int32_t window,
+                      double sm_scale, double softcap, const double* alibi_slopes, const double* sinks,
+                      float k_scale, float v_scale, uint16_t* out, double* out_f64) {
+  if (check_args(d, seq_lens, query_start_loc, num_seqs, num_q_heads, causal, causal_per_seq, window,
+                 max_blocks_per_seq)) return -1;
   const int D = d->head_dim, Hkv = d->num_kv_heads, Hq = num_q_heads, G = Hq / Hkv;
   if (sm_scale <= 0.0) sm_scale = 1.0 / sqrt((double)D);
   orc_ctx c = {d, cache, block_tables, max_blocks_per_seq, k_scale, v_scale};
@@ -331,8 +350,9 @@ int orc_attention(const orc_cache_desc* d, const uint8_t* cache, const uint16_t*
     const int b = (int)(task / Hkv), kvh = (int)(task % Hkv);
     const int32_t L = seq_lens[b], ql = query_start_loc[b + 1] - query_start_loc[b];
     if (ql == 0) continue;
+    const int32_t cz = causal_per_seq ? causal_per_seq[b] : causal;
     int32_t lo0, hi0;
-    key_range(L, ql, 0, causal, window, &lo0, &hi0);
+    key_range(L, ql, 0, cz, window, &lo0, &hi0);
     const int32_t n = L - lo0;
     double* kk = (double*)malloc(sizeof(double) * (size_t)n * D);
     double* vv = (double*)malloc(sizeof(double) * (size_t)n * D);
@@ -345,13 +365,14 @@ int orc_attention(const orc_cache_desc* d, const uint8_t* cache, const uint16_t*
     } else {
       for (int32_t i = 0; i < ql; ++i) {
         int32_t lo, hi;
-        key_range(L, ql, i, causal, window, &lo, &hi);
+        key_range(L, ql, i, cz, window, &lo, &hi);
         const int64_t tok = (int64_t)query_start_loc[b] + i;
         for (int g = 0; g < G; ++g) {
           const int hq = kvh * G + g;
           const uint16_t* qsrc = q + (tok * Hq + hq) * D;
           for (int dd = 0; dd < D; ++dd) qrow[dd] = (double)orc_bf16_to_f32(qsrc[dd]);
-          row_weights(qrow, kk, lo0, lo, hi, D, sm_scale, softcap, w, n);
+          row_weights(qrow, kk, lo0, lo, hi, D, sm_scale, softcap, alibi_slopes ? alibi_slopes[hq] : 0.0,
+                      L - ql + i, sinks ? sinks[hq] : -INFINITY, w, n);
           for (int dd = 0; dd < D; ++dd) o[dd] = 0.0;
           for (int32_t j = lo; j <= hi; ++j) {
             const double wj = w[j - lo0];
@@ -376,7 +397,19 @@ int orc_attention_weights(const orc_cache_desc* d, const uint8_t* cache, const u
                           int32_t num_q_heads, int32_t causal, int32_t window, double sm_scale,
                           double softcap, float k_scale, float v_scale, int32_t b, int32_t i,
                           int32_t hq, double* w) {
-  if (check_args(d, seq_lens, query_start_loc, num_seqs, num_q_heads, causal, window, max_blocks_per_seq)) return -1;
+  return orc_attention_weights_ext(d, cache, q, block_tables, max_blocks_per_seq, seq_lens, query_start_loc,
+                                   num_seqs, num_q_heads, causal, window, sm_scale, softcap, 0.0, -INFINITY,
+                                   k_scale, v_scale, b, i, hq, w);
+}
+
+int orc_attention_weights_ext(const orc_cache_desc* d, const uint8_t* cache, const uint16_t* q,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t causal, int32_t window, double sm_scale,
+                              double softcap, double alibi_slope, double sink, float k_scale, float v_scale,
+                              int32_t b, int32_t i, int32_t hq, double* w) {
+  if (check_args(d, seq_lens, query_start_loc, num_seqs, num_q_heads, causal, NULL, window, max_blocks_per_seq))
+    return -1;
   if (b < 0 || b >= num_seqs || hq < 0 || hq >= num_q_heads) return -1;
   const int D = d->head_dim, Hkv = d->num_kv_heads, G = num_q_heads / Hkv;
   const int32_t L = seq_lens[b], ql = query_start_loc[b + 1] - query_start_loc[b];
@@ -392,7 +425,7 @@ int orc_attention_weights(const orc_cache_desc* d, const uint8_t* cache, const u
   if (kk && vv && qrow && gather(&c, b, hq / G, 0, L, kk, vv) == 0) {
     const int64_t tok = (int64_t)query_start_loc[b] + i;
     for (int dd = 0; dd < D; ++dd) qrow[dd] = (double)orc_bf16_to_f32(q[(tok * num_q_heads + hq) * D + dd]);
-    row_weights(qrow, kk, 0, lo, hi, D, sm_scale, softcap, w, L);
+    row_weights(qrow, kk, 0, lo, hi, D, sm_scale, softcap, alibi_slope, L - ql + i, sink, w, L);
     rc = 0;
   }
   free(kk); free(vv); free(qrow);

@@ -88,6 +88,28 @@ int orc_attention_weights(const orc_cache_desc* d, const uint8_t* cache, const u
                           double softcap, float k_scale, float v_scale, int32_t b, int32_t i,
                           int32_t hq, double* w);
 
+/* The same with the remaining parameters of the varlen harness of the "Fix CPU FP8 attention
+ * scheduler scratch sizing" page (Code excerpt: dynamic_causal, use_alibi, use_sink), which the
+ * page names without defining; the readings taken:
+ *   causal_per_seq: int32 [num_seqs] (NULL: `causal` for every sequence): causal flag of each
+ *                   sequence; a window needs causal sequences.
+ *   alibi_slopes:   fp64 [Hq] (NULL: none): logit of key j for a query at position p gains
+ *                   slope * (j - p), after the soft-cap.
+ *   sinks:          fp64 [Hq] (NULL: none): one more logit per q head in the softmax, with no
+ *                   value row (it only enlarges the normaliser). */
+int orc_attention_ext(const orc_cache_desc* d, const uint8_t* cache, const uint16_t* q,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t causal, const int32_t* causal_per_seq, int32_t window,
+                      double sm_scale, double softcap, const double* alibi_slopes, const double* sinks,
+                      float k_scale, float v_scale, uint16_t* out, double* out_f64);
+int orc_attention_weights_ext(const orc_cache_desc* d, const uint8_t* cache, const uint16_t* q,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t causal, int32_t window, double sm_scale,
+                              double softcap, double alibi_slope, double sink, float k_scale, float v_scale,
+                              int32_t b, int32_t i, int32_t hq, double* w);
+
 #ifdef __cplusplus
 }
 #endif
