@@ -40,7 +40,8 @@ class AttnParams(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("window", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("sm_scale", ctypes.c_float), ("softcap", ctypes.c_float), ("decode_parallelism", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("reserved", ctypes.c_int32), ("causal_per_seq", ctypes.c_void_p), ("alibi_slopes", ctypes.c_void_p),
+                ("sinks", ctypes.c_void_p)]
 
 
 def _load() -> ctypes.CDLL:
@@ -113,9 +114,27 @@ def cache_desc(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: in
 
 def attn_params(num_q_heads: int, num_kv_heads: int, head_dim: int, max_blocks_per_seq: int, causal: bool = True,
                 window: int = 0, sm_scale: float = 0.0, softcap: float = 0.0,
-                decode_parallelism: int = 0) -> AttnParams:
-    return AttnParams(num_q_heads, num_kv_heads, head_dim, int(causal), window, max_blocks_per_seq, sm_scale,
-                      softcap, decode_parallelism, 0)
+                decode_parallelism: int = 0, causal_per_seq=None, alibi_slopes=None, sinks=None) -> AttnParams:
+    """causal_per_seq: host int sequence (one flag per sequence) or None; alibi_slopes, sinks:
+    device float32 tensors of num_q_heads values (anything with ``data_ptr()``) or None. The
+    returned object keeps them alive."""
+    p = AttnParams(num_q_heads, num_kv_heads, head_dim, int(causal), window, max_blocks_per_seq, sm_scale,
+                   softcap, decode_parallelism, 0, None, None, None)
+    keep = []
+    if causal_per_seq is not None:
+        cps = np.ascontiguousarray(np.asarray(causal_per_seq), dtype=np.int32)
+        keep.append(cps)
+        p.causal_per_seq = cps.ctypes.data
+    for name, t in (("alibi_slopes", alibi_slopes), ("sinks", sinks)):
+        if t is not None:
+            if hasattr(t, "dtype") and str(t.dtype) != "torch.float32":
+                raise TypeError(f"{name} must be float32")
+            if hasattr(t, "numel") and t.numel() != num_q_heads:
+                raise ValueError(f"{name} needs num_q_heads values")
+            keep.append(t)
+            setattr(p, name, t.data_ptr())
+    p._keep = keep
+    return p
 
 
 def cache_bytes(desc: CacheDesc) -> Tuple[int, int, int]:
@@ -157,7 +176,7 @@ _HDR_FIELDS = ("magic version dtype mode kv_elem_bytes staged_elem_bytes scale_b
                "tile_keys dec_iter_keys dec_waves pf_rows pf_kv_tile heads_per_unit dec_lds_bytes pf_lds_bytes "
                "num_dec_wgs num_dec_segs num_parts num_comb num_pf_items group_heads").split()
 _HDR_FIELDS64 = ("off_dec_segs off_dec_wg_start off_comb off_pf_items meta_bytes scratch_bytes page_bytes block_bytes "
-                 "dec_kv_keys").split()
+                 "dec_kv_keys off_seq_lens").split()
 
 
 def parse_header(meta: np.ndarray) -> dict:

@@ -197,6 +197,11 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   if (num_seqs > 0 && qsl[0] != 0) return fail(AQP_ERR_INVALID, "aqp_get_schedule: query_start_loc[0] must be 0");
   for (int32_t b = 0; b < num_seqs; ++b) {
     const int64_t L = seq_lens[b], ql = (int64_t)qsl[b + 1] - qsl[b];
+    if (p.causal_per_seq) {
+      const int32_t c = p.causal_per_seq[b];
+      if (c != 0 && c != 1) return fail(AQP_ERR_INVALID, "aqp_get_schedule: causal_per_seq[%d] must be 0 or 1", b);
+      if (c == 0 && p.window > 0) return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: a sliding window needs every sequence causal");
+    }
     if (L < 0 || ql < 0 || ql > L)
       return fail(AQP_ERR_INVALID, "aqp_get_schedule: sequence %d has seq_len %lld and query_len %lld (need 0 <= query_len <= seq_len)", b, (long long)L, (long long)ql);
     if ((L + bs - 1) / bs > p.max_blocks_per_seq)
@@ -308,12 +313,13 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   for (int32_t b = 0; b < num_seqs; ++b) {
     const int32_t L = seq_lens[b], ql = qsl[b + 1] - qsl[b];
     if (ql <= 1) continue;
+    const int32_t causal = p.causal_per_seq ? p.causal_per_seq[b] : p.causal;
     for (int32_t q0 = 0; q0 < ql; q0 += tpi) {
       const int32_t q1 = std::min(ql, q0 + tpi);
-      const int32_t khi = p.causal ? (L - ql + q1) : L;  // exclusive end of the last row's keys
+      const int32_t khi = causal ? (L - ql + q1) : L;  // exclusive end of the last row's keys
       for (int32_t h = 0; h < p.num_kv_heads; ++h)
         for (int32_t h0 = 0; h0 < G; h0 += hpi)
-          pf.push_back({b, h, q0, q1, L, ql, qsl[b], khi, h0, std::min(hpi, G - h0), 0, 0});
+          pf.push_back({b, h, q0, q1, L, ql, qsl[b], khi, h0, std::min(hpi, G - h0), causal, 0});
     }
   }
   if (pf.size() > 1) std::stable_sort(pf.begin(), pf.end(), [&](const PfItem& x, const PfItem& y) {
@@ -335,6 +341,8 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   off = round_up(off + (int64_t)comb.size() * sizeof(CombItem), 256);
   const int64_t off_pf = off;
   off = round_up(off + (int64_t)pf.size() * sizeof(PfItem), 256);
+  const int64_t off_sl = off;
+  off = round_up(off + (int64_t)num_seqs * 4, 256);
   const int64_t need = off;
   const int64_t scratch = (int64_t)num_parts * part_floats(hpu, desc->head_dim) * 4;
   if (scratch_bytes) *scratch_bytes = (size_t)scratch;
@@ -352,7 +360,8 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   zero_gap(off_segs + (int64_t)segs.size() * (int64_t)sizeof(DecSeg), off_wgs);
   zero_gap(off_wgs + (int64_t)wg_start.size() * 4, off_comb);
   zero_gap(off_comb + (int64_t)comb.size() * (int64_t)sizeof(CombItem), off_pf);
-  zero_gap(off_pf + (int64_t)pf.size() * (int64_t)sizeof(PfItem), need);
+  zero_gap(off_pf + (int64_t)pf.size() * (int64_t)sizeof(PfItem), off_sl);
+  zero_gap(off_sl + (int64_t)num_seqs * 4, need);
   SchedHeader h;
   std::memset(&h, 0, sizeof h);
   h.magic = kMagic;
@@ -397,11 +406,13 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   h.page_bytes = g.page_bytes;
   h.block_bytes = g.block_bytes;
   h.dec_kv_keys = dec_keys;
+  h.off_seq_lens = off_sl;
   std::memcpy(m, &h, sizeof h);
   if (!segs.empty()) std::memcpy(m + off_segs, segs.data(), segs.size() * sizeof(DecSeg));
   if (!wg_start.empty()) std::memcpy(m + off_wgs, wg_start.data(), wg_start.size() * sizeof(int32_t));
   if (!comb.empty()) std::memcpy(m + off_comb, comb.data(), comb.size() * sizeof(CombItem));
   if (!pf.empty()) std::memcpy(m + off_pf, pf.data(), pf.size() * sizeof(PfItem));
+  if (num_seqs > 0) std::memcpy(m + off_sl, seq_lens, (size_t)num_seqs * 4);
   return AQP_OK;
 }
 
@@ -467,6 +478,8 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
   a.softcap = params->softcap;
   a.k_scale = desc->mode == AQP_SCALE_PER_TENSOR ? k_scale : 1.0f;
   a.v_scale = desc->mode == AQP_SCALE_PER_TENSOR ? v_scale : 1.0f;
+  a.alibi_slopes = params->alibi_slopes;
+  a.sinks = params->sinks;
   a.hdr = &h;
   if (h.num_pf_items > 0) {
     rc = launch_prefill(desc->dtype, desc->mode, a, stream);

@@ -17,7 +17,7 @@
 namespace aqp {
 
 constexpr uint32_t kMagic = 0x53505141u;  // "AQPS"
-constexpr uint32_t kVersion = 2;
+constexpr uint32_t kVersion = 3;
 
 // ---- compile-time tile geometry of the kernels ----------------------------
 constexpr int kTileKeys = 16;        // keys per KV tile: one 16-row MFMA operand; block_size % 16 == 0
@@ -83,7 +83,8 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why);
 
 // ---- schedule metadata -----------------------------------------------------
 // Layout: [SchedHeader][DecSeg x num_dec_segs][int32 dec_wg_start x (num_dec_wgs + 1)]
-//         [CombItem x num_comb][PfItem x num_pf_items], each array 256-byte aligned.
+//         [CombItem x num_comb][PfItem x num_pf_items][int32 seq_lens x num_seqs], each array
+//         256-byte aligned.
 struct SchedHeader {
   uint32_t magic, version;
   // what the schedule was built for
@@ -101,10 +102,11 @@ struct SchedHeader {
   int64_t meta_bytes, scratch_bytes;
   int64_t page_bytes, block_bytes;
   int64_t dec_kv_keys;  // total visible (key, KV head) pairs of the decode work (for reporting)
+  int64_t off_seq_lens;  // keys of each sequence (the decode query of sequence b sits at seq_lens[b] - 1)
 };
 
 static_assert(offsetof(SchedHeader, off_dec_segs) == 136, "SchedHeader layout is part of the metadata format");
-static_assert(sizeof(SchedHeader) == 208, "SchedHeader layout is part of the metadata format");
+static_assert(sizeof(SchedHeader) == 216, "SchedHeader layout is part of the metadata format");
 
 // Decode segment: keys [k_lo, k_hi) of (sequence, KV head, q heads
 // [head0, head0 + nheads) of that KV head's group), one query token.
@@ -126,7 +128,7 @@ struct CombItem {
 // Prefill item: query tokens [q_lo, q_hi) of sequence seq times q heads [head0, head0 + nheads)
 // of KV head kvh; row r is token q_lo + r / nheads, head head0 + r % nheads.
 struct PfItem {
-  int32_t seq, kvh, q_lo, q_hi, L, ql, q_start, k_hi_max, head0, nheads, pad0, pad1;
+  int32_t seq, kvh, q_lo, q_hi, L, ql, q_start, k_hi_max, head0, nheads, causal, pad1;
 };
 
 // Scratch of a partial slot: nh = min(G, 16) heads x (D floats of O, then m, l).
@@ -159,6 +161,8 @@ struct AttnArgs {
   int32_t head_dim, block_size, num_kv_heads, num_q_heads, group, max_blocks_per_seq;
   int32_t window, causal;
   float sm_scale, softcap, k_scale, v_scale;
+  const float* alibi_slopes;  // device [num_q_heads] or null
+  const float* sinks;         // device [num_q_heads] or null
   const SchedHeader* hdr;  // host copy
 };
 int launch_decode(int dtype, int mode, const AttnArgs& a, void* stream);

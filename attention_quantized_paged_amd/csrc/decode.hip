@@ -50,6 +50,9 @@ struct DecArgs {
   float logit_scale;  // sm_scale * k_scale (per tensor) or sm_scale (per token-head)
   float softcap, inv_softcap;
   float v_scale;      // per tensor; 1 per token-head
+  const int32_t* seq_lens;  // keys of each sequence (schedule copy): the query sits at L - 1
+  const float* alibi;       // [num_q_heads] slopes or null
+  const float* sinks;       // [num_q_heads] sink logits or null
 };
 
 // Stored 16-byte chunk of logical chunk c in staged row `row` (rows of D bytes): c ^ dec_swz(row).
@@ -103,7 +106,15 @@ __device__ __forceinline__ void merge_store(const DecArgs& a, const float* mg, i
   }
   const int hq = sg.kvh * a.group + sg.head0 + r16;
   if (sg.part < 0) {
-    const float norm = a.v_scale / L;
+    float fs = 1.0f;
+    if (a.sinks) {
+      // the sink logit joins the normaliser (log2 domain); M_use is the reference of o and L
+      const float s2 = a.sinks[hq] * kLog2e;
+      const float Mx = fmaxf(M_use, s2);
+      fs = fast_exp2(M_use - Mx);
+      L = L * fs + fast_exp2(s2 - Mx);
+    }
+    const float norm = a.v_scale * fs / L;
     uint16_t* op = a.out + ((int64_t)sg.q_tok * a.num_q_heads + hq) * D;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -282,6 +293,13 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
   for (int si = s_begin; si < s_end; ++si) {
     const DecSeg sg = load_const(as_const(a.segs) + si);
     const bool head_ok = r16 < sg.nheads;
+    // ALiBi: slope of this lane's head (log2 domain) and the query's position L - 1
+    float slope2 = 0.0f;
+    int qpos = 0;
+    if (a.alibi) {
+      qpos = as_const(a.seq_lens)[sg.seq] - 1;
+      slope2 = head_ok ? a.alibi[sg.kvh * a.group + sg.head0 + r16] * kLog2e : 0.0f;
+    }
     Pos pc;
     const int n_my = first_pos(sg, pc);
 
@@ -338,6 +356,12 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
       if constexpr (CAP) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] = a.softcap * kLog2e * tanh_via_exp2(x[r] * a.inv_softcap);
+      }
+      if (a.alibi) {
+        // + slope * (key - position), after the soft-cap
+        const int base = pc.k0 + 4 * kg - qpos;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] += slope2 * (float)(base + r);
       }
       // masking is needed only on the segment's edge tiles (and tiles of an invalid block); rows
       // outside the range may hold unwritten bytes: their logits are replaced, their V codes
@@ -415,11 +439,11 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
 }
 
 // Split-KV merge: one wave per (item, head). M = max_s m_s;
-// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// O = sum_s 2^(m_s - M) O_s / (sum_s 2^(m_s - M) l_s [+ 2^(sink - M)]).
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(const CombItem* items, const float* scratch, uint16_t* out,
                                                      int32_t num_q_heads, int32_t group, int32_t group_heads,
-                                                     int32_t num_parts) {
+                                                     int32_t num_parts, const float* sinks) {
   const CombItem it = load_const(as_const(items) + blockIdx.x);
   const int h = blockIdx.y;
   if (h >= it.nheads) return;
@@ -441,8 +465,17 @@ __global__ __launch_bounds__(64) void combine_kernel(const CombItem* items, cons
 #pragma unroll
     for (int j = 0; j < PER; ++j) o[j] += f * pp[lane + 64 * j];
   }
-  const float inv = 1.0f / L;
-  uint16_t* op = out + ((int64_t)it.q_tok * num_q_heads + it.kvh * group + it.head0 + h) * D;
+  const int hq = it.kvh * group + it.head0 + h;
+  float fs = 1.0f;
+  if (sinks) {
+    // the sink logit joins the normaliser (log2 domain), relative to the same reference as o and L
+    const float s2 = sinks[hq] * kLog2e;
+    const float Mx = fmaxf(M_use, s2);
+    fs = fast_exp2(M_use - Mx);
+    L = L * fs + fast_exp2(s2 - Mx);
+  }
+  const float inv = fs / L;
+  uint16_t* op = out + ((int64_t)it.q_tok * num_q_heads + hq) * D;
 #pragma unroll
   for (int j = 0; j < PER; ++j) op[lane + 64 * j] = f32_to_bf16_rne(o[j] * inv);
 }
@@ -472,6 +505,9 @@ static int launch_dec(const AttnArgs& a, hipStream_t st) {
   d.softcap = a.softcap;
   d.inv_softcap = a.softcap > 0.0f ? 1.0f / a.softcap : 0.0f;
   d.v_scale = MODE == AQP_SCALE_PER_TENSOR ? a.v_scale : 1.0f;
+  d.seq_lens = (const int32_t*)(a.meta_dev + h.off_seq_lens);
+  d.alibi = a.alibi_slopes;
+  d.sinks = a.sinks;
   if (a.softcap > 0.0f)
     hipLaunchKernelGGL((decode_kernel<D, DT, MODE, true>), dim3(h.num_dec_wgs), dim3((kDecWaves + 1) * 64), h.dec_lds_bytes, st, d);
   else
@@ -513,9 +549,9 @@ int launch_combine(const AttnArgs& a, void* stream) {
   const CombItem* items = (const CombItem*)(a.meta_dev + h.off_comb);
   dim3 grid(h.num_comb, h.group_heads);
   switch (a.head_dim) {
-    case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(64), 0, st, items, a.scratch, a.out, a.num_q_heads, a.group, h.group_heads, h.num_parts); break;
-    case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(64), 0, st, items, a.scratch, a.out, a.num_q_heads, a.group, h.group_heads, h.num_parts); break;
-    case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(64), 0, st, items, a.scratch, a.out, a.num_q_heads, a.group, h.group_heads, h.num_parts); break;
+    case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(64), 0, st, items, a.scratch, a.out, a.num_q_heads, a.group, h.group_heads, h.num_parts, a.sinks); break;
+    case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(64), 0, st, items, a.scratch, a.out, a.num_q_heads, a.group, h.group_heads, h.num_parts, a.sinks); break;
+    case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(64), 0, st, items, a.scratch, a.out, a.num_q_heads, a.group, h.group_heads, h.num_parts, a.sinks); break;
     default: set_error("aqp_paged_attention: unsupported head_dim"); return AQP_ERR_UNSUPPORTED;
   }
   hipError_t e = hipGetLastError();

@@ -34,10 +34,12 @@ struct PfArgs {
   uint16_t* out;
   int64_t page_bytes, block_bytes;
   int32_t block_size, num_kv_heads, num_q_heads, group, max_blocks, num_blocks;
-  int32_t causal, window;
+  int32_t window;
   float logit_scale;  // sm_scale * k_scale (per tensor) or sm_scale (per token-head)
   float softcap, inv_softcap;
   float v_scale;
+  const float* alibi;  // [num_q_heads] slopes or null
+  const float* sinks;  // [num_q_heads] sink logits or null
 };
 
 // 16-byte chunk swizzle of a staged row: chunk c of row `row` is stored at chunk
@@ -98,6 +100,9 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   int lo_r[RT], hi_r[RT];
   bool row_ok[RT];
   int64_t orow[RT];
+  int pos_r[RT];      // position of the row's query
+  float slope_r[RT];  // ALiBi slope of the row's head, in the log2 domain (0 without ALiBi)
+  float sink_r[RT];   // sink logit of the row's head, in the log2 domain (-inf without sinks)
   bf16x8 qb[RT][QS];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -106,7 +111,11 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
     row_ok[rt] = tl < ntok;
     const int t = it.q_lo + (row_ok[rt] ? tl : 0);
     const int p = it.L - it.ql + t;
-    hi_r[rt] = a.causal ? p + 1 : it.L;
+    hi_r[rt] = it.causal ? p + 1 : it.L;
+    pos_r[rt] = p;
+    const int hq = it.kvh * G + g;
+    slope_r[rt] = a.alibi ? a.alibi[hq] * kLog2e : 0.0f;
+    sink_r[rt] = a.sinks ? a.sinks[hq] * kLog2e : -INFINITY;
     lo_r[rt] = (a.window > 0 && p - a.window + 1 > 0) ? p - a.window + 1 : 0;
     if (!row_ok[rt]) { lo_r[rt] = 0; hi_r[rt] = 0; }
     orow[rt] = ((int64_t)(it.q_start + t) * a.num_q_heads + it.kvh * G + g) * D;
@@ -123,7 +132,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   const int tw1 = min(ntok - 1, (wave * RPW + RPW - 1) / nh);
   const bool wave_rows_full = (wave * RPW + RPW - 1) / nh < ntok;
   const int pw0 = it.L - it.ql + it.q_lo + tw0, pw1 = it.L - it.ql + it.q_lo + tw1;
-  const int vis_hi = a.causal ? pw0 + 1 : it.L;
+  const int vis_hi = it.causal ? pw0 + 1 : it.L;
   const int vis_lo = (a.window > 0 && pw1 - a.window + 1 > 0) ? pw1 - a.window + 1 : 0;
   // ---- key range of the whole item: first token's window start .. last token's end
   const int p_first = it.L - it.ql + it.q_lo;
@@ -309,6 +318,15 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
         if constexpr (CAP) v = a.softcap * kLog2e * tanh_via_exp2(v * a.inv_softcap);
         x[rt][e] = v;
       }
+    if (a.alibi) {
+      // + slope * (key - position), after the soft-cap
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int base = kb0 + 4 * kg - pos_r[rt];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[rt][e] += slope_r[rt] * (float)(base + (e >> 2) * 16 + (e & 3));
+      }
+    }
     const bool full = wave_rows_full && kb0 >= vis_lo && kb0 + KT <= vis_hi && kb0 + KT <= it.L;
     if (!full) {
 #pragma unroll
@@ -406,9 +424,16 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   // ---- normalise and write the rows
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const float lt = sum_over_rows(l[rt]);
+    float lt = sum_over_rows(l[rt]);
     if (!row_ok[rt]) continue;
-    const float norm = a.v_scale / lt;
+    float f = 1.0f;
+    if (a.sinks) {
+      // the sink logit joins the normaliser: rescale to the larger of it and the row's reference
+      const float M = fmaxf(m[rt], sink_r[rt]);
+      f = fast_exp2(m[rt] - M);
+      lt = lt * f + fast_exp2(sink_r[rt] - M);
+    }
+    const float norm = a.v_scale * f / lt;
     uint16_t* op = a.out + orow[rt];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -437,12 +462,13 @@ static int launch_pf(const AttnArgs& a, hipStream_t st) {
   p.group = a.group;
   p.max_blocks = a.max_blocks_per_seq;
   p.num_blocks = h.num_blocks;
-  p.causal = a.causal;
   p.window = a.window;
   p.logit_scale = MODE == AQP_SCALE_PER_TENSOR ? a.sm_scale * a.k_scale : a.sm_scale;
   p.softcap = a.softcap;
   p.inv_softcap = a.softcap > 0.0f ? 1.0f / a.softcap : 0.0f;
   p.v_scale = MODE == AQP_SCALE_PER_TENSOR ? a.v_scale : 1.0f;
+  p.alibi = a.alibi_slopes;
+  p.sinks = a.sinks;
   if (a.softcap > 0.0f)
     hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, true>), dim3(h.num_pf_items), dim3(pf_waves(D) * 64), h.pf_lds_bytes, st, p);
   else

@@ -82,7 +82,8 @@ typedef struct {
 } aqp_cache_desc;
 
 /* Attention parameters ([P50194] Code excerpt: the scheduler's num_heads_q,
- * num_heads_kv, head_dim, causal, window_size; the harness's soft_cap). */
+ * num_heads_kv, head_dim, causal, window_size, dynamic_causal; the harness's
+ * soft_cap, use_alibi, use_sink). */
 typedef struct {
   int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads; q head h reads KV head h / (Hq / Hkv) */
   int32_t num_kv_heads;       /* must equal the cache's */
@@ -95,7 +96,17 @@ typedef struct {
   float softcap;              /* 0: none; c > 0: logit z -> c * tanh(z / c), applied after sm_scale */
   int32_t decode_parallelism; /* work-groups the decode work is split across; 0 = one resident wave of
                                  work-groups on the current device (CUs x 3 for head_dim <= 128, x 2 above) */
-  int32_t reserved;
+  int32_t reserved;           /* 0 */
+  /* The harness parameters the page names without defining them; the readings taken: */
+  const int32_t* causal_per_seq; /* host int32 [num_seqs] of 0/1, or NULL (= `causal` for every
+                                    sequence). Read by aqp_get_schedule only: the schedule carries
+                                    each sequence's flag. A window needs every sequence causal. */
+  const float* alibi_slopes;  /* device fp32 [num_q_heads], or NULL: the logit of key j for a query
+                                 at position p gains slope[h] * (j - p), after the soft-cap. Read by
+                                 aqp_paged_attention. */
+  const float* sinks;         /* device fp32 [num_q_heads], or NULL: one more logit per q head in the
+                                 softmax with no value row (it only enlarges the normaliser). Read
+                                 by aqp_paged_attention. */
 } aqp_attn_params;
 
 /* Parse a kv_cache_dtype string ([P50194] Code excerpt: parse_fp8_kv_dtype

@@ -62,8 +62,12 @@ def compare(out_u16, ref_u16, where=""):
 class Run:
     """One workload through both paths."""
 
-    def __init__(self, w, torch, aqp, two_call_write=True, fill=0, par=0):
+    def __init__(self, w, torch, aqp, two_call_write=True, fill=0, par=0, alibi=None, sinks=None,
+                 causal_per_seq=None):
+        """alibi, sinks: float32 numpy arrays of one value per q head (or None); causal_per_seq:
+        one flag per sequence (or None)."""
         self.w, self.torch, self.aqp = w, torch, aqp
+        self.alibi, self.sinks, self.causal_per_seq = alibi, sinks, causal_per_seq
         say(f"[case] {w.name} seqs={len(w.seqs)} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
             f"bs={w.block_size} dtype={w.kv_dtype} window={w.window} cap={w.softcap}")
         self.b = b = workloads.make_batch(w)
@@ -87,8 +91,10 @@ class Run:
         torch.cuda.synchronize()
         del k, v, s
         mb = b.block_tables.shape[1]
+        dev32 = lambda a: None if a is None else torch.from_numpy(np.asarray(a, np.float32)).cuda()
         self.params = aqp.attn_params(w.num_q_heads, w.num_kv_heads, w.head_dim, mb, causal=w.causal,
-                                      window=w.window, softcap=w.softcap, decode_parallelism=par)
+                                      window=w.window, softcap=w.softcap, decode_parallelism=par,
+                                      causal_per_seq=causal_per_seq, alibi_slopes=dev32(alibi), sinks=dev32(sinks))
 
     def cache_matches(self):
         g = self.gcache.cpu().numpy()
@@ -123,7 +129,10 @@ class Run:
         qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
         rows = np.concatenate([np.arange(b.query_start_loc[i], b.query_start_loc[i + 1]) for i in idx])
         q = np.ascontiguousarray(b.q[rows])
+        f64 = lambda a: None if a is None else np.asarray(a, np.float32).astype(np.float64)
+        cps = None if self.causal_per_seq is None else np.asarray(self.causal_per_seq, np.int32)[idx]
         out = oracle.attention(self.odesc, self.ocache, q, b.block_tables[idx], sl, qsl, self.w.num_q_heads,
                                causal=self.w.causal, window=self.w.window, softcap=self.w.softcap,
-                               k_scale=b.k_scale, v_scale=b.v_scale)
+                               k_scale=b.k_scale, v_scale=b.v_scale, causal_per_seq=cps,
+                               alibi_slopes=f64(self.alibi), sinks=f64(self.sinks))
         return out, rows

@@ -67,6 +67,40 @@ def test_small_parity(aqp, w):
     compare(out[rows], ref, w.name)
 
 
+def _alibi_slopes(hq):
+    """The usual geometric ALiBi slopes 2^(-8 h / Hq), h = 1 .. Hq."""
+    return (2.0 ** (-8.0 * np.arange(1, hq + 1) / hq)).astype(np.float32)
+
+
+EXT = [
+    # (workload, ALiBi, sinks, per-sequence causal flags)
+    (W.Workload("ext_decode_alibi_sink_split", "fp8_e4m3", ((1, 900), (1, 40), (1, 2100)), 16, 4, 128, 16, 200,
+                seed=101), True, True, None),
+    (W.Workload("ext_mixed_pth_alibi_w_cap", "fp8_per_token_head", ((1, 500), (33, 120), (1, 64)), 8, 2, 64, 16, 60,
+                window=70, softcap=20.0, seed=102), True, False, None),
+    (W.Workload("ext_prefill_sinks_dyncausal", "int8_per_token_head", ((40, 40), (17, 50), (1, 30), (25, 25)), 8, 2,
+                128, 16, 40, seed=103), False, True, (1, 0, 1, 0)),
+    (W.Workload("ext_d256_all", "fp8_e5m2", ((29, 29), (1, 700), (8, 60)), 16, 2, 256, 32, 40, seed=104),
+     True, True, (0, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("case", EXT, ids=[c[0].name for c in EXT])
+def test_alibi_sinks_dynamic_causal_parity(aqp, case):
+    """The harness parameters the large-prefill page names (use_alibi, use_sink, dynamic_causal):
+    ALiBi slopes, per-head sink logits and per-sequence causal flags, decode (split and whole),
+    prefill and mixed batches, against the oracle."""
+    w, use_alibi, use_sinks, flags = case
+    rng = np.random.default_rng(w.seed)
+    alibi = _alibi_slopes(w.num_q_heads) if use_alibi else None
+    sinks = (rng.standard_normal(w.num_q_heads) * 2.0).astype(np.float32) if use_sinks else None
+    r = Run(w, torch, aqp, par=9, alibi=alibi, sinks=sinks, causal_per_seq=flags)
+    r.cache_matches()
+    out = r.gpu_attention()
+    ref, rows = r.oracle_attention()
+    compare(out[rows], ref, w.name)
+
+
 NAN_FILL = [
     W.Workload("nanfill_decode_pth", "fp8_per_token_head", ((1, 37), (1, 100), (1, 16)), 8, 2, 128, 16, 24, seed=91),
     W.Workload("nanfill_mixed_int8", "int8_per_token_head", ((1, 50), (21, 45)), 8, 2, 64, 32, 12, seed=92),

@@ -13,7 +13,7 @@ import workloads
 
 SEG = np.dtype([(n, "<i4") for n in "seq kvh head0 nheads k_lo k_hi q_tok part".split()])
 COMB = np.dtype([(n, "<i4") for n in "kvh head0 nheads q_tok first_part num_parts pad0 pad1".split()])
-PF = np.dtype([(n, "<i4") for n in "seq kvh q_lo q_hi L ql q_start k_hi_max head0 nheads pad0 pad1".split()])
+PF = np.dtype([(n, "<i4") for n in "seq kvh q_lo q_hi L ql q_start k_hi_max head0 nheads causal pad1".split()])
 
 
 def h_rows(s):
@@ -115,6 +115,7 @@ def test_prefill_coverage_and_order(seqs, hq, hkv, d, bs, window, par):
                 assert key not in seen
                 seen[key] = 1
         assert it["k_hi_max"] == it["L"] - it["ql"] + it["q_hi"]
+        assert it["causal"] == 1
     expect = {(b, k, t, hh) for b, (ql, L) in enumerate(seqs) if ql > 1 for k in range(hkv) for t in range(ql)
               for hh in range(G)}
     assert set(seen) == expect
@@ -197,3 +198,28 @@ def test_large_block_size_geometry_is_consistent():
     assert h["pf_lds_bytes"] == 4 * (2 * 32 * 256 * 1 + 2 * 32 * 4) + 4 * 32 * 256 * 2 + 2 * 2 * 32 * 4
     # decode: per wave 2 ring slots of 16 keys of K and V, one Q slot of 8 heads; merge area of 4 waves
     assert h["dec_lds_bytes"] == 4 * (2 * (2 * 16 * 256) + 8 * 256 * 2) + 4 * 8 * (256 + 2) * 4
+
+
+def test_per_sequence_causal_flags_and_seq_lens_are_recorded():
+    """dynamic_causal (one flag per sequence): non-causal prefill items span all L keys, causal
+    ones end at the last row's position; the schedule also carries every sequence's key count."""
+    seqs = ((12, 40), (9, 9), (1, 77), (20, 20))
+    flags = np.array([0, 1, 0, 1], np.int32)
+    sl = np.array([L for _, L in seqs], np.int32)
+    qsl = np.concatenate([[0], np.cumsum([q for q, _ in seqs])]).astype(np.int32)
+    desc = aqp.cache_desc(64, 16, 2, 64, "fp8_e4m3")
+    params = aqp.attn_params(8, 2, 64, 8, causal_per_seq=flags)
+    s = aqp.get_schedule(params, desc, sl, qsl)
+    _, _, _, pf = _arrays(s)
+    for it in pf:
+        c = flags[it["seq"]]
+        assert it["causal"] == c
+        assert it["k_hi_max"] == (it["L"] - it["ql"] + it["q_hi"] if c else it["L"])
+    h = s.header
+    assert np.array_equal(s.meta[h["off_seq_lens"]: h["off_seq_lens"] + 4 * len(seqs)].view(np.int32), sl)
+    with pytest.raises(aqp.AqpError) as e:
+        aqp.get_schedule(aqp.attn_params(8, 2, 64, 8, causal_per_seq=[1, 2, 0, 1]), desc, sl, qsl)
+    assert e.value.status == aqp.ERR_INVALID
+    with pytest.raises(aqp.AqpError) as e:
+        aqp.get_schedule(aqp.attn_params(8, 2, 64, 8, window=5, causal_per_seq=flags), desc, sl, qsl)
+    assert e.value.status == aqp.ERR_UNSUPPORTED
