@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -68,6 +69,32 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
   g->pf_lds_bytes = kPfStages * (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes + 2 * kPfKvTile * 4) +
                     4 * kPfKvTile * d.head_dim * kPfOperandBytes + 2 * (2 * kPfKvTile * 4);
   return AQP_OK;
+}
+
+// Second stream of the current device for mixed batches (created on first use, default
+// priority, kept until the process ends), with the events that fork it from and join it back
+// into a caller's stream. The mutex serialises the fork / launch / join of concurrent callers.
+SideStream* side_stream() {
+  static std::mutex mu;
+  static SideStream* per_dev[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    set_error("aqp_paged_attention: no current HIP device");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_dev[dev]) {
+    SideStream* ss = new SideStream();
+    if (hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss->join, hipEventDisableTiming) != hipSuccess) {
+      set_error("aqp_paged_attention: could not create the side stream");
+      delete ss;
+      return nullptr;
+    }
+    per_dev[dev] = ss;
+  }
+  return per_dev[dev];
 }
 
 int device_cu_count() {
@@ -481,17 +508,36 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
   a.alibi_slopes = params->alibi_slopes;
   a.sinks = params->sinks;
   a.hdr = &h;
+  auto run_decode = [&](void* st) -> int {
+    int r = launch_decode(desc->dtype, desc->mode, a, st);
+    if (r == AQP_OK && h.num_comb > 0) r = launch_combine(a, st);
+    return r;
+  };
+  if (h.num_pf_items > 0 && h.num_dec_segs > 0) {
+    // A mixed batch: the decode (HBM-bound) runs beside the prefill (matrix-bound) on a second
+    // stream of this device, forked from and joined back into the caller's stream, so the two
+    // kernels share the CUs instead of running one after the other.
+    SideStream* ss = side_stream();
+    if (!ss) return AQP_ERR_HIP;
+    std::lock_guard<std::mutex> lock(ss->mu);
+    hipStream_t st = (hipStream_t)stream;
+    if (hipEventRecord(ss->fork, st) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+      return fail(AQP_ERR_HIP, "aqp_paged_attention: fork to the side stream failed");
+    rc = run_decode(ss->s);
+    if (rc) return rc;
+    rc = launch_prefill(desc->dtype, desc->mode, a, stream);
+    if (rc) return rc;
+    if (hipEventRecord(ss->join, ss->s) != hipSuccess || hipStreamWaitEvent(st, ss->join, 0) != hipSuccess)
+      return fail(AQP_ERR_HIP, "aqp_paged_attention: join of the side stream failed");
+    return AQP_OK;
+  }
   if (h.num_pf_items > 0) {
     rc = launch_prefill(desc->dtype, desc->mode, a, stream);
     if (rc) return rc;
   }
   if (h.num_dec_segs > 0) {
-    rc = launch_decode(desc->dtype, desc->mode, a, stream);
+    rc = run_decode(stream);
     if (rc) return rc;
-    if (h.num_comb > 0) {
-      rc = launch_combine(a, stream);
-      if (rc) return rc;
-    }
   }
   return AQP_OK;
 }

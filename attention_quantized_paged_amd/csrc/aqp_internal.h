@@ -12,6 +12,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/aqp.h"
 
 namespace aqp {
@@ -62,6 +64,12 @@ constexpr int decode_wgs_per_cu(int head_dim, int32_t lds_bytes) {
 }
 // Compute units of the current device (256 on MI355X; 256 when no device is visible).
 int device_cu_count();
+struct SideStream {
+  hipStream_t s;
+  hipEvent_t fork, join;
+  std::mutex mu;
+};
+SideStream* side_stream();
 
 // Geometry derived from the cache descriptor. One function computes it for
 // both the scheduler and the launcher.

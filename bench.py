@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 1 GiB device-to-device copy (calibrates the HBM byte counters)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="time a large bf16 GEMM from the vendor library (the achievable dense bf16 rate)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="one JSON line per configuration (1-5): cache write of its history and one "
+                         "attention call, median kernel times with a 1 GiB read between repetitions")
     return ap.parse_args()
 
 
@@ -223,6 +228,76 @@ def cpu_baseline(W, s, target_seconds=10.0):
                       f"dequantised, gathered cache"}
 
 
+def run_all_configs(torch, aqp, W, args):
+    """Every configuration through the whole path once: the cache write of its full history
+    (bf16 K/V drawn on the device, per-tensor scales absmax/qmax of that history), then one
+    paged-attention call; medians of HIP-event times over repetitions separated by a 1 GiB read
+    (cold L2 and Infinity Cache). Decode KV GB/s counts every visible key and value code (and
+    per-token-head scales); prefill TFLOP/s counts 4 * D flops per visible (query, key) pair and
+    q head. Mixed batches report the one call's time against both units."""
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    for w in (W.CFG1, W.CFG2, W.CFG3, W.CFG4, W.CFG5A, W.CFG5B):
+        log(args, f"[bench] {w.name}")
+        b = W.make_batch(w, with_kv=False)
+        desc = aqp.cache_desc(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
+        cache = torch.zeros(aqp.cache_bytes(desc)[2], dtype=torch.uint8, device="cuda")
+        n = int(b.seq_lens.sum())
+        g = torch.Generator(device="cuda").manual_seed(w.seed)
+        k = (torch.randn((n, w.num_kv_heads, w.head_dim), device="cuda", generator=g) * w.sigma).to(torch.bfloat16)
+        v = (torch.randn((n, w.num_kv_heads, w.head_dim), device="cuda", generator=g) * w.sigma).to(torch.bfloat16)
+        pth = desc.mode == 1
+        qm = {1: 448.0, 2: 57344.0, 3: 127.0}[desc.dtype]
+        ks = float(k.float().abs().max()) / qm
+        vs = float(v.float().abs().max()) / qm
+        slots = torch.from_numpy(b.slots_hist).cuda()
+        cw = lambda: aqp.cache_write(desc, cache, k, v, slots, ks, vs)
+        cw()
+        cw_ms = timed(cw, 5)
+        cw_bytes = n * w.num_kv_heads * w.head_dim * 2 * 3 + n * 8 + (n * w.num_kv_heads * 8 if pth else 0)
+        del k, v
+        q = (torch.randn((int(b.query_start_loc[-1]), w.num_q_heads, w.head_dim), device="cuda", generator=g)
+             * w.sigma).to(torch.bfloat16)
+        out = torch.empty_like(q)
+        bt = torch.from_numpy(b.block_tables).cuda()
+        params = aqp.attn_params(w.num_q_heads, w.num_kv_heads, w.head_dim, b.block_tables.shape[1], causal=w.causal,
+                                 window=w.window, softcap=w.softcap)
+        sch = aqp.get_schedule(params, desc, b.seq_lens, b.query_start_loc)
+        md = torch.from_numpy(sch.meta.copy()).cuda()
+        scr = torch.empty(max(4, sch.scratch_bytes), dtype=torch.uint8, device="cuda")
+        att = lambda: aqp.paged_attention(params, desc, cache, q, bt, sch.meta, md, ks, vs, scr, scr.numel(), out)
+        for _ in range(3):
+            att()
+        att_ms = timed(att, 20)
+        kvb = W.kv_read_bytes(w, per_token_head=pth)
+        fl = W.prefill_flops(w)
+        row = {"workload": w.name, "kv_cache_dtype": w.kv_dtype, "attention_ms": round(att_ms, 4),
+               "cache_write": {"tokens": n, "ms": round(cw_ms, 4), "gbs": round(cw_bytes / cw_ms / 1e6, 1),
+                               "frac_of_hbm_peak": round(cw_bytes / cw_ms / 1e6 / HBM_PEAK_GBS, 4)}}
+        if kvb:
+            row["decode_kv_bytes"] = kvb
+            row["decode_gbs"] = round(kvb / att_ms / 1e6, 1)
+            row["decode_frac_of_hbm_peak"] = round(kvb / att_ms / 1e6 / HBM_PEAK_GBS, 4)
+        if fl:
+            row["prefill_flops"] = fl
+            row["prefill_tflops"] = round(fl / att_ms / 1e9, 1)
+            row["prefill_frac_of_bf16_peak"] = round(fl / att_ms / 1e9 / BF16_PEAK_TFLOPS, 4)
+        print(json.dumps(row), flush=True)
+        del cache, q, out, scr
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -249,8 +324,30 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
                           "GBps_read_plus_write": round(2 * n / ms / 1e6, 1)}))
         return
+    if args.mfma_probe:
+        n = 8192
+        a = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+        b = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        tf = 2 * n ** 3 / ms / 1e9
+        print(json.dumps({"gemm": f"bf16 {n}x{n}x{n} torch.matmul", "ms": round(ms, 4), "tflops": round(tf, 1),
+                          "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}))
+        return
     import attention_quantized_paged_amd as aqp
     import workloads as W
+
+    if args.all_configs:
+        run_all_configs(torch, aqp, W, args)
+        return
 
     log(args, "[bench] setting up decode batch")
     s = setup_decode(torch, aqp, W, args)
