@@ -146,6 +146,57 @@ def test_reused_schedule_copy_gives_identical_results(aqp):
     compare(last[rows], ref, w.name)
 
 
+GUARDED = [
+    # the large-prefill shape the scratch-sizing page's regression test uses (block 2176, head_dim
+    # 256), shortened so the oracle stays fast; a split decode; a mixed per-token-head batch
+    W.scaled(W.CFG2, name="guard_prefill_bs2176_d256", seqs=((300, 300), (1, 900), (64, 64)), num_blocks=5),
+    W.scaled(W.CFG3, name="guard_decode_split", seqs=((1, 3000), (1, 129), (1, 2047)), num_blocks=400),
+    W.scaled(W.CFG4, name="guard_mixed_int8_pth", seqs=((1, 600), (70, 310), (1, 17)), num_blocks=80),
+    W.Workload("guard_e5m2_pth_d64", "fp8_e5m2_per_token_head", ((1, 70), (9, 40)), 8, 2, 64, 16, 10, seed=95),
+]
+
+
+@pytest.mark.parametrize("w", GUARDED, ids=[w.name for w in GUARDED])
+def test_guard_bands_untouched(aqp, w):
+    """Cache, scratch and output sit inside larger allocations whose bytes before and after hold a
+    pattern: after the cache write and the attention call every guard byte is unchanged (an
+    out-of-range write by any kernel, the failure class of a schedule sized for the wrong element
+    size, would show here), and the results still match the oracle."""
+    G = 1 << 16  # guard bytes on each side
+    pat = 0xA5
+    say(f"[case] guards {w.name}")
+    b = workloads.make_batch(w)
+    desc = aqp.cache_desc(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
+    total = aqp.cache_bytes(desc)[2]
+    cbuf = torch.full((total + 2 * G,), pat, dtype=torch.uint8, device="cuda")
+    cache = cbuf[G:G + total]
+    aqp.cache_write(desc, cache, to_dev(b.k_hist, torch), to_dev(b.v_hist, torch), to_dev(b.slots_hist, torch),
+                    b.k_scale, b.v_scale)
+    params = aqp.attn_params(w.num_q_heads, w.num_kv_heads, w.head_dim, b.block_tables.shape[1], causal=w.causal,
+                             window=w.window, softcap=w.softcap, decode_parallelism=5)
+    sch = aqp.get_schedule(params, desc, b.seq_lens, b.query_start_loc)
+    nsc = sch.scratch_bytes
+    sbuf = torch.full((nsc + 2 * G,), pat, dtype=torch.uint8, device="cuda")
+    q = to_dev(b.q, torch)
+    nout = q.numel() * 2
+    obuf = torch.full((nout + 2 * G,), pat, dtype=torch.uint8, device="cuda")
+    out = obuf[G:G + nout].view(torch.int16).view(q.shape)
+    aqp.paged_attention(params, desc, cache, q, to_dev(b.block_tables, torch), sch.meta,
+                        torch.from_numpy(sch.meta).cuda(), b.k_scale, b.v_scale, sbuf[G:G + nsc] if nsc else None,
+                        nsc, out)
+    torch.cuda.synchronize()
+    for name, buf, n in (("cache", cbuf, total), ("scratch", sbuf, nsc), ("out", obuf, nout)):
+        h = buf.cpu().numpy()
+        assert np.all(h[:G] == pat) and np.all(h[G + n:] == pat), f"{name}: a guard byte changed"
+    od = oracle.CacheDesc(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, OFMT[desc.dtype], desc.mode)
+    ocache = np.full(od.total_bytes, pat, np.uint8)
+    oracle.cache_write(od, ocache, b.k_hist, b.v_hist, b.slots_hist, b.k_scale, b.v_scale)
+    assert np.array_equal(cache.cpu().numpy(), ocache)
+    ref = oracle.attention(od, ocache, b.q, b.block_tables, b.seq_lens, b.query_start_loc, w.num_q_heads,
+                           causal=w.causal, window=w.window, softcap=w.softcap, k_scale=b.k_scale, v_scale=b.v_scale)
+    compare(out.cpu().numpy().view(np.uint16), ref, w.name)
+
+
 def test_block_permutation_bit_identical(aqp):
     """Same keys in a contiguous pool or a permuted one: bit-identical GPU output."""
     w = W.scaled(W.CFG4, name="perm_a", seqs=((1, 500), (40, 200)), num_blocks=60)
