@@ -48,9 +48,13 @@ constexpr int dec_stages(int head_dim) { return head_dim >= 256 ? 2 : 3; }
 constexpr int dec_slot_bytes(int head_dim, int mode) {
   return 2 * kDecIterKeys * head_dim + (mode == AQP_SCALE_PER_TOKEN_HEAD ? 2 * kDecIterKeys * 4 : 0);
 }
+// Floats per (wave, head) row of the merge area: D of O, then m and l, padded to a multiple of 4
+// so each lane's 4 consecutive values move as one 16-byte LDS access; with D/4 + 1 16-byte units
+// per row, the 16 heads of a 16-lane pass start on 16 distinct units (no bank conflicts).
+constexpr int merge_stride(int head_dim) { return head_dim + 4; }
 constexpr int32_t dec_lds_bytes(int head_dim, int mode, int group_heads) {
   return kDecWaves * (dec_stages(head_dim) * dec_slot_bytes(head_dim, mode) + group_heads * head_dim * 2) +
-         kDecWaves * group_heads * (head_dim + 2) * 4;
+         kDecWaves * group_heads * merge_stride(head_dim) * 4;
 }
 // Waves per SIMD the decode kernel's registers are sized for; a work-group is kDecWaves compute
 // waves and one merging wave.

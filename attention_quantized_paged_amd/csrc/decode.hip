@@ -69,7 +69,7 @@ __device__ __forceinline__ int dec_swz(int row) {
 // need no ordering against the other waves, and the copies in flight must not be waited for).
 __device__ __forceinline__ void block_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Merge of the four compute waves' (O, m, l) of one segment, left in LDS as [wave][head][D + 2],
+// Merge of the four compute waves' (O, m, l) of one segment, left in LDS as [wave][head][merge_stride(D)],
 // into the output rows (bf16) or the segment's partial slot. Lane (r16, kg) handles head r16 and
 // head-dim elements t * 16 + 4 kg + r, the layout the waves' accumulators have.
 template <int D>
@@ -79,7 +79,7 @@ __device__ __forceinline__ void merge_store(const DecArgs& a, const float* mg, i
   float mw[kDecWaves], lw[kDecWaves];
 #pragma unroll
   for (int w = 0; w < kDecWaves; ++w) {
-    const float* src = mg + (w * gh + r16) * (D + 2);
+    const float* src = mg + (w * gh + r16) * merge_stride(D);
     mw[w] = src[D];
     lw[w] = src[D + 1];
   }
@@ -99,7 +99,7 @@ __device__ __forceinline__ void merge_store(const DecArgs& a, const float* mg, i
     o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) {
-      const float* src = mg + (w * gh + r16) * (D + 2) + t * 16 + 4 * kg;
+      const f32x4 src = *(const f32x4*)(mg + (w * gh + r16) * merge_stride(D) + t * 16 + 4 * kg);
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[t][r] += f[w] * src[r];
     }
@@ -161,7 +161,7 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
   const int QB = gh * D * 2;  // bytes of a Q slot: the group's q rows, bf16
   uint8_t* ring = smem + wave * (NS * SLOT);
   uint8_t* qslots = smem + kDecWaves * NS * SLOT + wave * (NQ * QB);
-  float* mg = (float*)(smem + kDecWaves * NS * SLOT + kDecWaves * NQ * QB);  // [wave][head][D + 2]
+  float* mg = (float*)(smem + kDecWaves * NS * SLOT + kDecWaves * NQ * QB);  // [wave][head][merge_stride(D)]
   const uint32_t ring_lds = lds_addr(ring), q_lds = lds_addr(qslots);
   const int s_begin = as_const(a.wg_start)[blockIdx.x], s_end = as_const(a.wg_start)[blockIdx.x + 1];
 
@@ -425,11 +425,9 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
     l = sum_over_rows(l);
     block_sync_lds();  // the fetching wave has read the previous segment's values
     if (r16 < gh) {
-      float* dst = mg + (wave * gh + r16) * (D + 2);
+      float* dst = mg + (wave * gh + r16) * merge_stride(D);
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[t * 16 + 4 * kg + r] = acc[t][r];
+      for (int t = 0; t < NT; ++t) *(f32x4*)(dst + t * 16 + 4 * kg) = acc[t];
       if (kg == 0) { dst[D] = m; dst[D + 1] = l; }
     }
     block_sync_lds();

@@ -197,7 +197,7 @@ def test_large_block_size_geometry_is_consistent():
     # prefill: 4 ring stages of codes and scales, two K and two V bf16 images, two scale copies
     assert h["pf_lds_bytes"] == 4 * (2 * 32 * 256 * 1 + 2 * 32 * 4) + 4 * 32 * 256 * 2 + 2 * 2 * 32 * 4
     # decode: per wave 2 ring slots of 16 keys of K and V, one Q slot of 8 heads; merge area of 4 waves
-    assert h["dec_lds_bytes"] == 4 * (2 * (2 * 16 * 256) + 8 * 256 * 2) + 4 * 8 * (256 + 2) * 4
+    assert h["dec_lds_bytes"] == 4 * (2 * (2 * 16 * 256) + 8 * 256 * 2) + 4 * 8 * (256 + 4) * 4
 
 
 def test_per_sequence_causal_flags_and_seq_lens_are_recorded():
