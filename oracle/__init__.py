@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-FMT_E4M3, FMT_E5M2, FMT_INT8 = 1, 2, 3
+FMT_BF16, FMT_E4M3, FMT_E5M2, FMT_INT8 = 0, 1, 2, 3
 MODE_PER_TENSOR, MODE_PER_TOKEN_HEAD = 0, 1
 
 

@@ -163,8 +163,11 @@ uint16_t orc_f64_to_bf16(double x) {
 /* followed by block_size fp32 scales (one per row: the "inline" scale of    */
 /* the PR 38378 page). Each page is padded to a multiple of 128 bytes.       */
 /* ------------------------------------------------------------------------ */
+/* Bytes per stored element: 2 for the unquantised bf16 cache, 1 for every code format. */
+static int elem_bytes(int fmt) { return fmt == ORC_FMT_BF16 ? 2 : 1; }
+
 int64_t orc_page_bytes(const orc_cache_desc* d) {
-  int64_t content = (int64_t)d->block_size * d->head_dim;
+  int64_t content = (int64_t)d->block_size * d->head_dim * elem_bytes(d->fmt);
   if (d->mode == ORC_MODE_PER_TOKEN_HEAD) content += 4 * (int64_t)d->block_size;
   return (content + 127) / 128 * 128;
 }
@@ -193,6 +196,7 @@ int orc_cache_write(const orc_cache_desc* d, uint8_t* cache, const uint16_t* k, 
   int64_t t;
   for (t = 0; t < num_tokens; ++t)
     if (slot_mapping[t] >= total_slots) bad = 1;
+  if (d->fmt == ORC_FMT_BF16 && d->mode != ORC_MODE_PER_TENSOR) bad = 1;
   if (bad) return -1;
 #pragma omp parallel for schedule(static)
   for (t = 0; t < num_tokens; ++t) {
@@ -204,6 +208,10 @@ int orc_cache_write(const orc_cache_desc* d, uint8_t* cache, const uint16_t* k, 
       for (int kv = 0; kv < 2; ++kv) {
         const uint16_t* src = (kv == 0 ? k : v) + t * token_stride + (int64_t)h * D;
         uint8_t* page = cache + orc_page_offset(d, block, kv, h);
+        if (d->fmt == ORC_FMT_BF16) { /* unquantised: the input row as given */
+          memcpy(page + (int64_t)off * D * 2, src, (size_t)D * 2);
+          continue;
+        }
         float s;
         if (d->mode == ORC_MODE_PER_TOKEN_HEAD) {
           float a = 0.0f;
@@ -234,6 +242,14 @@ void orc_read_row(const orc_cache_desc* d, const uint8_t* cache, int kv, int64_t
                   int off, float k_scale, float v_scale, double* row) {
   const int D = d->head_dim;
   const uint8_t* page = cache + orc_page_offset(d, block, kv, head);
+  if (d->fmt == ORC_FMT_BF16) {
+    uint16_t w;
+    for (int i = 0; i < D; ++i) {
+      memcpy(&w, page + ((int64_t)off * D + i) * 2, 2);
+      row[i] = (double)orc_bf16_to_f32(w);
+    }
+    return;
+  }
   double s;
   if (d->mode == ORC_MODE_PER_TOKEN_HEAD) {
     float sf;

@@ -32,7 +32,9 @@
 extern "C" {
 #endif
 
-enum { ORC_FMT_E4M3 = 1, ORC_FMT_E5M2 = 2, ORC_FMT_INT8 = 3 };
+/* ORC_FMT_BF16: the unquantised cache ("auto" dtype): the bf16 inputs stored as given, two bytes
+ * per element, per-tensor mode only (no scales). */
+enum { ORC_FMT_BF16 = 0, ORC_FMT_E4M3 = 1, ORC_FMT_E5M2 = 2, ORC_FMT_INT8 = 3 };
 enum { ORC_MODE_PER_TENSOR = 0, ORC_MODE_PER_TOKEN_HEAD = 1 };
 
 typedef struct {
