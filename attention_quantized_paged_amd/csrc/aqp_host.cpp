@@ -39,11 +39,12 @@ static int fail(int code, const char* fmt, ...) {
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Which (dtype, mode) pairs are built: per-tensor fp8 (e4m3, e5m2) as on the
-// PR 39445 page, per-token-head int8 / fp8 e4m3 as on the PR 38378 page.
+// PR 39445 page, per-token-head int8 / fp8 e4m3 as on the PR 38378 page, the
+// two remaining code pairs, and the unquantised bf16 cache ("auto", no scales).
 static int check_dtype_mode(int32_t dtype, int32_t mode, const char** why) {
   if (mode != AQP_SCALE_PER_TENSOR && mode != AQP_SCALE_PER_TOKEN_HEAD) { *why = "unknown scale mode"; return AQP_ERR_INVALID; }
-  if (dtype == AQP_KV_AUTO) { *why = "kv dtype 'auto' (unquantised cache) is not supported by this build"; return AQP_ERR_UNSUPPORTED; }
-  if (dtype != AQP_KV_FP8_E4M3 && dtype != AQP_KV_FP8_E5M2 && dtype != AQP_KV_INT8) { *why = "unknown kv dtype"; return AQP_ERR_INVALID; }
+  if (dtype == AQP_KV_AUTO && mode != AQP_SCALE_PER_TENSOR) { *why = "an unquantised cache has no per-token-head scales"; return AQP_ERR_UNSUPPORTED; }
+  if (dtype != AQP_KV_AUTO && dtype != AQP_KV_FP8_E4M3 && dtype != AQP_KV_FP8_E5M2 && dtype != AQP_KV_INT8) { *why = "unknown kv dtype"; return AQP_ERR_INVALID; }
   return AQP_OK;
 }
 
@@ -56,8 +57,10 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
   if ((int64_t)d.block_size * d.head_dim > (1ll << 30)) { *why = "block_size too large"; return AQP_ERR_UNSUPPORTED; }
   g->head_dim = d.head_dim;
   g->block_size = d.block_size;
-  g->kv_elem_bytes = 1;      // every supported dtype stores one byte per element
-  g->staged_elem_bytes = 1;  // the kernels stage raw codes in LDS and widen them in registers
+  // bytes of one stored element: one per code; two for the unquantised bf16 cache. The kernels
+  // stage raw elements in LDS, so the staged element has the same size.
+  g->kv_elem_bytes = d.dtype == AQP_KV_AUTO ? 2 : 1;
+  g->staged_elem_bytes = g->kv_elem_bytes;
   g->scale_bytes = d.mode == AQP_SCALE_PER_TOKEN_HEAD ? 4 : 0;
   g->pad_ = 0;
   g->page_bytes = round_up((int64_t)d.block_size * d.head_dim * g->kv_elem_bytes + (int64_t)d.block_size * g->scale_bytes, 128);
@@ -131,10 +134,10 @@ extern "C" int aqp_parse_kv_dtype(const char* s, int32_t* dtype, int32_t* mode) 
   for (auto& e : table) {
     if (std::strcmp(s, e.name) == 0) { *dtype = e.dt; *mode = e.md; return AQP_OK; }
   }
-  if (std::strcmp(s, "auto") == 0) {
+  if (std::strcmp(s, "auto") == 0) {  // the unquantised cache: bf16 elements, no scales
     *dtype = AQP_KV_AUTO;
     *mode = AQP_SCALE_PER_TENSOR;
-    return fail(AQP_ERR_UNSUPPORTED, "kv_cache_dtype 'auto' (unquantised cache) is not supported by this build");
+    return AQP_OK;
   }
   return fail(AQP_ERR_INVALID, "unknown kv_cache_dtype '%s'", s);
 }
@@ -254,7 +257,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   pf.clear();
   const int32_t max_hpu = heads_per_unit(desc->head_dim);
   const int32_t hpu = std::min<int32_t>(G, max_hpu);
-  const int32_t dec_lds = dec_lds_bytes(desc->head_dim, desc->mode, hpu);
+  const int32_t dec_lds = dec_lds_bytes(desc->head_dim, desc->mode, hpu, g.kv_elem_bytes);
   if (dec_lds > kLdsPerCu) return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: decode needs %d bytes of LDS", dec_lds);
   int64_t total_tiles = 0, dec_keys = 0;
   for (int32_t b = 0; b < num_seqs; ++b) {
@@ -331,6 +334,13 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
     }
     while (w_cur < P) wg_start[++w_cur] = (int32_t)segs.size();
   }
+
+  if (desc->dtype == AQP_KV_AUTO && desc->head_dim > 128 && total_q > 0)
+    return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: an unquantised cache at head_dim %d is not built", desc->head_dim);
+  if (desc->dtype == AQP_KV_AUTO)
+    for (int32_t b = 0; b < num_seqs; ++b)
+      if (qsl[b + 1] - qsl[b] > 1)
+        return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: prefill over an unquantised cache is not built (sequence %d has %d queries)", b, qsl[b + 1] - qsl[b]);
 
   // ---- prefill items: (sequence, KV head, run of query tokens, run of its q heads): all G
   // heads of the KV head when G <= kPfRows, else one token and kPfRows heads at a time;
@@ -475,7 +485,7 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
   MISMATCH_IF(h.sm_scale != effective_sm_scale(*params) || h.softcap != params->softcap, "logit scale / soft-cap");
   MISMATCH_IF(h.tile_keys != kTileKeys || h.dec_iter_keys != kDecIterKeys || h.dec_waves != kDecWaves || h.pf_rows != kPfRows ||
               h.pf_kv_tile != kPfKvTile || h.heads_per_unit != heads_per_unit(desc->head_dim) ||
-              h.dec_lds_bytes != dec_lds_bytes(desc->head_dim, desc->mode, std::min<int32_t>(params->num_q_heads / params->num_kv_heads, heads_per_unit(desc->head_dim))) ||
+              h.dec_lds_bytes != dec_lds_bytes(desc->head_dim, desc->mode, std::min<int32_t>(params->num_q_heads / params->num_kv_heads, heads_per_unit(desc->head_dim)), g.kv_elem_bytes) ||
               h.pf_lds_bytes != g.pf_lds_bytes, "tile geometry");
   if ((int64_t)scratch_bytes < h.scratch_bytes)
     return fail(AQP_ERR_SCRATCH_TOO_SMALL, "aqp_paged_attention: scratch of %zu bytes, schedule needs %lld", scratch_bytes, (long long)h.scratch_bytes);
@@ -503,8 +513,8 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
   a.causal = params->causal;
   a.sm_scale = h.sm_scale;
   a.softcap = params->softcap;
-  a.k_scale = desc->mode == AQP_SCALE_PER_TENSOR ? k_scale : 1.0f;
-  a.v_scale = desc->mode == AQP_SCALE_PER_TENSOR ? v_scale : 1.0f;
+  a.k_scale = desc->mode == AQP_SCALE_PER_TENSOR && desc->dtype != AQP_KV_AUTO ? k_scale : 1.0f;
+  a.v_scale = desc->mode == AQP_SCALE_PER_TENSOR && desc->dtype != AQP_KV_AUTO ? v_scale : 1.0f;
   a.alibi_slopes = params->alibi_slopes;
   a.sinks = params->sinks;
   a.hdr = &h;

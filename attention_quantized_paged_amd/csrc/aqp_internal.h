@@ -44,16 +44,17 @@ constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per compute unit (gfx950)
 // Decode LDS: per compute wave, a ring of dec_stages tiles (each the K and V codes of 16 keys plus
 // their per-token-head scales) and one Q slot (the q rows of one segment); then the merge area
 // where the compute waves hand their (O, m, l) to the merging wave.
-constexpr int dec_stages(int head_dim) { return head_dim >= 256 ? 2 : 3; }
-constexpr int dec_slot_bytes(int head_dim, int mode) {
-  return 2 * kDecIterKeys * head_dim + (mode == AQP_SCALE_PER_TOKEN_HEAD ? 2 * kDecIterKeys * 4 : 0);
+// (eb: bytes per stored element, 1 for the codes, 2 for the unquantised bf16 cache)
+constexpr int dec_stages(int head_dim, int eb) { return head_dim * eb >= 256 ? 2 : 3; }
+constexpr int dec_slot_bytes(int head_dim, int mode, int eb) {
+  return 2 * kDecIterKeys * head_dim * eb + (mode == AQP_SCALE_PER_TOKEN_HEAD ? 2 * kDecIterKeys * 4 : 0);
 }
 // Floats per (wave, head) row of the merge area: D of O, then m and l, padded to a multiple of 4
 // so each lane's 4 consecutive values move as one 16-byte LDS access; with D/4 + 1 16-byte units
 // per row, the 16 heads of a 16-lane pass start on 16 distinct units (no bank conflicts).
 constexpr int merge_stride(int head_dim) { return head_dim + 4; }
-constexpr int32_t dec_lds_bytes(int head_dim, int mode, int group_heads) {
-  return kDecWaves * (dec_stages(head_dim) * dec_slot_bytes(head_dim, mode) + group_heads * head_dim * 2) +
+constexpr int32_t dec_lds_bytes(int head_dim, int mode, int group_heads, int eb) {
+  return kDecWaves * (dec_stages(head_dim, eb) * dec_slot_bytes(head_dim, mode, eb) + group_heads * head_dim * 2) +
          kDecWaves * group_heads * merge_stride(head_dim) * 4;
 }
 // Waves per SIMD the decode kernel's registers are sized for; a work-group is kDecWaves compute

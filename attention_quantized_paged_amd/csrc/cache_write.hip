@@ -101,6 +101,11 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
       const int64_t blk = slot[u] / a.block_size;
       const int off = (int)(slot[u] - blk * a.block_size);
       uint8_t* page = a.cache + blk * a.block_bytes + (int64_t)(kv[u] * a.num_kv_heads + h[u]) * a.page_bytes;
+      if constexpr (DT == AQP_KV_AUTO) {
+        // the unquantised cache stores the row as given: 16 bytes in, 16 bytes out
+        *(uint4*)(page + (int64_t)off * D * 2 + sub * 16) = in[u];
+        continue;
+      }
       uint2 codes;
       codes.x = encode4<DT>(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
       codes.y = encode4<DT>(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
@@ -141,6 +146,7 @@ static int dispatch_d(const CacheWriteArgs& a, hipStream_t st) {
 
 int launch_cache_write(int dtype, int mode, const CacheWriteArgs& a, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_AUTO) return dispatch_d<AQP_KV_AUTO, AQP_SCALE_PER_TENSOR>(a, st);
   if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_FP8_E4M3) return dispatch_d<AQP_KV_FP8_E4M3, AQP_SCALE_PER_TENSOR>(a, st);
   if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_FP8_E5M2) return dispatch_d<AQP_KV_FP8_E5M2, AQP_SCALE_PER_TENSOR>(a, st);
   if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_INT8) return dispatch_d<AQP_KV_INT8, AQP_SCALE_PER_TOKEN_HEAD>(a, st);

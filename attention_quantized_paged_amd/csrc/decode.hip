@@ -55,13 +55,13 @@ struct DecArgs {
   const float* sinks;       // [num_q_heads] sink logits or null
 };
 
-// Stored 16-byte chunk of logical chunk c in staged row `row` (rows of D bytes): c ^ dec_swz(row).
-// Rows that fall on the same LDS banks (same row / (256 / D) residue) get distinct offsets, so the
-// 16 rows of a K operand read and the 4 x 2 rows of a transposed V read hit distinct banks.
-template <int D>
+// Stored 16-byte chunk of logical chunk c in staged row `row` (rows of ROWB bytes): c ^ dec_swz(row).
+// Rows that fall on the same LDS banks (same row / (256 / ROWB) residue) get distinct offsets, so
+// the 16 rows of a K operand read and the 4 x 2 rows of a transposed V read hit distinct banks.
+template <int ROWB>
 __device__ __forceinline__ int dec_swz(int row) {
-  constexpr int CPR = D / 16;
-  constexpr int RPB = D >= 256 ? 1 : 256 / D;
+  constexpr int CPR = ROWB / 16;
+  constexpr int RPB = ROWB >= 256 ? 1 : 256 / ROWB;
   return (row / RPB) % CPR;
 }
 
@@ -142,16 +142,19 @@ template <int D, int DT, int MODE, bool CAP>
 __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_per_eu(dec_waves_per_simd(D)))) void decode_kernel(DecArgs a) {
   constexpr int NT = D / 16;   // 16-wide head-dim tiles of the output
   constexpr int QS = D / 32;   // 32-deep MFMA steps of QK^T
-  constexpr int CPR = D / 16;  // 16-byte chunks per staged row
+  constexpr int EB = DT == AQP_KV_AUTO ? 2 : 1;   // bytes per stored element (bf16 when unquantised)
+  constexpr int ROWB = D * EB;                    // bytes of one staged key row
+  constexpr int CPR = ROWB / 16;                  // 16-byte chunks per staged row
   constexpr int STEP = kDecWaves * kDecIterKeys;  // keys between a wave's consecutive tiles
   constexpr int PTH = MODE == AQP_SCALE_PER_TOKEN_HEAD ? 1 : 0;
-  constexpr int NS = dec_stages(D);               // ring slots per wave
+  constexpr int NS = dec_stages(D, EB);           // ring slots per wave
   constexpr int NQ = 1;                           // Q slots per wave
-  constexpr int TB = kDecIterKeys * D;            // bytes of one K (or V) tile
+  constexpr int TB = kDecIterKeys * ROWB;         // bytes of one K (or V) tile
   constexpr int KI = TB / 1024;                   // 1 KB copies per K (or V) tile
-  constexpr int SLOT = dec_slot_bytes(D, MODE);   // K tile, V tile, K scales, V scales
+  constexpr int SLOT = dec_slot_bytes(D, MODE, EB);  // K tile, V tile, K scales, V scales
   constexpr int IPT = 2 * KI + PTH;               // copies per tile
-  static_assert(KI >= 1 && IPT * (NS - 1) <= 15, "tile copies and waits");
+  static_assert(KI >= 1 && IPT * (NS - 1) <= 63, "tile copies and waits");
+  static_assert(EB == 1 || !PTH, "the unquantised cache has no scales");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -184,15 +187,23 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
   const int tr_row = 4 * kg + (tr_i & 3);
   const int tr_hi = tr_i >> 2;
   const int tr_base = tr_row * D + (r16 & 1) * 8;
-  const int tr_swz = dec_swz<D>(tr_row);
-  const int k_swz = dec_swz<D>(r16);
+  const int tr_swz = dec_swz<ROWB>(tr_row);
+  const int k_swz = dec_swz<ROWB>(r16);
+  // unquantised V rows: lane (r16, kg) reads keys 4kg + r of head-dim column t * 16 + r16, one bf16
+  // each, from logical chunk 2t + r16 / 8 of row 4kg + r
+  int v16_row[4], v16_swz[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    v16_row[r] = (4 * kg + r) * ROWB + (r16 & 7) * 2;
+    v16_swz[r] = dec_swz<ROWB>(4 * kg + r);
+  }
   // byte offset, within a tile's 16 rows of a page, of this lane's 16-byte chunk in copy i:
   // LDS chunk q = 64 i + lane holds logical chunk (q % CPR) ^ dec_swz(row) of row q / CPR
   int dma_off[KI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
     const int q = 64 * i + lane;
-    dma_off[i] = (q / CPR) * D + (((q % CPR) ^ dec_swz<D>(q / CPR)) << 4);
+    dma_off[i] = (q / CPR) * ROWB + (((q % CPR) ^ dec_swz<ROWB>(q / CPR)) << 4);
   }
 
   // without a soft-cap, log2(e) folds into the logit scale
@@ -259,7 +270,7 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
     const bool ok = (uint32_t)is_blk < (uint32_t)a.num_blocks;
     ok_bits |= (uint64_t)ok << (n_issued & 63);
     const uint8_t* kpage = is_kv + (uint64_t)(ok ? (uint32_t)is_blk : 0u) * (uint64_t)a.block_bytes +
-                           (int64_t)is_p.r0 * D;
+                           (int64_t)is_p.r0 * ROWB;
     const uint8_t* vpage = kpage + (int64_t)a.num_kv_heads * a.page_bytes;
     const uint32_t slot = ring_lds + is_slot;
 #pragma unroll
@@ -332,16 +343,36 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
 
       // ---- S^T = K * Q^T: lane holds keys k0 + 4kg + r of head r16
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (EB == 1) {
 #pragma unroll
-      for (int c2 = 0; c2 < QS / 2; ++c2) {
-        const uint4 w = *(const uint4*)(kl + r16 * D + (((kg * (QS / 2) + c2) ^ k_swz) << 4));
-        s = mfma16x16x32(widen8<DT>(w.x, w.y), qb[2 * c2], s);
-        s = mfma16x16x32(widen8<DT>(w.z, w.w), qb[2 * c2 + 1], s);
+        for (int c2 = 0; c2 < QS / 2; ++c2) {
+          const uint4 w = *(const uint4*)(kl + r16 * ROWB + (((kg * (QS / 2) + c2) ^ k_swz) << 4));
+          s = mfma16x16x32(widen8<DT>(w.x, w.y), qb[2 * c2], s);
+          s = mfma16x16x32(widen8<DT>(w.z, w.w), qb[2 * c2 + 1], s);
+        }
+      } else {
+        // bf16 rows: each 16-byte chunk is one operand (depth kg * D/4 + 8 st .. +7)
+#pragma unroll
+        for (int st = 0; st < QS; ++st)
+          s = mfma16x16x32(*(const bf16x8*)(kl + r16 * ROWB + (((kg * QS + st) ^ k_swz) << 4)), qb[st], s);
       }
       // V^T operands: transposed reads issued now, used after the softmax
-      i32x2 vw[NT / 2];
+      i32x2 vw[EB == 1 ? NT / 2 : 1];
+      uint32_t vb[EB == 2 ? NT : 1][2];
+      if constexpr (EB == 1) {
 #pragma unroll
-      for (int t2 = 0; t2 < NT / 2; ++t2) vw[t2] = lds_read_tr8(vl + tr_base + (((2 * t2 + tr_hi) ^ tr_swz) << 4));
+        for (int t2 = 0; t2 < NT / 2; ++t2) vw[t2] = lds_read_tr8(vl + tr_base + (((2 * t2 + tr_hi) ^ tr_swz) << 4));
+      } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          uint32_t e[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            e[r] = *(const uint16_t*)(vl + v16_row[r] + (((2 * t + (r16 >> 3)) ^ v16_swz[r]) << 4));
+          vb[t][0] = e[0] | (e[1] << 16);
+          vb[t][1] = e[2] | (e[3] << 16);
+        }
+      }
       float4 ks, vs;
       if constexpr (PTH) {
         ks = *(const float4*)(kl + 2 * TB + 16 * kg);
@@ -408,10 +439,21 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
 #pragma unroll
       for (int r = 0; r < 4; ++r) pb[r] = (__bf16)p4[r];
       // ---- O^T[d][head] += V^T[d][keys] P^T[keys][head]
+      if constexpr (EB == 1) {
 #pragma unroll
-      for (int t2 = 0; t2 < NT / 2; ++t2) {
-        acc[2 * t2] = mfma16x16x16(widen4v<DT>((uint32_t)vw[t2].x & vmask), pb, acc[2 * t2]);
-        acc[2 * t2 + 1] = mfma16x16x16(widen4v<DT>((uint32_t)vw[t2].y & vmask), pb, acc[2 * t2 + 1]);
+        for (int t2 = 0; t2 < NT / 2; ++t2) {
+          acc[2 * t2] = mfma16x16x16(widen4v<DT>((uint32_t)vw[t2].x & vmask), pb, acc[2 * t2]);
+          acc[2 * t2 + 1] = mfma16x16x16(widen4v<DT>((uint32_t)vw[t2].y & vmask), pb, acc[2 * t2 + 1]);
+        }
+      } else {
+        // masked keys: their (possibly unwritten) bf16 values are zeroed like the codes above
+        const uint32_t m01 = ((vmask & 0xFFu) ? 0xFFFFu : 0u) | ((vmask & 0xFF00u) ? 0xFFFF0000u : 0u);
+        const uint32_t m23 = ((vmask & 0xFF0000u) ? 0xFFFFu : 0u) | ((vmask & 0xFF000000u) ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const uint2 u = make_uint2(vb[t][0] & m01, vb[t][1] & m23);
+          acc[t] = mfma16x16x16(__builtin_bit_cast(bf16x4, u), pb, acc[t]);
+        }
       }
       ++n_done;
       c_slot = c_slot + SLOT == NS * SLOT ? 0u : c_slot + SLOT;
@@ -523,7 +565,10 @@ static int dec_d(const AttnArgs& a, hipStream_t st) {
   switch (a.head_dim) {
     case 64: return launch_dec<64, DT, MODE>(a, st);
     case 128: return launch_dec<128, DT, MODE>(a, st);
-    case 256: return launch_dec<256, DT, MODE>(a, st);
+    case 256:
+      // the unquantised cache at head_dim 256 needs more LDS than a CU has (the schedule refuses it)
+      if constexpr (DT != AQP_KV_AUTO) return launch_dec<256, DT, MODE>(a, st);
+      break;
   }
   set_error("aqp_paged_attention: unsupported head_dim %d", a.head_dim);
   return AQP_ERR_UNSUPPORTED;
@@ -531,6 +576,7 @@ static int dec_d(const AttnArgs& a, hipStream_t st) {
 
 int launch_decode(int dtype, int mode, const AttnArgs& a, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_AUTO) return dec_d<AQP_KV_AUTO, AQP_SCALE_PER_TENSOR>(a, st);
   if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_FP8_E4M3) return dec_d<AQP_KV_FP8_E4M3, AQP_SCALE_PER_TENSOR>(a, st);
   if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_FP8_E5M2) return dec_d<AQP_KV_FP8_E5M2, AQP_SCALE_PER_TENSOR>(a, st);
   if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_INT8) return dec_d<AQP_KV_INT8, AQP_SCALE_PER_TOKEN_HEAD>(a, st);

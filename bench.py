@@ -249,7 +249,10 @@ def run_all_configs(torch, aqp, W, args):
             ts.append(e0.elapsed_time(e1))
         return float(np.median(ts))
 
-    for w in (W.CFG1, W.CFG2, W.CFG3, W.CFG4, W.CFG5A, W.CFG5B):
+    # the decode batch once more over an unquantised (bf16, "auto") cache: the same kernels with
+    # two-byte elements, for the quantisation's bandwidth saving side by side
+    auto3 = W.scaled(W.CFG3, name="decode64_bf16_auto_llama8b", kv_dtype="auto")
+    for w in (W.CFG1, W.CFG2, W.CFG3, W.CFG4, W.CFG5A, W.CFG5B, auto3):
         log(args, f"[bench] {w.name}")
         b = W.make_batch(w, with_kv=False)
         desc = aqp.cache_desc(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
@@ -259,14 +262,15 @@ def run_all_configs(torch, aqp, W, args):
         k = (torch.randn((n, w.num_kv_heads, w.head_dim), device="cuda", generator=g) * w.sigma).to(torch.bfloat16)
         v = (torch.randn((n, w.num_kv_heads, w.head_dim), device="cuda", generator=g) * w.sigma).to(torch.bfloat16)
         pth = desc.mode == 1
-        qm = {1: 448.0, 2: 57344.0, 3: 127.0}[desc.dtype]
+        qm = {0: 1.0, 1: 448.0, 2: 57344.0, 3: 127.0}[desc.dtype]
+        eb = 2 if desc.dtype == 0 else 1
         ks = float(k.float().abs().max()) / qm
         vs = float(v.float().abs().max()) / qm
         slots = torch.from_numpy(b.slots_hist).cuda()
         cw = lambda: aqp.cache_write(desc, cache, k, v, slots, ks, vs)
         cw()
         cw_ms = timed(cw, 5)
-        cw_bytes = n * w.num_kv_heads * w.head_dim * 2 * 3 + n * 8 + (n * w.num_kv_heads * 8 if pth else 0)
+        cw_bytes = n * w.num_kv_heads * w.head_dim * 2 * (2 + eb) + n * 8 + (n * w.num_kv_heads * 8 if pth else 0)
         del k, v
         q = (torch.randn((int(b.query_start_loc[-1]), w.num_q_heads, w.head_dim), device="cuda", generator=g)
              * w.sigma).to(torch.bfloat16)
@@ -281,7 +285,7 @@ def run_all_configs(torch, aqp, W, args):
         for _ in range(3):
             att()
         att_ms = timed(att, 20)
-        kvb = W.kv_read_bytes(w, per_token_head=pth)
+        kvb = W.kv_read_bytes(w, per_token_head=pth) * eb
         fl = W.prefill_flops(w)
         row = {"workload": w.name, "kv_cache_dtype": w.kv_dtype, "attention_ms": round(att_ms, 4),
                "cache_write": {"tokens": n, "ms": round(cw_ms, 4), "gbs": round(cw_bytes / cw_ms / 1e6, 1),

@@ -23,7 +23,7 @@ def bf16_ulp(x):
     e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
     return 2.0 ** (e - 7)
 
-OFMT = {1: oracle.FMT_E4M3, 2: oracle.FMT_E5M2, 3: oracle.FMT_INT8}
+OFMT = {0: oracle.FMT_BF16, 1: oracle.FMT_E4M3, 2: oracle.FMT_E5M2, 3: oracle.FMT_INT8}
 
 
 def say(*a):

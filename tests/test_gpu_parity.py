@@ -55,6 +55,11 @@ SMALL = [
     W.Workload("int8_pt_prefill_d256", "int8", ((70, 70), (9, 130)), 16, 2, 256, 32, 12, seed=87),
     W.Workload("e5m2_pth_prefill_d64", "fp8_e5m2_per_token_head", ((45, 45), (3, 99), (1, 20)), 8, 2, 64, 16, 16,
                seed=88),
+    # the unquantised ("auto", bf16) cache: decode batches, with splits, window and soft-cap
+    W.scaled(W.CFG3, name="auto_decode_llama8b", kv_dtype="auto", seqs=((1, 700), (1, 33), (1, 1500), (1, 16)),
+             num_blocks=200),
+    W.Workload("auto_decode_d64_w_cap", "auto", ((1, 900), (1, 77), (1, 2000)), 16, 2, 64, 16, 200, window=300,
+               softcap=15.0, seed=89),
 ]
 
 
@@ -215,7 +220,7 @@ def test_block_permutation_bit_identical(aqp):
 
 
 @pytest.mark.parametrize("dtype_str", ["fp8_e4m3", "fp8_e5m2", "int8_per_token_head", "fp8_per_token_head", "int8",
-                                       "fp8_e5m2_per_token_head"])
+                                       "fp8_e5m2_per_token_head", "auto"])
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_cache_write_bit_exact(aqp, dtype_str, D):
     """Random slots (some negative), a fused-QKV token stride, specials (zero rows, huge and tiny

@@ -46,12 +46,8 @@ def _golden_dtypes():
 
 @pytest.mark.parametrize("s,idx,mode", _golden_dtypes())
 def test_parse_kv_dtype_matches_pages(s, idx, mode):
-    if s == "auto":
-        with pytest.raises(aqp.AqpError) as e:
-            aqp.parse_kv_dtype(s)
-        assert e.value.status == aqp.ERR_UNSUPPORTED
-    else:
-        assert aqp.parse_kv_dtype(s) == (idx, mode)
+    # "auto" is the unquantised (bf16) cache
+    assert aqp.parse_kv_dtype(s) == (idx, mode)
 
 
 @pytest.mark.parametrize("s,idx,mode", [("int8", 3, 0), ("fp8_e5m2_per_token_head", 2, 1)])
@@ -67,11 +63,12 @@ def test_parse_rejects_unknown():
     assert aqp.parse_kv_dtype("fp8") == (aqp.KV_FP8_E4M3, aqp.SCALE_PER_TENSOR)
 
 
-FMT = {aqp.KV_FP8_E4M3: oracle.FMT_E4M3, aqp.KV_FP8_E5M2: oracle.FMT_E5M2, aqp.KV_INT8: oracle.FMT_INT8}
+FMT = {aqp.KV_AUTO: oracle.FMT_BF16, aqp.KV_FP8_E4M3: oracle.FMT_E4M3, aqp.KV_FP8_E5M2: oracle.FMT_E5M2,
+       aqp.KV_INT8: oracle.FMT_INT8}
 
 
 @pytest.mark.parametrize("dtype_str", ["fp8_e4m3", "fp8_e5m2", "int8_per_token_head", "fp8_per_token_head", "int8",
-                                       "fp8_e5m2_per_token_head"])
+                                       "fp8_e5m2_per_token_head", "auto"])
 @pytest.mark.parametrize("nb,bs,h,d", [(8, 16, 2, 64), (4, 2176, 2, 256), (40000, 16, 8, 128), (3, 32, 3, 128)])
 def test_cache_bytes_match_oracle_layout(dtype_str, nb, bs, h, d):
     desc = aqp.cache_desc(nb, bs, h, d, dtype_str)
@@ -90,7 +87,7 @@ def test_unsupported_geometry(bad):
     assert e.value.status in (aqp.ERR_UNSUPPORTED, aqp.ERR_INVALID)
 
 
-@pytest.mark.parametrize("dt,md", [(aqp.KV_AUTO, 0), (aqp.KV_AUTO, 1)])
+@pytest.mark.parametrize("dt,md", [(aqp.KV_AUTO, 1)])
 def test_unbuilt_dtype_mode_pairs_are_errors(dt, md):
     with pytest.raises(aqp.AqpError) as e:
         aqp.cache_bytes(aqp.CacheDesc(4, 16, 2, 64, dt, md))
@@ -117,3 +114,24 @@ def test_cache_write_argument_errors():
     assert e.value.status == aqp.ERR_INVALID
     # zero tokens: nothing to do, no device touched
     aqp._check(aqp._lib.aqp_cache_write(ctypes.byref(desc), None, None, None, 0, 128, None, 1.0, 1.0, None))
+
+
+def test_unquantised_cache_geometry_and_limits():
+    """The "auto" cache stores two bytes per element: the schedule records that size and sizes
+    the decode LDS from it; prefill over it, and decode at head_dim 256 (more LDS than a CU
+    has), are refused rather than run."""
+    desc = aqp.cache_desc(8, 16, 2, 128, "auto")
+    pb, bb, tb = aqp.cache_bytes(desc)
+    assert pb == 16 * 128 * 2 and bb == 2 * 2 * pb
+    params = aqp.attn_params(8, 2, 128, 4)
+    sl, qsl = np.array([40, 17], np.int32), np.array([0, 1, 2], np.int32)
+    h = aqp.get_schedule(params, desc, sl, qsl).header
+    assert h["kv_elem_bytes"] == 2 and h["staged_elem_bytes"] == 2
+    assert h["dec_lds_bytes"] == 4 * (2 * (2 * 16 * 128 * 2) + 4 * 128 * 2) + 4 * 4 * (128 + 4) * 4
+    with pytest.raises(aqp.AqpError) as e:
+        aqp.get_schedule(params, desc, np.array([40, 17], np.int32), np.array([0, 5, 6], np.int32))
+    assert e.value.status == aqp.ERR_UNSUPPORTED
+    d256 = aqp.cache_desc(8, 16, 2, 256, "auto")
+    with pytest.raises(aqp.AqpError) as e:
+        aqp.get_schedule(aqp.attn_params(8, 2, 256, 4), d256, sl, qsl)
+    assert e.value.status == aqp.ERR_UNSUPPORTED
