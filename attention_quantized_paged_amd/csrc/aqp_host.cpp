@@ -337,10 +337,6 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
 
   if (desc->dtype == AQP_KV_AUTO && desc->head_dim > 128 && total_q > 0)
     return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: an unquantised cache at head_dim %d is not built", desc->head_dim);
-  if (desc->dtype == AQP_KV_AUTO)
-    for (int32_t b = 0; b < num_seqs; ++b)
-      if (qsl[b + 1] - qsl[b] > 1)
-        return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: prefill over an unquantised cache is not built (sequence %d has %d queries)", b, qsl[b + 1] - qsl[b]);
 
   // ---- prefill items: (sequence, KV head, run of query tokens, run of its q heads): all G
   // heads of the KV head when G <= kPfRows, else one token and kPfRows heads at a time;

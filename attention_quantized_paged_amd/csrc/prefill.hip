@@ -43,14 +43,14 @@ struct PfArgs {
 };
 
 // 16-byte chunk swizzle of a staged row: chunk c of row `row` is stored at chunk
-// c ^ swz(row). Rows are D bytes; 256 bytes span all LDS banks, so rows that share banks
-// (same row / (256 / D) residue) get different chunk offsets, and the second 16-key tile gets
+// c ^ swz(row). Rows are ROWB bytes; 256 bytes span all LDS banks, so rows that share banks
+// (same row / (256 / ROWB) residue) get different chunk offsets, and the second 16-key tile gets
 // the upper half of the offsets. This keeps the K-operand reads (16 rows, one chunk) and the
 // transposed V reads (8 rows of two tiles, one chunk) free of bank conflicts.
-template <int D>
+template <int ROWB>
 __device__ __forceinline__ int swz(int row) {
-  constexpr int CPR = D / 16;                  // chunks per row
-  constexpr int RPL = D >= 256 ? 1 : 256 / D;  // rows per 256 bytes
+  constexpr int CPR = ROWB / 16;                        // chunks per row
+  constexpr int RPL = ROWB >= 256 ? 1 : 256 / ROWB;     // rows per 256 bytes
   return ((row / RPL) % CPR) ^ (((row >> 4) & 1) * (CPR / 2));
 }
 
@@ -63,8 +63,10 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   constexpr int RPW = 16 * RT;                    // query rows per wave
   constexpr int KT = kPfKvTile;                   // keys per step (two 16-key tiles)
   constexpr int NS = kPfStages;                   // LDS ring stages
-  constexpr int CPR = D / 16;                     // 16-byte chunks per row
-  constexpr int STAGE = 2 * KT * D + 2 * KT * 4;  // K codes, V codes, K scales, V scales
+  constexpr int EB = DT == AQP_KV_AUTO ? 2 : 1;   // bytes per stored element (bf16 when unquantised)
+  constexpr int ROWB = D * EB;                    // bytes of one staged key row
+  constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
+  constexpr int STAGE = 2 * KT * ROWB + 2 * KT * 4;  // K rows, V rows, K scales, V scales
   constexpr int KV_INSTR = KT * CPR / 64;         // 1 KB copies per K (or V) step
   constexpr int IPW = 2 * KV_INSTR / WAVES;       // K+V copies per wave per step
   static_assert(IPW >= 1 && (2 * KV_INSTR) % WAVES == 0, "copies must split evenly over the waves");
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       const int q0 = 64 * (ii % KV_INSTR);
       const int q = q0 + lane;
       const int row = q / CPR;
-      const int lc = (q % CPR) ^ swz<D>(row);
+      const int lc = (q % CPR) ^ swz<ROWB>(row);
       // tile of this copy (uniform), clamped to the tile of key L-1
       const int tile_k0 = min(kb0 + ((q0 / CPR) & ~15), last_tile);
       const int tbi = tile_k0 / a.block_size;
@@ -179,8 +181,8 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       if ((uint32_t)blk >= (uint32_t)a.num_blocks) blk = 0;  // invalid table entry: stay in the pool
       const int key = min(kb0 + row, it.L - 1);
       const uint8_t* src = (kv ? vbase : kbase) + (int64_t)blk * a.block_bytes +
-                           (int64_t)(tr0 + (key - tile_k0)) * D + lc * 16;
-      dma16_to_lds(src, sbase + (uint32_t)(kv * KT * D + q0 * 16));
+                           (int64_t)(tr0 + (key - tile_k0)) * ROWB + lc * 16;
+      dma16_to_lds(src, sbase + (uint32_t)(kv * KT * ROWB + q0 * 16));
     }
     if constexpr (PTH) {
       if (wave == WAVES - 1) {
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
         const int r0 = tk0 - (tl ? bi1 : bi0) * a.block_size;
         const uint8_t* src = (kv ? vbase : kbase) + (int64_t)blk * a.block_bytes + (int64_t)a.block_size * D +
                              4 * (r0 + 4 * part);
-        if (lane < 16) dma16_to_lds(src, sbase + (uint32_t)(2 * KT * D));
+        if (lane < 16) dma16_to_lds(src, sbase + (uint32_t)(2 * KT * ROWB));
       }
     }
   };
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   // transposed V read: row i of lane group kg is key (i < 4 ? 4kg + i : 16 + 4kg + i - 4)
   const int tr_i = r16 >> 1;
   const int tr_row = (tr_i < 4) ? (4 * kg + tr_i) : (16 + 4 * kg + tr_i - 4);
-  const int tr_swz = swz<D>(tr_row);
+  const int tr_swz = swz<ROWB>(tr_row);
 
   // ---- widen the K codes of one step into its K image: block kt * QS + st holds, for lane l,
   // the 8 depth values kg * D/4 + 8 st .. +7 of key kt * 16 + l % 16 (the A operand of S^T = K Q^T)
@@ -216,9 +218,14 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       const int blk = wave * KB_PW + j;
       const int kt = blk / QS, st = blk - (blk / QS) * QS;
       const int krow = kt * 16 + r16;
-      const int dbyte = kg * (D / 4) + st * 8;
-      const uint2 c = *(const uint2*)(kl + krow * D + ((((dbyte >> 4) ^ swz<D>(krow)) << 4) | (dbyte & 8)));
-      *(bf16x8*)(img + blk * 1024) = widen8<DT>(c.x, c.y);
+      const int dbyte = (kg * (D / 4) + st * 8) * EB;
+      if constexpr (EB == 1) {
+        const uint2 c = *(const uint2*)(kl + krow * ROWB + ((((dbyte >> 4) ^ swz<ROWB>(krow)) << 4) | (dbyte & 8)));
+        *(bf16x8*)(img + blk * 1024) = widen8<DT>(c.x, c.y);
+      } else {
+        // bf16 rows: the 16 bytes are the operand already
+        *(uint4*)(img + blk * 1024) = *(const uint4*)(kl + krow * ROWB + (((dbyte >> 4) ^ swz<ROWB>(krow)) << 4));
+      }
     }
   };
   // ---- widen the V codes of one step into its V image: block t holds, for lane l, dim
@@ -227,15 +234,32 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   auto convert_v = [&](int step) {
     const uint8_t* kl = smem + (step % NS) * STAGE;
     uint8_t* slot = smem + VIMG + (step & 1) * VSLOT;
-    const uint8_t* rp = kl + KT * D + tr_row * D + (r16 & 1) * 8;
+    if constexpr (EB == 1) {
+      const uint8_t* rp = kl + KT * ROWB + tr_row * ROWB + (r16 & 1) * 8;
 #pragma unroll
-    for (int j = 0; j < VB_PW; ++j) {
-      const int t = wave * VB_PW + j;
-      const i32x2 c = lds_read_tr8(rp + ((t ^ tr_swz) << 4));
-      *(bf16x8*)(slot + t * 1024 + lane * 16) = widen8<DT>((uint32_t)c.x, (uint32_t)c.y);
+      for (int j = 0; j < VB_PW; ++j) {
+        const int t = wave * VB_PW + j;
+        const i32x2 c = lds_read_tr8(rp + ((t ^ tr_swz) << 4));
+        *(bf16x8*)(slot + t * 1024 + lane * 16) = widen8<DT>((uint32_t)c.x, (uint32_t)c.y);
+      }
+    } else {
+      // bf16 rows: the lane's 8 keys of head-dim column t * 16 + r16, one 16-bit read each
+      const uint8_t* vl = kl + KT * ROWB + (r16 & 7) * 2;
+#pragma unroll
+      for (int j = 0; j < VB_PW; ++j) {
+        const int t = wave * VB_PW + j;
+        uint32_t e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = i < 4 ? 4 * kg + i : 16 + 4 * kg + i - 4;
+          e[i] = *(const uint16_t*)(vl + row * ROWB + (((2 * t + (r16 >> 3)) ^ swz<ROWB>(row)) << 4));
+        }
+        *(uint4*)(slot + t * 1024 + lane * 16) =
+            make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+      }
     }
     if constexpr (PTH) {
-      if (wave == WAVES - 1 && lane < 16) *(uint4*)(slot + IMG + lane * 16) = *(const uint4*)(kl + 2 * KT * D + lane * 16);
+      if (wave == WAVES - 1 && lane < 16) *(uint4*)(slot + IMG + lane * 16) = *(const uint4*)(kl + 2 * KT * ROWB + lane * 16);
     }
   };
 
@@ -486,7 +510,10 @@ static int pf_d(const AttnArgs& a, hipStream_t st) {
   switch (a.head_dim) {
     case 64: return launch_pf<64, DT, MODE>(a, st);
     case 128: return launch_pf<128, DT, MODE>(a, st);
-    case 256: return launch_pf<256, DT, MODE>(a, st);
+    case 256:
+      // the unquantised cache at head_dim 256 needs more LDS than a CU has (the schedule refuses it)
+      if constexpr (DT != AQP_KV_AUTO) return launch_pf<256, DT, MODE>(a, st);
+      break;
   }
   set_error("aqp_paged_attention: unsupported head_dim %d", a.head_dim);
   return AQP_ERR_UNSUPPORTED;
@@ -494,6 +521,7 @@ static int pf_d(const AttnArgs& a, hipStream_t st) {
 
 int launch_prefill(int dtype, int mode, const AttnArgs& a, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_AUTO) return pf_d<AQP_KV_AUTO, AQP_SCALE_PER_TENSOR>(a, st);
   if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_FP8_E4M3) return pf_d<AQP_KV_FP8_E4M3, AQP_SCALE_PER_TENSOR>(a, st);
   if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_FP8_E5M2) return pf_d<AQP_KV_FP8_E5M2, AQP_SCALE_PER_TENSOR>(a, st);
   if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_INT8) return pf_d<AQP_KV_INT8, AQP_SCALE_PER_TOKEN_HEAD>(a, st);

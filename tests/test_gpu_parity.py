@@ -60,6 +60,9 @@ SMALL = [
              num_blocks=200),
     W.Workload("auto_decode_d64_w_cap", "auto", ((1, 900), (1, 77), (1, 2000)), 16, 2, 64, 16, 200, window=300,
                softcap=15.0, seed=89),
+    W.Workload("auto_mixed_d128", "auto", ((1, 600), (70, 310), (33, 33), (1, 17)), 32, 8, 128, 16, 80, seed=90),
+    W.Workload("auto_prefill_d64_w_cap", "auto", ((40, 40), (9, 130)), 8, 2, 64, 32, 12, window=50, softcap=10.0,
+               seed=96),
 ]
 
 

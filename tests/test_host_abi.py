@@ -118,8 +118,8 @@ def test_cache_write_argument_errors():
 
 def test_unquantised_cache_geometry_and_limits():
     """The "auto" cache stores two bytes per element: the schedule records that size and sizes
-    the decode LDS from it; prefill over it, and decode at head_dim 256 (more LDS than a CU
-    has), are refused rather than run."""
+    the decode and prefill LDS from it; head_dim 256 (more LDS than a CU has) is refused rather
+    than run."""
     desc = aqp.cache_desc(8, 16, 2, 128, "auto")
     pb, bb, tb = aqp.cache_bytes(desc)
     assert pb == 16 * 128 * 2 and bb == 2 * 2 * pb
@@ -128,9 +128,10 @@ def test_unquantised_cache_geometry_and_limits():
     h = aqp.get_schedule(params, desc, sl, qsl).header
     assert h["kv_elem_bytes"] == 2 and h["staged_elem_bytes"] == 2
     assert h["dec_lds_bytes"] == 4 * (2 * (2 * 16 * 128 * 2) + 4 * 128 * 2) + 4 * 4 * (128 + 4) * 4
-    with pytest.raises(aqp.AqpError) as e:
-        aqp.get_schedule(params, desc, np.array([40, 17], np.int32), np.array([0, 5, 6], np.int32))
-    assert e.value.status == aqp.ERR_UNSUPPORTED
+    h2 = aqp.get_schedule(params, desc, np.array([40, 17], np.int32), np.array([0, 5, 6], np.int32)).header
+    assert h2["num_pf_items"] > 0
+    assert h2["pf_lds_bytes"] == 4 * (2 * 32 * 128 * 2 + 2 * 32 * 4) + 4 * 32 * 128 * 2 + 2 * 2 * 32 * 4
+    assert h2["pf_lds_bytes"] <= 160 * 1024
     d256 = aqp.cache_desc(8, 16, 2, 256, "auto")
     with pytest.raises(aqp.AqpError) as e:
         aqp.get_schedule(aqp.attn_params(8, 2, 256, 4), d256, sl, qsl)
