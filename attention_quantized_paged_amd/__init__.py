@@ -40,7 +40,7 @@ class AttnParams(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("window", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("sm_scale", ctypes.c_float), ("softcap", ctypes.c_float), ("decode_parallelism", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("causal_per_seq", ctypes.c_void_p), ("alibi_slopes", ctypes.c_void_p),
+                ("prefill_rows", ctypes.c_int32), ("causal_per_seq", ctypes.c_void_p), ("alibi_slopes", ctypes.c_void_p),
                 ("sinks", ctypes.c_void_p)]
 
 
@@ -114,12 +114,13 @@ def cache_desc(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: in
 
 def attn_params(num_q_heads: int, num_kv_heads: int, head_dim: int, max_blocks_per_seq: int, causal: bool = True,
                 window: int = 0, sm_scale: float = 0.0, softcap: float = 0.0,
-                decode_parallelism: int = 0, causal_per_seq=None, alibi_slopes=None, sinks=None) -> AttnParams:
+                decode_parallelism: int = 0, causal_per_seq=None, alibi_slopes=None, sinks=None,
+                prefill_rows: int = 0) -> AttnParams:
     """causal_per_seq: host int sequence (one flag per sequence) or None; alibi_slopes, sinks:
     device float32 tensors of num_q_heads values (anything with ``data_ptr()``) or None. The
     returned object keeps them alive."""
     p = AttnParams(num_q_heads, num_kv_heads, head_dim, int(causal), window, max_blocks_per_seq, sm_scale,
-                   softcap, decode_parallelism, 0, None, None, None)
+                   softcap, decode_parallelism, prefill_rows, None, None, None)
     keep = []
     if causal_per_seq is not None:
         cps = np.ascontiguousarray(np.asarray(causal_per_seq), dtype=np.int32)

@@ -202,6 +202,7 @@ static int check_params(const aqp_attn_params& p, const aqp_cache_desc& d, const
   if (!(p.sm_scale >= 0.0f) || !std::isfinite(p.sm_scale)) { *why = "sm_scale must be finite and >= 0"; return AQP_ERR_INVALID; }
   if (!(p.softcap >= 0.0f) || !std::isfinite(p.softcap)) { *why = "softcap must be finite and >= 0"; return AQP_ERR_INVALID; }
   if (p.decode_parallelism < 0) { *why = "negative decode_parallelism"; return AQP_ERR_INVALID; }
+  if (p.prefill_rows != 0 && p.prefill_rows != kPfRows && p.prefill_rows != kPfRowsSmall) { *why = "prefill_rows must be 0, 64 or 128"; return AQP_ERR_INVALID; }
   return AQP_OK;
 }
 
@@ -339,10 +340,29 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
     return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: an unquantised cache at head_dim %d is not built", desc->head_dim);
 
   // ---- prefill items: (sequence, KV head, run of query tokens, run of its q heads): all G
-  // heads of the KV head when G <= kPfRows, else one token and kPfRows heads at a time;
-  // heaviest (most keys) first.
-  const int32_t hpi = std::min<int32_t>(G, kPfRows);
-  const int32_t tpi = std::max<int32_t>(1, kPfRows / G);
+  // heads of the KV head when G <= rows, else one token and `rows` heads at a time;
+  // heaviest (most keys) first. rows = kPfRows, or kPfRowsSmall at head_dim <= 128 when
+  // kPfRows-row items would give the CUs fewer than two work-groups each and the batch has no
+  // decode work (decode runs beside the prefill and needs the room the second work-group takes).
+  auto count_items = [&](int32_t rows) {
+    const int32_t hp = std::min<int32_t>(G, rows), tp = std::max<int32_t>(1, rows / G);
+    int64_t n = 0;
+    for (int32_t b = 0; b < num_seqs; ++b) {
+      const int32_t ql = qsl[b + 1] - qsl[b];
+      if (ql > 1) n += (int64_t)((ql + tp - 1) / tp) * p.num_kv_heads * ((G + hp - 1) / hp);
+    }
+    return n;
+  };
+  int32_t pf_rows = kPfRows;
+  if (p.prefill_rows > 0) {
+    pf_rows = p.prefill_rows;
+  } else if (desc->head_dim <= 128 && total_tiles == 0 && total_q > 0 && count_items(kPfRows) < 2 * (int64_t)device_cu_count()) {
+    pf_rows = kPfRowsSmall;
+  }
+  if (pf_rows < pf_waves(desc->head_dim) * 16)
+    return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: %d rows per prefill item at head_dim %d is not built", pf_rows, desc->head_dim);
+  const int32_t hpi = std::min<int32_t>(G, pf_rows);
+  const int32_t tpi = std::max<int32_t>(1, pf_rows / G);
   for (int32_t b = 0; b < num_seqs; ++b) {
     const int32_t L = seq_lens[b], ql = qsl[b + 1] - qsl[b];
     if (ql <= 1) continue;
@@ -419,7 +439,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   h.tile_keys = kTileKeys;
   h.dec_iter_keys = kDecIterKeys;
   h.dec_waves = kDecWaves;
-  h.pf_rows = kPfRows;
+  h.pf_rows = pf_rows;
   h.pf_kv_tile = kPfKvTile;
   h.heads_per_unit = max_hpu;
   h.dec_lds_bytes = dec_lds;
@@ -479,7 +499,8 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
   MISMATCH_IF(h.num_q_heads != params->num_q_heads || h.num_kv_heads != params->num_kv_heads, "head count");
   MISMATCH_IF(h.causal != params->causal || h.window != params->window || h.max_blocks_per_seq != params->max_blocks_per_seq, "mask / block-table shape");
   MISMATCH_IF(h.sm_scale != effective_sm_scale(*params) || h.softcap != params->softcap, "logit scale / soft-cap");
-  MISMATCH_IF(h.tile_keys != kTileKeys || h.dec_iter_keys != kDecIterKeys || h.dec_waves != kDecWaves || h.pf_rows != kPfRows ||
+  MISMATCH_IF(h.tile_keys != kTileKeys || h.dec_iter_keys != kDecIterKeys || h.dec_waves != kDecWaves || (h.pf_rows != kPfRows && h.pf_rows != kPfRowsSmall) ||
+              (params->prefill_rows != 0 && h.pf_rows != params->prefill_rows) ||
               h.pf_kv_tile != kPfKvTile || h.heads_per_unit != heads_per_unit(desc->head_dim) ||
               h.dec_lds_bytes != dec_lds_bytes(desc->head_dim, desc->mode, std::min<int32_t>(params->num_q_heads / params->num_kv_heads, heads_per_unit(desc->head_dim)), g.kv_elem_bytes) ||
               h.pf_lds_bytes != g.pf_lds_bytes, "tile geometry");

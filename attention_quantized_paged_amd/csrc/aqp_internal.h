@@ -29,6 +29,9 @@ constexpr int kDecWaves = 4;         // compute waves per decode work-group (the
 // (Q rows and the merge area grow with the heads) stays within one CU's
 constexpr int heads_per_unit(int head_dim) { return head_dim >= 256 ? 8 : 16; }
 constexpr int kPfRows = 128;         // prefill: query rows (token, q head) per work item
+// prefill: rows per item when 128-row items would leave CUs with fewer than two work-groups
+// (head_dim <= 128): twice the items, so a CU overlaps one work-group's waits with another's work
+constexpr int kPfRowsSmall = 64;
 // Prefill waves per work-group: head_dim 256 gives each of 8 waves 16 rows (so a wave's
 // 16 x 256 fp32 output tile and its Q rows stay in ordinary registers at two waves per SIMD);
 // smaller head dims give each of 4 waves 32 rows, which halves the LDS operand reads per MFMA.

@@ -54,12 +54,13 @@ __device__ __forceinline__ int swz(int row) {
   return ((row / RPL) % CPR) ^ (((row >> 4) & 1) * (CPR / 2));
 }
 
-template <int D, int DT, int MODE, bool CAP>
+template <int D, int DT, int MODE, bool CAP, int ROWS>
 __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 2))) void prefill_kernel(PfArgs a) {
   constexpr int NT = D / 16;
   constexpr int QS = D / 32;
   constexpr int WAVES = pf_waves(D);
-  constexpr int RT = kPfRows / (16 * WAVES);      // 16-row MFMA column blocks per wave
+  constexpr int RT = ROWS / (16 * WAVES);         // 16-row MFMA column blocks per wave
+  static_assert(RT >= 1 && ROWS % (16 * WAVES) == 0, "rows must split evenly over the waves");
   constexpr int RPW = 16 * RT;                    // query rows per wave
   constexpr int KT = kPfKvTile;                   // keys per step (two 16-key tiles)
   constexpr int NS = kPfStages;                   // LDS ring stages
@@ -493,10 +494,25 @@ static int launch_pf(const AttnArgs& a, hipStream_t st) {
   p.v_scale = MODE == AQP_SCALE_PER_TENSOR ? a.v_scale : 1.0f;
   p.alibi = a.alibi_slopes;
   p.sinks = a.sinks;
-  if (a.softcap > 0.0f)
-    hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, true>), dim3(h.num_pf_items), dim3(pf_waves(D) * 64), h.pf_lds_bytes, st, p);
-  else
-    hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, false>), dim3(h.num_pf_items), dim3(pf_waves(D) * 64), h.pf_lds_bytes, st, p);
+  const dim3 grid(h.num_pf_items), block(pf_waves(D) * 64);
+  if (h.pf_rows == kPfRows) {
+    if (a.softcap > 0.0f)
+      hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, true, kPfRows>), grid, block, h.pf_lds_bytes, st, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, false, kPfRows>), grid, block, h.pf_lds_bytes, st, p);
+  } else if constexpr (pf_waves(D) * 16 <= kPfRowsSmall) {
+    if (h.pf_rows != kPfRowsSmall) {
+      set_error("aqp_paged_attention: schedule rows per prefill item %d not built", h.pf_rows);
+      return AQP_ERR_SCHEDULE_MISMATCH;
+    }
+    if (a.softcap > 0.0f)
+      hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, true, kPfRowsSmall>), grid, block, h.pf_lds_bytes, st, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, false, kPfRowsSmall>), grid, block, h.pf_lds_bytes, st, p);
+  } else {
+    set_error("aqp_paged_attention: schedule rows per prefill item %d not built at head_dim %d", h.pf_rows, D);
+    return AQP_ERR_SCHEDULE_MISMATCH;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("aqp_paged_attention: prefill launch failed: %s", hipGetErrorString(e));

@@ -35,7 +35,7 @@ extern "C" {
  * [P50194] Code excerpt (0 = auto, 1 = fp8_e4m3, 2 = fp8_e5m2); 3 adds int8
  * for the per-token-head mode of [P38378]. */
 typedef enum {
-  AQP_KV_AUTO = 0,     /* unquantised cache: not supported by this build (AQP_ERR_UNSUPPORTED) */
+  AQP_KV_AUTO = 0,     /* unquantised cache: the bf16 inputs stored as given, per-tensor mode, no scales */
   AQP_KV_FP8_E4M3 = 1, /* OCP E4M3, finite-only ("fn"), largest code 448 */
   AQP_KV_FP8_E5M2 = 2, /* OCP E5M2, largest finite code 57344 */
   AQP_KV_INT8 = 3      /* two's-complement int8, codes in [-128, 127] */
@@ -64,14 +64,16 @@ typedef enum {
  *  - num_blocks blocks, block b at byte b * block_bytes;
  *  - block_bytes = 2 * num_kv_heads * page_bytes: the K pages of heads
  *    0..Hkv-1, then the V pages;
- *  - a page holds block_size rows of head_dim code bytes, token-major (row
+ *  - a page holds block_size rows of head_dim codes (one byte each; two, the
+ *    bf16 bits, for AUTO), token-major (row
  *    = one token of one head), followed in per-token-head mode by block_size
  *    fp32 scales (the scale of row r at page + block_size*head_dim + 4*r:
  *    the inline scale storage of [P38378] Implementation item 2, kept at the
  *    page tail so rows stay 16-byte aligned);
  *  - page_bytes is that content rounded up to a multiple of 128 bytes;
  *  - slot s is row (s % block_size) of block (s / block_size).
- * Supported: head_dim in {64, 128, 256}; block_size a positive multiple of 16. */
+ * Supported: head_dim in {64, 128, 256} (AUTO: 64 and 128 in attention);
+ * block_size a positive multiple of 16. */
 typedef struct {
   int32_t num_blocks;
   int32_t block_size;
@@ -96,7 +98,10 @@ typedef struct {
   float softcap;              /* 0: none; c > 0: logit z -> c * tanh(z / c), applied after sm_scale */
   int32_t decode_parallelism; /* work-groups the decode work is split across; 0 = one resident wave of
                                  work-groups on the current device (CUs x 3 for head_dim <= 128, x 2 above) */
-  int32_t reserved;           /* 0 */
+  int32_t prefill_rows;       /* query rows (token, q head) per prefill work-group: 64 or 128 (64 needs
+                                 head_dim <= 128); 0 = 128, or 64 at head_dim <= 128 for a batch with no
+                                 decode sequence whose 128-row items would number fewer than two per
+                                 CU of the current device */
   /* The harness parameters the page names without defining them; the readings taken: */
   const int32_t* causal_per_seq; /* host int32 [num_seqs] of 0/1, or NULL (= `causal` for every
                                     sequence). Read by aqp_get_schedule only: the schedule carries
@@ -121,9 +126,8 @@ typedef struct {
  * library's own:
  *   "int8"                  -> INT8,     PER_TENSOR
  *   "fp8_e5m2_per_token_head" -> FP8_E5M2, PER_TOKEN_HEAD
- *   "auto"                  -> AUTO, PER_TENSOR, returns AQP_ERR_UNSUPPORTED
- * Anything else: AQP_ERR_INVALID. Outputs are written only on AQP_OK (and for
- * "auto"). */
+ *   "auto"                  -> AUTO,     PER_TENSOR (the unquantised cache)
+ * Anything else: AQP_ERR_INVALID. Outputs are written only on AQP_OK. */
 int aqp_parse_kv_dtype(const char* s, int32_t* dtype, int32_t* mode);
 
 /* Byte sizes of the cache layout described at aqp_cache_desc. Any output
@@ -146,9 +150,9 @@ int aqp_cache_bytes(const aqp_cache_desc* desc, size_t* page_bytes, size_t* bloc
  *   inv  = (s == 0) ? 0 : 1 / s  (correctly rounded);
  *   code = fp8: round-to-nearest-even of x_d * inv, saturated to the largest finite code;
  *          int8: round-to-nearest-even, clamped to [-128, 127].
+ * AUTO copies the bf16 values unchanged (no scale).
  * Errors: INVALID (null pointers, negative sizes, stride too small), UNSUPPORTED
- * (dtype/mode combination not built: per token-head needs INT8 or E4M3;
- * per tensor needs E4M3 or E5M2), HIP. */
+ * (AUTO with per-token-head mode), HIP. */
 int aqp_cache_write(const aqp_cache_desc* desc, void* cache, const void* k, const void* v, int64_t num_tokens,
                     int64_t token_stride, const int64_t* slot_mapping, float k_scale, float v_scale, void* stream);
 

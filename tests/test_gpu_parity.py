@@ -130,6 +130,22 @@ def test_unwritten_cache_bytes_do_not_leak(aqp, w):
     compare(out[rows], ref, w.name)
 
 
+ROWS_CASES = [w for w in SMALL if w.name in ("prefill_cap5_w37_d128", "g160_mixed_e5m2", "auto_prefill_d64_w_cap",
+                                             "e5m2_pth_mixed_w_cap", "d64_int8_mixed", "noncausal_prefill")]
+
+
+@pytest.mark.parametrize("rows", [64, 128])
+@pytest.mark.parametrize("w", ROWS_CASES, ids=[w.name for w in ROWS_CASES])
+def test_prefill_rows_per_item(aqp, w, rows):
+    """Both prefill item sizes (64 and 128 query rows per work-group) match the oracle, whichever
+    the schedule would pick by itself; G = 160 splits a token's heads into 64-head items."""
+    r = Run(w, torch, aqp, prefill_rows=rows)
+    out = r.gpu_attention()
+    assert r.sched.header["pf_rows"] == rows
+    ref, rows_idx = r.oracle_attention()
+    compare(out[rows_idx], ref, f"{w.name} rows={rows}")
+
+
 @pytest.mark.parametrize("par", [1, 3, 64, 4096])
 def test_decode_split_counts(aqp, par):
     """The same decode batch cut into 1 .. many work-groups gives the same result."""

@@ -29,12 +29,12 @@ def _arrays(s):
     return segs, wgs, comb, pf
 
 
-def _sched(seqs, hq, hkv, d, bs, dtype="fp8_e4m3", window=0, causal=True, par=0, nb=None):
+def _sched(seqs, hq, hkv, d, bs, dtype="fp8_e4m3", window=0, causal=True, par=0, nb=None, rows=0):
     sl = np.array([L for _, L in seqs], np.int32)
     qsl = np.concatenate([[0], np.cumsum([q for q, _ in seqs])]).astype(np.int32)
     mb = int(max(1, max((L + bs - 1) // bs for L in sl)))
     desc = aqp.cache_desc(nb or 4 * mb * len(seqs), bs, hkv, d, dtype)
-    params = aqp.attn_params(hq, hkv, d, mb, causal=causal, window=window, decode_parallelism=par)
+    params = aqp.attn_params(hq, hkv, d, mb, causal=causal, window=window, decode_parallelism=par, prefill_rows=rows)
     return aqp.get_schedule(params, desc, sl, qsl), sl, qsl, params, desc
 
 
@@ -99,9 +99,17 @@ def test_decode_coverage_exact(seqs, hq, hkv, d, bs, window, par):
         assert len(set(tiles[:-1])) <= 1 and tiles[-1] <= tiles[0]
 
 
+@pytest.mark.parametrize("rows", [0, 64, 128])
 @pytest.mark.parametrize("seqs,hq,hkv,d,bs,window,par", CASES)
-def test_prefill_coverage_and_order(seqs, hq, hkv, d, bs, window, par):
-    s, sl, qsl, params, desc = _sched(seqs, hq, hkv, d, bs, window=window, par=par)
+def test_prefill_coverage_and_order(seqs, hq, hkv, d, bs, window, par, rows):
+    if rows == 64 and d > 128:
+        with pytest.raises(aqp.AqpError) as e:
+            _sched(seqs, hq, hkv, d, bs, window=window, par=par, rows=rows)
+        assert e.value.status == aqp.ERR_UNSUPPORTED
+        return
+    s, sl, qsl, params, desc = _sched(seqs, hq, hkv, d, bs, window=window, par=par, rows=rows)
+    if rows:
+        assert h_rows(s) == rows
     _, _, _, pf = _arrays(s)
     G = hq // hkv
     seen = {}
@@ -223,3 +231,27 @@ def test_per_sequence_causal_flags_and_seq_lens_are_recorded():
     with pytest.raises(aqp.AqpError) as e:
         aqp.get_schedule(aqp.attn_params(8, 2, 64, 8, window=5, causal_per_seq=flags), desc, sl, qsl)
     assert e.value.status == aqp.ERR_UNSUPPORTED
+
+
+def test_prefill_rows_choice():
+    """128 query rows per prefill item by default; 64 at head_dim <= 128 for a prefill-only batch
+    whose 128-row items would number fewer than two per CU (256 CUs without a device); an explicit
+    choice is kept, recorded and checked."""
+    few = ((100, 300), (40, 40))
+    assert h_rows(_sched(few, 32, 8, 128, 16)[0]) == 64
+    assert h_rows(_sched(few, 8, 2, 64, 16)[0]) == 64
+    assert h_rows(_sched(few + ((1, 500),), 32, 8, 128, 16)[0]) == 128  # decode runs beside the prefill
+    assert h_rows(_sched(few, 16, 2, 256, 64)[0]) == 128
+    many = ((1024, 1024),) * 4  # 4 x 32 x 8 = 1024 items of 128 rows
+    assert h_rows(_sched(many, 32, 8, 128, 16)[0]) == 128
+    assert h_rows(_sched(few, 32, 8, 128, 16, rows=128)[0]) == 128
+    assert h_rows(_sched(many, 32, 8, 128, 16, rows=64)[0]) == 64
+    with pytest.raises(aqp.AqpError) as e:
+        _sched(few, 32, 8, 128, 16, rows=32)
+    assert e.value.status == aqp.ERR_INVALID
+    # a schedule of 64-row items used with parameters that ask for 128: refused before any launch
+    s, sl, qsl, params, desc = _sched(few, 32, 8, 128, 16, rows=64)
+    p128 = aqp.attn_params(32, 8, 128, params.max_blocks_per_seq, prefill_rows=128)
+    rc = aqp._lib.aqp_paged_attention(ctypes.byref(p128), ctypes.byref(desc), 16, 16, 16, s.meta.ctypes.data, 16,
+                                      1.0, 1.0, 16, 1 << 30, 16, None)
+    assert rc == aqp.ERR_SCHEDULE_MISMATCH
