@@ -488,22 +488,46 @@ __global__ __launch_bounds__(64) void combine_kernel(const CombItem* items, cons
   const int h = blockIdx.y;
   if (h >= it.nheads) return;
   const int lane = threadIdx.x;
+  const int P = it.num_parts;
   const float* ml = scratch + (int64_t)num_parts * group_heads * D;
+  auto slot = [&](int s) { return (int64_t)(it.first_part + s) * group_heads + h; };
+  // (m, l) of the parts: lane s takes parts s, s + 64, ..., so their loads are all in flight at once
   float M = -INFINITY;
-  for (int s = 0; s < it.num_parts; ++s) M = fmaxf(M, ml[((int64_t)(it.first_part + s) * group_heads + h) * 2]);
+  for (int s = lane; s < P; s += 64) M = fmaxf(M, ml[slot(s) * 2]);
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, shfl_xor_f(M, k));
   const float M_use = M == -INFINITY ? 0.0f : M;
+  float L = 0.0f;
+  for (int s = lane; s < P; s += 64) L += fast_exp2(ml[slot(s) * 2] - M_use) * ml[slot(s) * 2 + 1];
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) L += shfl_xor_f(L, k);
   constexpr int PER = D / 64;
   float o[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) o[j] = 0.0f;
-  float L = 0.0f;
-  for (int s = 0; s < it.num_parts; ++s) {
-    const int64_t slot = (int64_t)(it.first_part + s) * group_heads + h;
-    const float* pp = scratch + slot * D;
-    const float f = fast_exp2(ml[slot * 2] - M_use);
-    L += f * ml[slot * 2 + 1];
+  for (int s0 = 0; s0 < P; s0 += 64) {
+    // weight of part s0 + lane, broadcast part by part; four parts' rows loaded before any is summed
+    const float fl = s0 + lane < P ? fast_exp2(ml[slot(s0 + lane) * 2] - M_use) : 0.0f;
+    const int n = min(64, P - s0);
+    int s = 0;
+    for (; s + 4 <= n; s += 4) {
+      float v[4][PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) o[j] += f * pp[lane + 64 * j];
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) v[u][j] = scratch[slot(s0 + s + u) * D + lane + 64 * j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), s + u));
+#pragma unroll
+        for (int j = 0; j < PER; ++j) o[j] += f * v[u][j];
+      }
+    }
+    for (; s < n; ++s) {
+      const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), s));
+#pragma unroll
+      for (int j = 0; j < PER; ++j) o[j] += f * scratch[slot(s0 + s) * D + lane + 64 * j];
+    }
   }
   const int hq = it.kvh * group + it.head0 + h;
   float fs = 1.0f;
