@@ -123,6 +123,23 @@ def test_chunk_equals_rows_of_full_prefill(window):
     assert np.array_equal(a[L - ch:], b)
 
 
+@pytest.mark.parametrize("window,softcap", [(0, 0.0), (9, 0.0), (0, 3.0)])
+def test_row_equals_one_query_sequence_ending_at_its_position(window, softcap):
+    """Under the causal mask a query row at position p sees the keys of a one-query sequence of
+    p + 1 keys over the same block table: the full-size GPU tests recompute sampled prefill rows
+    that way, so the two must agree bit for bit."""
+    c = Case([(30, 30), (1, 23), (12, 50)], 8, 2, 64, seed=12)
+    full = c.run(window=window, softcap=softcap)
+    picks = [(0, 0), (0, 17), (0, 29), (1, 0), (2, 0), (2, 5), (2, 11)]
+    seqs = [b for b, _ in picks]
+    pos1 = np.array([int(c.seq_lens[b] - (c.qsl[b + 1] - c.qsl[b]) + i + 1) for b, i in picks], np.int32)
+    rows = np.array([int(c.qsl[b] + i) for b, i in picks])
+    one = oracle.attention(c.desc, c.cache, np.ascontiguousarray(c.q[rows]), c.bt[seqs], pos1,
+                           np.arange(len(picks) + 1, dtype=np.int32), c.hq, window=window, softcap=softcap,
+                           k_scale=c.s, v_scale=2 * c.s)
+    assert np.array_equal(one, full[rows])
+
+
 def test_window_edges():
     c = Case([(6, 30), (1, 12)], 4, 2, 64, seed=6)
     base = c.run()
