@@ -20,7 +20,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 FMT_BF16, FMT_E4M3, FMT_E5M2, FMT_INT8 = 0, 1, 2, 3
-MODE_PER_TENSOR, MODE_PER_TOKEN_HEAD = 0, 1
+MODE_PER_TENSOR, MODE_PER_TOKEN_HEAD, MODE_PER_GROUP = 0, 1, 2
+GROUP = 32  # head-dim channels per scale in per-group mode
 
 
 def build(force: bool = True) -> str:

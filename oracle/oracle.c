@@ -161,7 +161,9 @@ uint16_t orc_f64_to_bf16(double x) {
 /* K pages of heads 0..Hkv-1, then the V pages. A page holds block_size rows */
 /* of head_dim code bytes, token-major; in per-token-head mode it is         */
 /* followed by block_size fp32 scales (one per row: the "inline" scale of    */
-/* the PR 38378 page). Each page is padded to a multiple of 128 bytes.       */
+/* the PR 38378 page); in per-group mode by block_size x head_dim/32 fp32    */
+/* scales (row r's group g at index r * head_dim/32 + g). Each page is       */
+/* padded to a multiple of 128 bytes.                                        */
 /* ------------------------------------------------------------------------ */
 /* Bytes per stored element: 2 for the unquantised bf16 cache, 1 for every code format. */
 static int elem_bytes(int fmt) { return fmt == ORC_FMT_BF16 ? 2 : 1; }
@@ -169,6 +171,7 @@ static int elem_bytes(int fmt) { return fmt == ORC_FMT_BF16 ? 2 : 1; }
 int64_t orc_page_bytes(const orc_cache_desc* d) {
   int64_t content = (int64_t)d->block_size * d->head_dim * elem_bytes(d->fmt);
   if (d->mode == ORC_MODE_PER_TOKEN_HEAD) content += 4 * (int64_t)d->block_size;
+  if (d->mode == ORC_MODE_PER_GROUP) content += 4 * (int64_t)d->block_size * (d->head_dim / ORC_GROUP);
   return (content + 127) / 128 * 128;
 }
 int64_t orc_block_bytes(const orc_cache_desc* d) { return 2 * (int64_t)d->num_kv_heads * orc_page_bytes(d); }
@@ -182,7 +185,8 @@ int64_t orc_page_offset(const orc_cache_desc* d, int64_t block, int kv, int head
 /* Per token with a non-negative slot, per KV head, for K then V:           */
 /*   x_d  = fp32(bf16 input)                                                 */
 /*   s    = per-tensor: the given scale; per-token-head: max_d |x_d| / qmax  */
-/*          (fp32 division), stored inline                                   */
+/*          (fp32 division), stored inline; per-group: the same over each    */
+/*          run of ORC_GROUP consecutive d, one scale per run, stored inline */
 /*   inv  = (s == 0) ? 0 : 1 / s   (fp32)                                    */
 /*   code = encode(x_d * inv)      (fp32 product, then the format's rounding)*/
 /* ------------------------------------------------------------------------ */
@@ -197,6 +201,7 @@ int orc_cache_write(const orc_cache_desc* d, uint8_t* cache, const uint16_t* k, 
   for (t = 0; t < num_tokens; ++t)
     if (slot_mapping[t] >= total_slots) bad = 1;
   if (d->fmt == ORC_FMT_BF16 && d->mode != ORC_MODE_PER_TENSOR) bad = 1;
+  if (d->mode == ORC_MODE_PER_GROUP && D % ORC_GROUP != 0) bad = 1;
   if (bad) return -1;
 #pragma omp parallel for schedule(static)
   for (t = 0; t < num_tokens; ++t) {
@@ -210,6 +215,24 @@ int orc_cache_write(const orc_cache_desc* d, uint8_t* cache, const uint16_t* k, 
         uint8_t* page = cache + orc_page_offset(d, block, kv, h);
         if (d->fmt == ORC_FMT_BF16) { /* unquantised: the input row as given */
           memcpy(page + (int64_t)off * D * 2, src, (size_t)D * 2);
+          continue;
+        }
+        if (d->mode == ORC_MODE_PER_GROUP) {
+          const int ng = D / ORC_GROUP;
+          for (int g = 0; g < ng; ++g) {
+            float a = 0.0f;
+            for (int i = g * ORC_GROUP; i < (g + 1) * ORC_GROUP; ++i) {
+              float x = fabsf(orc_bf16_to_f32(src[i]));
+              if (x > a) a = x;
+            }
+            const float sg = a / qmax;
+            memcpy(page + (int64_t)bs * D + 4 * ((int64_t)off * ng + g), &sg, 4);
+            const float inv = (sg == 0.0f) ? 0.0f : 1.0f / sg;
+            for (int i = g * ORC_GROUP; i < (g + 1) * ORC_GROUP; ++i) {
+              const float y = orc_bf16_to_f32(src[i]) * inv;
+              page[(int64_t)off * D + i] = (uint8_t)orc_encode(d->fmt, y);
+            }
+          }
           continue;
         }
         float s;
@@ -247,6 +270,15 @@ void orc_read_row(const orc_cache_desc* d, const uint8_t* cache, int kv, int64_t
     for (int i = 0; i < D; ++i) {
       memcpy(&w, page + ((int64_t)off * D + i) * 2, 2);
       row[i] = (double)orc_bf16_to_f32(w);
+    }
+    return;
+  }
+  if (d->mode == ORC_MODE_PER_GROUP) {
+    const int ng = D / ORC_GROUP;
+    for (int i = 0; i < D; ++i) {
+      float sf;
+      memcpy(&sf, page + (int64_t)d->block_size * D + 4 * ((int64_t)off * ng + i / ORC_GROUP), 4);
+      row[i] = orc_decode(d->fmt, page[(int64_t)off * D + i]) * (double)sf;
     }
     return;
   }

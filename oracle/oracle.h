@@ -35,7 +35,12 @@ extern "C" {
 /* ORC_FMT_BF16: the unquantised cache ("auto" dtype): the bf16 inputs stored as given, two bytes
  * per element, per-tensor mode only (no scales). */
 enum { ORC_FMT_BF16 = 0, ORC_FMT_E4M3 = 1, ORC_FMT_E5M2 = 2, ORC_FMT_INT8 = 3 };
-enum { ORC_MODE_PER_TENSOR = 0, ORC_MODE_PER_TOKEN_HEAD = 1 };
+/* ORC_MODE_PER_GROUP: one dynamic scale per (token, head, run of ORC_GROUP consecutive head-dim
+ * channels), absmax / qmax like per-token-head: the per-group granularity the "Per-token-head
+ * INT8/FP8 KV quantisation for Triton" page (Risk/Impact) names as a later addition without
+ * defining it; the group width is this reading's choice. */
+enum { ORC_MODE_PER_TENSOR = 0, ORC_MODE_PER_TOKEN_HEAD = 1, ORC_MODE_PER_GROUP = 2 };
+enum { ORC_GROUP = 32 };
 
 typedef struct {
   int32_t num_blocks;
