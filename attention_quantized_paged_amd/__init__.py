@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libaqp.so")
 
 KV_AUTO, KV_FP8_E4M3, KV_FP8_E5M2, KV_INT8 = 0, 1, 2, 3
-SCALE_PER_TENSOR, SCALE_PER_TOKEN_HEAD = 0, 1
+SCALE_PER_TENSOR, SCALE_PER_TOKEN_HEAD, SCALE_PER_GROUP = 0, 1, 2
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_SCHEDULE_MISMATCH, ERR_SCRATCH_TOO_SMALL, ERR_HIP = 0, -1, -2, -3, -4, -5
 
 

@@ -42,8 +42,8 @@ static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // PR 39445 page, per-token-head int8 / fp8 e4m3 as on the PR 38378 page, the
 // two remaining code pairs, and the unquantised bf16 cache ("auto", no scales).
 static int check_dtype_mode(int32_t dtype, int32_t mode, const char** why) {
-  if (mode != AQP_SCALE_PER_TENSOR && mode != AQP_SCALE_PER_TOKEN_HEAD) { *why = "unknown scale mode"; return AQP_ERR_INVALID; }
-  if (dtype == AQP_KV_AUTO && mode != AQP_SCALE_PER_TENSOR) { *why = "an unquantised cache has no per-token-head scales"; return AQP_ERR_UNSUPPORTED; }
+  if (mode != AQP_SCALE_PER_TENSOR && mode != AQP_SCALE_PER_TOKEN_HEAD && mode != AQP_SCALE_PER_GROUP) { *why = "unknown scale mode"; return AQP_ERR_INVALID; }
+  if (dtype == AQP_KV_AUTO && mode != AQP_SCALE_PER_TENSOR) { *why = "an unquantised cache has no stored scales"; return AQP_ERR_UNSUPPORTED; }
   if (dtype != AQP_KV_AUTO && dtype != AQP_KV_FP8_E4M3 && dtype != AQP_KV_FP8_E5M2 && dtype != AQP_KV_INT8) { *why = "unknown kv dtype"; return AQP_ERR_INVALID; }
   return AQP_OK;
 }
@@ -61,7 +61,7 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
   // stage raw elements in LDS, so the staged element has the same size.
   g->kv_elem_bytes = d.dtype == AQP_KV_AUTO ? 2 : 1;
   g->staged_elem_bytes = g->kv_elem_bytes;
-  g->scale_bytes = d.mode == AQP_SCALE_PER_TOKEN_HEAD ? 4 : 0;
+  g->scale_bytes = 4 * row_scales(d.head_dim, d.mode);
   g->pad_ = 0;
   g->page_bytes = round_up((int64_t)d.block_size * d.head_dim * g->kv_elem_bytes + (int64_t)d.block_size * g->scale_bytes, 128);
   g->block_bytes = 2 * (int64_t)d.num_kv_heads * g->page_bytes;
@@ -69,7 +69,7 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
   // Prefill work-group: a ring of kPfStages steps, each the K and V codes of kPfKvTile keys
   // plus their row scales; then two K and two V operand images of a step in bf16 (the codes
   // widened once per work-group), each V image followed by a copy of its step's scales.
-  g->pf_lds_bytes = kPfStages * (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes + 2 * kPfKvTile * 4) +
+  g->pf_lds_bytes = kPfStages * (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes + pf_stage_scale_bytes(d.head_dim, d.mode)) +
                     4 * kPfKvTile * d.head_dim * kPfOperandBytes + 2 * (2 * kPfKvTile * 4);
   return AQP_OK;
 }
@@ -130,6 +130,10 @@ extern "C" int aqp_parse_kv_dtype(const char* s, int32_t* dtype, int32_t* mode) 
       // the remaining codec x scale-mode pairs, named after the ones above
       {"int8", AQP_KV_INT8, AQP_SCALE_PER_TENSOR},
       {"fp8_e5m2_per_token_head", AQP_KV_FP8_E5M2, AQP_SCALE_PER_TOKEN_HEAD},
+      // per-group scales (one per 32 head-dim channels), named the same way
+      {"int8_per_group", AQP_KV_INT8, AQP_SCALE_PER_GROUP},
+      {"fp8_per_group", AQP_KV_FP8_E4M3, AQP_SCALE_PER_GROUP},
+      {"fp8_e5m2_per_group", AQP_KV_FP8_E5M2, AQP_SCALE_PER_GROUP},
   };
   for (auto& e : table) {
     if (std::strcmp(s, e.name) == 0) { *dtype = e.dt; *mode = e.md; return AQP_OK; }

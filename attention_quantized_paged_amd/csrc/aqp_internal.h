@@ -43,6 +43,14 @@ constexpr int kMinRunTiles = 32;     // decode: fewest 16-key tiles a work-group
 constexpr int kCwRowsPerLane = 4;    // cache write: rows each lane loads before converting
 constexpr int kCwWgsPerCu = 16;      // cache write: resident work-groups per CU (grid cap)
 constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per compute unit (gfx950)
+// fp32 scales stored per cache row: none per tensor, one per token-head, head_dim / 32 per group
+constexpr int row_scales(int head_dim, int mode) {
+  return mode == AQP_SCALE_PER_TOKEN_HEAD ? 1 : (mode == AQP_SCALE_PER_GROUP ? head_dim / AQP_SCALE_GROUP : 0);
+}
+// prefill: scale bytes of one ring stage (K and V of kPfKvTile keys; at least one float per key)
+constexpr int pf_stage_scale_bytes(int head_dim, int mode) {
+  return 2 * kPfKvTile * 4 * (row_scales(head_dim, mode) > 1 ? row_scales(head_dim, mode) : 1);
+}
 
 // Decode LDS: per compute wave, a ring of dec_stages tiles (each the K and V codes of 16 keys plus
 // their per-token-head scales) and one Q slot (the q rows of one segment); then the merge area
@@ -50,7 +58,7 @@ constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per compute unit (gfx950)
 // (eb: bytes per stored element, 1 for the codes, 2 for the unquantised bf16 cache)
 constexpr int dec_stages(int head_dim, int eb) { return head_dim * eb >= 256 ? 2 : 3; }
 constexpr int dec_slot_bytes(int head_dim, int mode, int eb) {
-  return 2 * kDecIterKeys * head_dim * eb + (mode == AQP_SCALE_PER_TOKEN_HEAD ? 2 * kDecIterKeys * 4 : 0);
+  return 2 * kDecIterKeys * head_dim * eb + 2 * kDecIterKeys * 4 * row_scales(head_dim, mode);
 }
 // Floats per (wave, head) row of the merge area: D of O, then m and l, padded to a multiple of 4
 // so each lane's 4 consecutive values move as one 16-byte LDS access; with D/4 + 1 16-byte units

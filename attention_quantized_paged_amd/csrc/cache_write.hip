@@ -14,7 +14,7 @@
 // several rows before it converts any, so enough bytes are in flight per CU
 // to cover HBM latency; the grid is one resident wave of work-groups that
 // strides over the rows. The per-token-head absmax is a butterfly over the
-// row's lanes.
+// row's lanes (per group: over the group's lanes).
 //
 // Rounding: the hardware fp32 -> fp8 conversions of gfx950 round to nearest
 // even; values are first clamped to the largest finite code (v_med3) so that
@@ -86,12 +86,15 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
       float x[8] = {bf16_lo(in[u].x), bf16_hi(in[u].x), bf16_lo(in[u].y), bf16_hi(in[u].y),
                     bf16_lo(in[u].z), bf16_hi(in[u].z), bf16_lo(in[u].w), bf16_hi(in[u].w)};
       float s;
-      if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
+      if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD || MODE == AQP_SCALE_PER_GROUP) {
+        // absmax over the row (per token-head) or over the lane's group of AQP_SCALE_GROUP
+        // channels (per group: AQP_SCALE_GROUP / 8 neighbouring lanes)
+        constexpr int SPAN = MODE == AQP_SCALE_PER_GROUP ? AQP_SCALE_GROUP / 8 : TPR;
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
 #pragma unroll
-        for (int o = TPR / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        for (int o = SPAN / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
         s = amax / QMAX;  // correctly rounded fp32 division
       } else {
         s = kv[u] ? a.v_scale : a.k_scale;
@@ -112,6 +115,11 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
       *(uint2*)(page + (int64_t)off * D + sub * 8) = codes;
       if constexpr (MODE == AQP_SCALE_PER_TOKEN_HEAD) {
         if (sub == 0) *(float*)(page + (int64_t)a.block_size * D + 4 * off) = s;
+      }
+      if constexpr (MODE == AQP_SCALE_PER_GROUP) {
+        constexpr int NG = D / AQP_SCALE_GROUP;
+        constexpr int SPAN = AQP_SCALE_GROUP / 8;
+        if (sub % SPAN == 0) *(float*)(page + (int64_t)a.block_size * D + 4 * ((int64_t)off * NG + sub / SPAN)) = s;
       }
     }
   }
@@ -153,6 +161,9 @@ int launch_cache_write(int dtype, int mode, const CacheWriteArgs& a, void* strea
   if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_FP8_E4M3) return dispatch_d<AQP_KV_FP8_E4M3, AQP_SCALE_PER_TOKEN_HEAD>(a, st);
   if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_INT8) return dispatch_d<AQP_KV_INT8, AQP_SCALE_PER_TENSOR>(a, st);
   if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_FP8_E5M2) return dispatch_d<AQP_KV_FP8_E5M2, AQP_SCALE_PER_TOKEN_HEAD>(a, st);
+  if (mode == AQP_SCALE_PER_GROUP && dtype == AQP_KV_INT8) return dispatch_d<AQP_KV_INT8, AQP_SCALE_PER_GROUP>(a, st);
+  if (mode == AQP_SCALE_PER_GROUP && dtype == AQP_KV_FP8_E4M3) return dispatch_d<AQP_KV_FP8_E4M3, AQP_SCALE_PER_GROUP>(a, st);
+  if (mode == AQP_SCALE_PER_GROUP && dtype == AQP_KV_FP8_E5M2) return dispatch_d<AQP_KV_FP8_E5M2, AQP_SCALE_PER_GROUP>(a, st);
   set_error("aqp_cache_write: dtype %d with scale mode %d is not built", dtype, mode);
   return AQP_ERR_UNSUPPORTED;
 }

@@ -147,14 +147,17 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
   constexpr int CPR = ROWB / 16;                  // 16-byte chunks per staged row
   constexpr int STEP = kDecWaves * kDecIterKeys;  // keys between a wave's consecutive tiles
   constexpr int PTH = MODE == AQP_SCALE_PER_TOKEN_HEAD ? 1 : 0;
+  constexpr int PG = MODE == AQP_SCALE_PER_GROUP ? 1 : 0;
+  constexpr int NG = D / AQP_SCALE_GROUP;          // scale groups of a row (per-group mode)
   constexpr int NS = dec_stages(D, EB);           // ring slots per wave
   constexpr int NQ = 1;                           // Q slots per wave
   constexpr int TB = kDecIterKeys * ROWB;         // bytes of one K (or V) tile
   constexpr int KI = TB / 1024;                   // 1 KB copies per K (or V) tile
   constexpr int SLOT = dec_slot_bytes(D, MODE, EB);  // K tile, V tile, K scales, V scales
-  constexpr int IPT = 2 * KI + PTH;               // copies per tile
+  constexpr int IPT = 2 * KI + PTH + PG;          // copies per tile
   static_assert(KI >= 1 && IPT * (NS - 1) <= 63, "tile copies and waits");
-  static_assert(EB == 1 || !PTH, "the unquantised cache has no scales");
+  static_assert(EB == 1 || (!PTH && !PG), "the unquantised cache has no scales");
+  static_assert(8 * NG <= 64, "one copy holds a tile's group scales");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -283,6 +286,13 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
       const uint8_t* sp = ((lane & 4) ? vpage : kpage) + (int64_t)(a.block_size - is_p.r0) * D + 4 * (is_p.r0 + 4 * (lane & 3));
       if (lane < 8) dma16_to_lds(sp, slot + (uint32_t)(2 * TB));
     }
+    if constexpr (PG) {
+      // the tile's 16 x NG group scales of K (lanes 0 .. 4NG-1), then of V (lanes 4NG .. 8NG-1)
+      const int sl = lane % (4 * NG);
+      const uint8_t* sp = (lane >= 4 * NG ? vpage : kpage) + (int64_t)(a.block_size - is_p.r0) * D +
+                          4 * (int64_t)is_p.r0 * NG + 16 * sl;
+      if (lane < 8 * NG) dma16_to_lds(sp, slot + (uint32_t)(2 * TB));
+    }
     ++n_issued;
     is_slot = is_slot + SLOT == NS * SLOT ? 0u : is_slot + SLOT;
     if (--is_left > 0) {
@@ -326,10 +336,11 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
       wait_tiles_ahead<IPT, NS>(n_issued - n_done - 1);
       if (k == 0) {
         // Q^T operand: lane (column head r16, group kg) holds q[head][kg*D/4 + 8*st + 0..7]
-        const uint8_t* qp = qslots + (q_read % NQ) * QB + r16 * (D * 2) + kg * (D / 2);
+        // (per group: q[head][32*st + 8*kg + 0..7], so that MFMA step st covers scale group st)
+        const uint8_t* qp = qslots + (q_read % NQ) * QB + r16 * (D * 2) + (PG ? kg * 16 : kg * (D / 2));
 #pragma unroll
         for (int st = 0; st < QS; ++st) {
-          uint4 u = *(const uint4*)(qp + st * 16);
+          uint4 u = *(const uint4*)(qp + st * (PG ? 64 : 16));
           if (!head_ok) u = make_uint4(0, 0, 0, 0);
           qb[st] = __builtin_bit_cast(bf16x8, u);
         }
@@ -343,7 +354,18 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
 
       // ---- S^T = K * Q^T: lane holds keys k0 + 4kg + r of head r16
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (EB == 1) {
+      if constexpr (PG) {
+        // per group: MFMA step st takes depth 32*st + 8*kg + 0..7 (group st) from K, exactly
+        // widened; its product is scaled per key by that key's group scale, in fp32
+        const float* ksr = (const float*)(kl + 2 * TB) + (4 * kg) * NG;
+#pragma unroll
+        for (int st = 0; st < QS; ++st) {
+          const uint2 w = *(const uint2*)(kl + r16 * ROWB + (((2 * st + (kg >> 1)) ^ k_swz) << 4) + 8 * (kg & 1));
+          const f32x4 sg = mfma16x16x32(widen8<DT>(w.x, w.y), qb[st], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[r] += ksr[r * NG + st] * sg[r];
+        }
+      } else if constexpr (EB == 1) {
 #pragma unroll
         for (int c2 = 0; c2 < QS / 2; ++c2) {
           const uint4 w = *(const uint4*)(kl + r16 * ROWB + (((kg * (QS / 2) + c2) ^ k_swz) << 4));
@@ -439,7 +461,22 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
 #pragma unroll
       for (int r = 0; r < 4; ++r) pb[r] = (__bf16)p4[r];
       // ---- O^T[d][head] += V^T[d][keys] P^T[keys][head]
-      if constexpr (EB == 1) {
+      if constexpr (PG) {
+        // per group: head-dim tiles 2g, 2g+1 form group g; its P^T operand carries the keys' V
+        // scales of that group (masked keys select 0: their scale slots may be unwritten)
+        const float* vsg = (const float*)(kl + 2 * TB) + 16 * NG + (4 * kg) * NG;
+#pragma unroll
+        for (int t2 = 0; t2 < NT / 2; ++t2) {
+          bf16x4 pg;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool kok = (vmask >> (8 * r)) & 1;
+            pg[r] = (__bf16)(kok ? p4[r] * vsg[r * NG + t2] : 0.0f);
+          }
+          acc[2 * t2] = mfma16x16x16(widen4v<DT>((uint32_t)vw[t2].x & vmask), pg, acc[2 * t2]);
+          acc[2 * t2 + 1] = mfma16x16x16(widen4v<DT>((uint32_t)vw[t2].y & vmask), pg, acc[2 * t2 + 1]);
+        }
+      } else if constexpr (EB == 1) {
 #pragma unroll
         for (int t2 = 0; t2 < NT / 2; ++t2) {
           acc[2 * t2] = mfma16x16x16(widen4v<DT>((uint32_t)vw[t2].x & vmask), pb, acc[2 * t2]);
@@ -607,6 +644,9 @@ int launch_decode(int dtype, int mode, const AttnArgs& a, void* stream) {
   if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_FP8_E4M3) return dec_d<AQP_KV_FP8_E4M3, AQP_SCALE_PER_TOKEN_HEAD>(a, st);
   if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_INT8) return dec_d<AQP_KV_INT8, AQP_SCALE_PER_TENSOR>(a, st);
   if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_FP8_E5M2) return dec_d<AQP_KV_FP8_E5M2, AQP_SCALE_PER_TOKEN_HEAD>(a, st);
+  if (mode == AQP_SCALE_PER_GROUP && dtype == AQP_KV_INT8) return dec_d<AQP_KV_INT8, AQP_SCALE_PER_GROUP>(a, st);
+  if (mode == AQP_SCALE_PER_GROUP && dtype == AQP_KV_FP8_E4M3) return dec_d<AQP_KV_FP8_E4M3, AQP_SCALE_PER_GROUP>(a, st);
+  if (mode == AQP_SCALE_PER_GROUP && dtype == AQP_KV_FP8_E5M2) return dec_d<AQP_KV_FP8_E5M2, AQP_SCALE_PER_GROUP>(a, st);
   set_error("aqp_paged_attention: dtype %d with scale mode %d is not built", dtype, mode);
   return AQP_ERR_UNSUPPORTED;
 }

@@ -68,6 +68,16 @@ __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// Eight codes of one scale (per-group mode) -> bf16(value * s), rounded to nearest even once.
+template <int DT>
+__device__ __forceinline__ bf16x8 widen8_scaled(uint32_t w0, uint32_t w1, float s) {
+  const bf16x8 e = widen8<DT>(w0, w1);
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)((float)e[i] * s);
+  return r;
+}
+
 template <int DT>
 __device__ __forceinline__ bf16x4 widen4v(uint32_t w) {
   uint32_t r0, r1;

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   constexpr int EB = DT == AQP_KV_AUTO ? 2 : 1;   // bytes per stored element (bf16 when unquantised)
   constexpr int ROWB = D * EB;                    // bytes of one staged key row
   constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
-  constexpr int STAGE = 2 * KT * ROWB + 2 * KT * 4;  // K rows, V rows, K scales, V scales
+  constexpr int STAGE = 2 * KT * ROWB + pf_stage_scale_bytes(D, MODE);  // K rows, V rows, K scales, V scales
   constexpr int KV_INSTR = KT * CPR / 64;         // 1 KB copies per K (or V) step
   constexpr int IPW = 2 * KV_INSTR / WAVES;       // K+V copies per wave per step
   static_assert(IPW >= 1 && (2 * KV_INSTR) % WAVES == 0, "copies must split evenly over the waves");
@@ -82,6 +82,11 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   constexpr int VB_PW = NT / WAVES;               // V blocks each wave converts
   static_assert(KB_PW >= 1 && KBLK % WAVES == 0 && VB_PW >= 1 && NT % WAVES == 0, "blocks must split evenly");
   constexpr int PTH = MODE == AQP_SCALE_PER_TOKEN_HEAD ? 1 : 0;
+  constexpr int PG = MODE == AQP_SCALE_PER_GROUP ? 1 : 0;
+  constexpr int NG = D / AQP_SCALE_GROUP;          // scale groups of a row (per-group mode)
+  constexpr int SCH = 64 * NG;                     // bytes of one 16-key tile's group scales
+  constexpr int SCI = PTH ? 1 : (PG ? (4 * SCH + 1023) / 1024 : 0);  // scale copies per step
+  static_assert(EB == 1 || (!PTH && !PG), "the unquantised cache has no scales");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   const uint8_t* vbase = a.cache + (int64_t)(a.num_kv_heads + it.kvh) * a.page_bytes;
   const uint32_t lds0 = lds_addr(smem);
   // copies this wave issues per step: its share of K/V, plus the scale copy on the last wave
-  const int ipw_me = IPW + ((PTH && wave == WAVES - 1) ? 1 : 0);
+  const int ipw_me = IPW + (wave == WAVES - 1 ? SCI : 0);
 
   // ---- rows of this lane (as MFMA column r16 of the wave's row tiles)
   int lo_r[RT], hi_r[RT];
@@ -122,10 +127,11 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
     lo_r[rt] = (a.window > 0 && p - a.window + 1 > 0) ? p - a.window + 1 : 0;
     if (!row_ok[rt]) { lo_r[rt] = 0; hi_r[rt] = 0; }
     orow[rt] = ((int64_t)(it.q_start + t) * a.num_q_heads + it.kvh * G + g) * D;
-    const uint16_t* qp = a.q + orow[rt] + kg * (D / 4);
+    // (per group: depth 32*st + 8*kg + 0..7, so that MFMA step st covers scale group st)
+    const uint16_t* qp = a.q + orow[rt] + (PG ? kg * 8 : kg * (D / 4));
 #pragma unroll
     for (int st = 0; st < QS; ++st) {
-      uint4 u = *(const uint4*)(qp + st * 8);
+      uint4 u = *(const uint4*)(qp + st * (PG ? 32 : 8));
       if (!row_ok[rt]) u = make_uint4(0, 0, 0, 0);
       qb[rt][st] = __builtin_bit_cast(bf16x8, u);
     }
@@ -202,6 +208,26 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
         if (lane < 16) dma16_to_lds(src, sbase + (uint32_t)(2 * KT * ROWB));
       }
     }
+    if constexpr (PG) {
+      if (wave == WAVES - 1) {
+        // [K scales of key tile 0][K tile 1][V tile 0][V tile 1]: 16 rows x NG floats each
+        const int t0 = min(kb0, last_tile), t1 = min(kb0 + 16, last_tile);
+        const int bi0 = t0 / a.block_size, bi1 = t1 / a.block_size;
+        int32_t b0 = bt[bi0], b1 = bt[bi1];
+        if ((uint32_t)b0 >= (uint32_t)a.num_blocks) b0 = 0;
+        if ((uint32_t)b1 >= (uint32_t)a.num_blocks) b1 = 0;
+#pragma unroll
+        for (int j = 0; j < SCI; ++j) {
+          const int o = 1024 * j + 16 * lane;
+          const int c = o / SCH, w = o - (o / SCH) * SCH;
+          const int tl = c & 1, kv = (c >> 1) & 1;
+          const int r0 = (tl ? t1 : t0) - (tl ? bi1 : bi0) * a.block_size;
+          const uint8_t* src = (kv ? vbase : kbase) + (int64_t)(tl ? b1 : b0) * a.block_bytes +
+                               (int64_t)a.block_size * D + 4 * (int64_t)r0 * NG + w;
+          if (o < 4 * SCH) dma16_to_lds(src, sbase + (uint32_t)(2 * KT * ROWB + 1024 * j));
+        }
+      }
+    }
   };
 
   // transposed V read: row i of lane group kg is key (i < 4 ? 4kg + i : 16 + 4kg + i - 4)
@@ -220,7 +246,13 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       const int kt = blk / QS, st = blk - (blk / QS) * QS;
       const int krow = kt * 16 + r16;
       const int dbyte = (kg * (D / 4) + st * 8) * EB;
-      if constexpr (EB == 1) {
+      if constexpr (PG) {
+        // per group: depth 32*st + 8*kg + 0..7 (group st), exact codes; the key's group scale
+        // multiplies the product in the QK step
+        const int gbyte = 32 * st + 8 * kg;
+        const uint2 c = *(const uint2*)(kl + krow * ROWB + ((((gbyte >> 4) ^ swz<ROWB>(krow)) << 4) | (gbyte & 8)));
+        *(bf16x8*)(img + blk * 1024) = widen8<DT>(c.x, c.y);
+      } else if constexpr (EB == 1) {
         const uint2 c = *(const uint2*)(kl + krow * ROWB + ((((dbyte >> 4) ^ swz<ROWB>(krow)) << 4) | (dbyte & 8)));
         *(bf16x8*)(img + blk * 1024) = widen8<DT>(c.x, c.y);
       } else {
@@ -241,7 +273,22 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       for (int j = 0; j < VB_PW; ++j) {
         const int t = wave * VB_PW + j;
         const i32x2 c = lds_read_tr8(rp + ((t ^ tr_swz) << 4));
-        *(bf16x8*)(slot + t * 1024 + lane * 16) = widen8<DT>((uint32_t)c.x, (uint32_t)c.y);
+        if constexpr (PG) {
+          // element i is key row (i < 4 ? 4kg + i : 16 + 4kg + i - 4) at a head-dim column of
+          // group t / 2: bf16(code * that key's scale); keys past L get 0
+          const float* vsc = (const float*)(kl + 2 * KT * ROWB) + 2 * 16 * NG;
+          const bf16x8 e = widen8<DT>((uint32_t)c.x, (uint32_t)c.y);
+          bf16x8 r;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int row = i < 4 ? 4 * kg + i : 16 + 4 * kg + i - 4;
+            const float sc = k_begin + step * KT + row < it.L ? vsc[row * NG + (t >> 1)] : 0.0f;
+            r[i] = (__bf16)((float)e[i] * sc);
+          }
+          *(bf16x8*)(slot + t * 1024 + lane * 16) = r;
+        } else {
+          *(bf16x8*)(slot + t * 1024 + lane * 16) = widen8<DT>((uint32_t)c.x, (uint32_t)c.y);
+        }
       }
     } else {
       // bf16 rows: the lane's 8 keys of head-dim column t * 16 + r16, one 16-bit read each
@@ -273,14 +320,38 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       for (int st = 0; st < QS; ++st) kw[kt][st] = *(const bf16x8*)(img + (kt * QS + st) * 1024);
   };
   // ---- half h of the depth slices of S^T = K Q^T: [key tile kt][row tile rt]
-  auto qk_half = [&](int h, const bf16x8 (&kw)[2][QS], f32x4 (&s)[2][RT]) {
+  // (per group: `sstep` is the step S belongs to; each depth slice is group st, its product
+  // scaled per key by the key's group scale from that step's ring stage, keys past L by 0)
+  auto qk_half = [&](int h, const bf16x8 (&kw)[2][QS], f32x4 (&s)[2][RT], int sstep) {
+    if constexpr (PG) {
+      const float* ksc = (const float*)(smem + (sstep % NS) * STAGE + 2 * KT * ROWB);
+      const int kb = k_begin + sstep * KT;
 #pragma unroll
-    for (int st = h * (QS / 2); st < (h + 1) * (QS / 2); ++st)
+      for (int st = h * (QS / 2); st < (h + 1) * (QS / 2); ++st)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt) {
+          float sc[4];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          s[kt][rt] = mfma16x16x32(kw[kt][st], qb[rt][st], st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kt][rt]);
+          for (int r = 0; r < 4; ++r) {
+            const int key = kt * 16 + 4 * kg + r;
+            sc[r] = kb + key < it.L ? ksc[key * NG + st] : 0.0f;
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const f32x4 sg = mfma16x16x32(kw[kt][st], qb[rt][st], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[kt][rt][r] = (st == 0 ? 0.0f : s[kt][rt][r]) + sc[r] * sg[r];
+          }
+        }
+    } else {
+#pragma unroll
+      for (int st = h * (QS / 2); st < (h + 1) * (QS / 2); ++st)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            s[kt][rt] = mfma16x16x32(kw[kt][st], qb[rt][st], st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kt][rt]);
+    }
   };
 
   // ---- prologue: stages 0 and 1 widened, S of step 0
@@ -303,8 +374,8 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
     __syncthreads();
     bf16x8 kw[2][QS];
     read_k(0, kw);
-    qk_half(0, kw, s_cur);
-    qk_half(1, kw, s_cur);
+    qk_half(0, kw, s_cur, 0);
+    qk_half(1, kw, s_cur, 0);
   }
   for (int step = 0; step < n_steps; ++step) {
     // stage step + 2 landed once only the copies of later stages are outstanding
@@ -365,7 +436,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
 
     // first half of S of step + 1 while the row maxima of step are taken
     f32x4 s_next[2][RT];
-    qk_half(0, kw, s_next);
+    qk_half(0, kw, s_next, step + 1);
     float mx[RT];
     bool grow = false;
 #pragma unroll
@@ -400,7 +471,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
     bf16x8 vw[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) vw[t] = *(const bf16x8*)(vimg + t * 1024);
-    qk_half(1, kw, s_next);
+    qk_half(1, kw, s_next, step + 1);
     bf16x8 pb[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -544,6 +615,9 @@ int launch_prefill(int dtype, int mode, const AttnArgs& a, void* stream) {
   if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_FP8_E4M3) return pf_d<AQP_KV_FP8_E4M3, AQP_SCALE_PER_TOKEN_HEAD>(a, st);
   if (mode == AQP_SCALE_PER_TENSOR && dtype == AQP_KV_INT8) return pf_d<AQP_KV_INT8, AQP_SCALE_PER_TENSOR>(a, st);
   if (mode == AQP_SCALE_PER_TOKEN_HEAD && dtype == AQP_KV_FP8_E5M2) return pf_d<AQP_KV_FP8_E5M2, AQP_SCALE_PER_TOKEN_HEAD>(a, st);
+  if (mode == AQP_SCALE_PER_GROUP && dtype == AQP_KV_INT8) return pf_d<AQP_KV_INT8, AQP_SCALE_PER_GROUP>(a, st);
+  if (mode == AQP_SCALE_PER_GROUP && dtype == AQP_KV_FP8_E4M3) return pf_d<AQP_KV_FP8_E4M3, AQP_SCALE_PER_GROUP>(a, st);
+  if (mode == AQP_SCALE_PER_GROUP && dtype == AQP_KV_FP8_E5M2) return pf_d<AQP_KV_FP8_E5M2, AQP_SCALE_PER_GROUP>(a, st);
   set_error("aqp_paged_attention: dtype %d with scale mode %d is not built", dtype, mode);
   return AQP_ERR_UNSUPPORTED;
 }

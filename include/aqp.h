@@ -42,11 +42,16 @@ typedef enum {
 } aqp_kv_dtype;
 
 /* Scale granularity ([P38378] Implementation item 1: the quantisation-mode
- * switch between per-tensor and per-token-head). */
+ * switch between per-tensor and per-token-head; its Risk/Impact names
+ * per-group scales as a later addition without defining them: the reading
+ * taken is AQP_SCALE_PER_GROUP). */
 typedef enum {
-  AQP_SCALE_PER_TENSOR = 0,    /* one k_scale and one v_scale, passed by the caller */
-  AQP_SCALE_PER_TOKEN_HEAD = 1 /* one dynamic scale per (token, KV head), K and V apart, stored in the cache */
+  AQP_SCALE_PER_TENSOR = 0,     /* one k_scale and one v_scale, passed by the caller */
+  AQP_SCALE_PER_TOKEN_HEAD = 1, /* one dynamic scale per (token, KV head), K and V apart, stored in the cache */
+  AQP_SCALE_PER_GROUP = 2       /* one dynamic scale per (token, KV head, run of AQP_SCALE_GROUP consecutive
+                                   head-dim channels), K and V apart, stored in the cache */
 } aqp_scale_mode;
+#define AQP_SCALE_GROUP 32
 
 typedef enum {
   AQP_OK = 0,
@@ -69,7 +74,9 @@ typedef enum {
  *    = one token of one head), followed in per-token-head mode by block_size
  *    fp32 scales (the scale of row r at page + block_size*head_dim + 4*r:
  *    the inline scale storage of [P38378] Implementation item 2, kept at the
- *    page tail so rows stay 16-byte aligned);
+ *    page tail so rows stay 16-byte aligned), in per-group mode by
+ *    block_size * head_dim/32 fp32 scales (row r's group g at
+ *    page + block_size*head_dim + 4*(r*head_dim/32 + g));
  *  - page_bytes is that content rounded up to a multiple of 128 bytes;
  *  - slot s is row (s % block_size) of block (s / block_size).
  * Supported: head_dim in {64, 128, 256} (AUTO: 64 and 128 in attention);
@@ -126,6 +133,9 @@ typedef struct {
  * library's own:
  *   "int8"                  -> INT8,     PER_TENSOR
  *   "fp8_e5m2_per_token_head" -> FP8_E5M2, PER_TOKEN_HEAD
+ *   "int8_per_group"        -> INT8,     PER_GROUP
+ *   "fp8_per_group"         -> FP8_E4M3, PER_GROUP
+ *   "fp8_e5m2_per_group"    -> FP8_E5M2, PER_GROUP
  *   "auto"                  -> AUTO,     PER_TENSOR (the unquantised cache)
  * Anything else: AQP_ERR_INVALID. Outputs are written only on AQP_OK. */
 int aqp_parse_kv_dtype(const char* s, int32_t* dtype, int32_t* mode);

@@ -63,6 +63,18 @@ SMALL = [
     W.Workload("auto_mixed_d128", "auto", ((1, 600), (70, 310), (33, 33), (1, 17)), 32, 8, 128, 16, 80, seed=90),
     W.Workload("auto_prefill_d64_w_cap", "auto", ((40, 40), (9, 130)), 8, 2, 64, 32, 12, window=50, softcap=10.0,
                seed=96),
+    # per-group scales (one per 32 head-dim channels): every codec and head_dim, decode (split and
+    # whole), prefill (64- and 128-row items) and mixed batches, window and soft-cap
+    W.scaled(W.CFG3, name="pg_e4m3_decode_llama8b", kv_dtype="fp8_per_group",
+             seqs=((1, 700), (1, 33), (1, 1500), (1, 16), (1, 1)), num_blocks=300),
+    W.Workload("pg_int8_mixed_d128_w_cap", "int8_per_group", ((1, 900), (40, 200), (1, 31), (17, 17)), 32, 8, 128,
+               16, 100, window=150, softcap=20.0, seed=97),
+    W.Workload("pg_e5m2_mixed_d64", "fp8_e5m2_per_group", ((1, 300), (12, 12), (1, 3), (30, 95)), 8, 2, 64, 16, 40,
+               seed=98),
+    W.Workload("pg_e4m3_d256_mixed_cap", "fp8_per_group", ((1, 333), (3, 40), (1, 1024), (37, 37)), 32, 2, 256, 64,
+               40, softcap=8.0, seed=99),
+    W.Workload("pg_int8_prefill_d256_bs2176", "int8_per_group", ((130, 130), (9, 300)), 16, 2, 256, 2176, 3,
+               seed=100),
 ]
 
 
@@ -115,6 +127,8 @@ NAN_FILL = [
     W.Workload("nanfill_prefill_e4m3", "fp8_e4m3", ((19, 19), (40, 70)), 8, 2, 256, 32, 12, seed=93),
     W.Workload("nanfill_prefill_e4m3_pth_w", "fp8_per_token_head", ((33, 33), (9, 60)), 4, 1, 128, 16, 16, window=20,
                seed=94),
+    W.Workload("nanfill_pg_mixed_d128", "fp8_per_group", ((1, 37), (21, 45), (1, 100)), 8, 2, 128, 32, 16, seed=95),
+    W.Workload("nanfill_pg_prefill_d256_int8", "int8_per_group", ((19, 19), (40, 70)), 8, 2, 256, 32, 12, seed=101),
 ]
 
 
@@ -131,7 +145,8 @@ def test_unwritten_cache_bytes_do_not_leak(aqp, w):
 
 
 ROWS_CASES = [w for w in SMALL if w.name in ("prefill_cap5_w37_d128", "g160_mixed_e5m2", "auto_prefill_d64_w_cap",
-                                             "e5m2_pth_mixed_w_cap", "d64_int8_mixed", "noncausal_prefill")]
+                                             "e5m2_pth_mixed_w_cap", "d64_int8_mixed", "noncausal_prefill",
+                                             "pg_int8_mixed_d128_w_cap", "pg_e5m2_mixed_d64")]
 
 
 @pytest.mark.parametrize("rows", [64, 128])
@@ -239,7 +254,8 @@ def test_block_permutation_bit_identical(aqp):
 
 
 @pytest.mark.parametrize("dtype_str", ["fp8_e4m3", "fp8_e5m2", "int8_per_token_head", "fp8_per_token_head", "int8",
-                                       "fp8_e5m2_per_token_head", "auto"])
+                                       "fp8_e5m2_per_token_head", "auto", "int8_per_group", "fp8_per_group",
+                                       "fp8_e5m2_per_group"])
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_cache_write_bit_exact(aqp, dtype_str, D):
     """Random slots (some negative), a fused-QKV token stride, specials (zero rows, huge and tiny

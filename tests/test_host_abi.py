@@ -50,9 +50,11 @@ def test_parse_kv_dtype_matches_pages(s, idx, mode):
     assert aqp.parse_kv_dtype(s) == (idx, mode)
 
 
-@pytest.mark.parametrize("s,idx,mode", [("int8", 3, 0), ("fp8_e5m2_per_token_head", 2, 1)])
+@pytest.mark.parametrize("s,idx,mode", [("int8", 3, 0), ("fp8_e5m2_per_token_head", 2, 1), ("int8_per_group", 3, 2),
+                                        ("fp8_per_group", 1, 2), ("fp8_e5m2_per_group", 2, 2)])
 def test_parse_extension_pairs(s, idx, mode):
-    """The two codec x scale-mode pairs the pages leave for later, under this library's names."""
+    """The codec x scale-mode pairs the pages leave for later (the two remaining per-tensor /
+    per-token-head pairs and the per-group mode), under this library's names."""
     assert aqp.parse_kv_dtype(s) == (idx, mode)
 
 
@@ -68,7 +70,8 @@ FMT = {aqp.KV_AUTO: oracle.FMT_BF16, aqp.KV_FP8_E4M3: oracle.FMT_E4M3, aqp.KV_FP
 
 
 @pytest.mark.parametrize("dtype_str", ["fp8_e4m3", "fp8_e5m2", "int8_per_token_head", "fp8_per_token_head", "int8",
-                                       "fp8_e5m2_per_token_head", "auto"])
+                                       "fp8_e5m2_per_token_head", "auto", "int8_per_group", "fp8_per_group",
+                                       "fp8_e5m2_per_group"])
 @pytest.mark.parametrize("nb,bs,h,d", [(8, 16, 2, 64), (4, 2176, 2, 256), (40000, 16, 8, 128), (3, 32, 3, 128)])
 def test_cache_bytes_match_oracle_layout(dtype_str, nb, bs, h, d):
     desc = aqp.cache_desc(nb, bs, h, d, dtype_str)
@@ -87,14 +90,14 @@ def test_unsupported_geometry(bad):
     assert e.value.status in (aqp.ERR_UNSUPPORTED, aqp.ERR_INVALID)
 
 
-@pytest.mark.parametrize("dt,md", [(aqp.KV_AUTO, 1)])
+@pytest.mark.parametrize("dt,md", [(aqp.KV_AUTO, 1), (aqp.KV_AUTO, 2)])
 def test_unbuilt_dtype_mode_pairs_are_errors(dt, md):
     with pytest.raises(aqp.AqpError) as e:
         aqp.cache_bytes(aqp.CacheDesc(4, 16, 2, 64, dt, md))
     assert e.value.status == aqp.ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("dt,md", [(4, 0), (aqp.KV_FP8_E4M3, 2), (-1, 0)])
+@pytest.mark.parametrize("dt,md", [(4, 0), (aqp.KV_FP8_E4M3, 3), (-1, 0)])
 def test_unknown_dtype_or_mode_is_invalid(dt, md):
     with pytest.raises(aqp.AqpError) as e:
         aqp.cache_bytes(aqp.CacheDesc(4, 16, 2, 64, dt, md))

@@ -255,3 +255,25 @@ def test_prefill_rows_choice():
     rc = aqp._lib.aqp_paged_attention(ctypes.byref(p128), ctypes.byref(desc), 16, 16, 16, s.meta.ctypes.data, 16,
                                       1.0, 1.0, 16, 1 << 30, 16, None)
     assert rc == aqp.ERR_SCHEDULE_MISMATCH
+
+
+@pytest.mark.parametrize("d,bs", [(64, 16), (128, 16), (256, 2176)])
+def test_per_group_geometry_and_mismatch(d, bs):
+    """Per-group mode: one fp32 scale per 32 channels per row, staged beside the codes (decode: a
+    tile's 16 rows x d/32 scales for K and V; prefill: 32 keys' for K and V per ring stage)."""
+    ng = d // 32
+    hq, hkv = 16, 2
+    s, sl, qsl, params, desc = _sched(((1, 300), (40, 40)), hq, hkv, d, bs, dtype="fp8_per_group")
+    h = s.header
+    assert h["scale_bytes"] == 4 * ng and h["kv_elem_bytes"] == 1
+    assert h["pf_lds_bytes"] == 4 * (2 * 32 * d + 2 * 32 * 4 * max(1, ng)) + 4 * 32 * d * 2 + 2 * 2 * 32 * 4
+    hpu = 16 if d <= 128 else 8
+    gh = min(hq // hkv, hpu)
+    stages = 2 if d >= 256 else 3
+    assert h["dec_lds_bytes"] == 4 * (stages * (2 * 16 * d + 2 * 16 * 4 * ng) + gh * d * 2) + 4 * gh * (d + 4) * 4
+    assert h["dec_lds_bytes"] <= 160 * 1024 and h["pf_lds_bytes"] <= 160 * 1024
+    # a schedule built for per-token-head scales is refused for the per-group cache
+    s2, *_ = _sched(((1, 300), (40, 40)), hq, hkv, d, bs, dtype="fp8_per_token_head")
+    rc = aqp._lib.aqp_paged_attention(ctypes.byref(params), ctypes.byref(desc), 16, 16, 16, s2.meta.ctypes.data, 16,
+                                      1.0, 1.0, 16, 1 << 30, 16, None)
+    assert rc == aqp.ERR_SCHEDULE_MISMATCH
