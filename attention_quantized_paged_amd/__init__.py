@@ -46,7 +46,7 @@ class AttnParams(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m attention_quantized_paged_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python attention_quantized_paged_amd/build.py` "
                           "(there is no fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t

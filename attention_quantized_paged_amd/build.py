@@ -1,7 +1,8 @@
 """Build libaqp.so (HIP for gfx950) in-tree with hipcc.
 
 Each source compiles to its own object in parallel, then one shared link.
-Run ``python -m attention_quantized_paged_amd.build``.
+Run ``python attention_quantized_paged_amd/build.py`` (the package refuses to import
+until the library exists, so the script is run by its path).
 """
 from __future__ import annotations
 
