@@ -41,7 +41,7 @@ class AttnParams(ctypes.Structure):
                 ("causal", ctypes.c_int32), ("window", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("sm_scale", ctypes.c_float), ("softcap", ctypes.c_float), ("decode_parallelism", ctypes.c_int32),
                 ("prefill_rows", ctypes.c_int32), ("causal_per_seq", ctypes.c_void_p), ("alibi_slopes", ctypes.c_void_p),
-                ("sinks", ctypes.c_void_p)]
+                ("sinks", ctypes.c_void_p), ("prefill_kv_split", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -115,12 +115,12 @@ def cache_desc(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: in
 def attn_params(num_q_heads: int, num_kv_heads: int, head_dim: int, max_blocks_per_seq: int, causal: bool = True,
                 window: int = 0, sm_scale: float = 0.0, softcap: float = 0.0,
                 decode_parallelism: int = 0, causal_per_seq=None, alibi_slopes=None, sinks=None,
-                prefill_rows: int = 0) -> AttnParams:
+                prefill_rows: int = 0, prefill_kv_split: int = 0) -> AttnParams:
     """causal_per_seq: host int sequence (one flag per sequence) or None; alibi_slopes, sinks:
     device float32 tensors of num_q_heads values (anything with ``data_ptr()``) or None. The
     returned object keeps them alive."""
     p = AttnParams(num_q_heads, num_kv_heads, head_dim, int(causal), window, max_blocks_per_seq, sm_scale,
-                   softcap, decode_parallelism, prefill_rows, None, None, None)
+                   softcap, decode_parallelism, prefill_rows, None, None, None, prefill_kv_split)
     keep = []
     if causal_per_seq is not None:
         cps = np.ascontiguousarray(np.asarray(causal_per_seq), dtype=np.int32)
@@ -177,7 +177,7 @@ _HDR_FIELDS = ("magic version dtype mode kv_elem_bytes staged_elem_bytes scale_b
                "tile_keys dec_iter_keys dec_waves pf_rows pf_kv_tile heads_per_unit dec_lds_bytes pf_lds_bytes "
                "num_dec_wgs num_dec_segs num_parts num_comb num_pf_items group_heads").split()
 _HDR_FIELDS64 = ("off_dec_segs off_dec_wg_start off_comb off_pf_items meta_bytes scratch_bytes page_bytes block_bytes "
-                 "dec_kv_keys off_seq_lens").split()
+                 "dec_kv_keys off_seq_lens num_slots comb_heads num_pf_split num_dec_comb").split()
 
 
 def parse_header(meta: np.ndarray) -> dict:

@@ -206,6 +206,7 @@ static int check_params(const aqp_attn_params& p, const aqp_cache_desc& d, const
   if (!(p.sm_scale >= 0.0f) || !std::isfinite(p.sm_scale)) { *why = "sm_scale must be finite and >= 0"; return AQP_ERR_INVALID; }
   if (!(p.softcap >= 0.0f) || !std::isfinite(p.softcap)) { *why = "softcap must be finite and >= 0"; return AQP_ERR_INVALID; }
   if (p.decode_parallelism < 0) { *why = "negative decode_parallelism"; return AQP_ERR_INVALID; }
+  if (p.prefill_kv_split < 0) { *why = "negative prefill_kv_split"; return AQP_ERR_INVALID; }
   if (p.prefill_rows != 0 && p.prefill_rows != kPfRows && p.prefill_rows != kPfRowsSmall) { *why = "prefill_rows must be 0, 64 or 128"; return AQP_ERR_INVALID; }
   return AQP_OK;
 }
@@ -304,7 +305,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
     for (size_t u = 0; u < units.size(); ++u) {
       if (unit_nseg[u] > 1) {
         unit_first_part[u] = num_parts;
-        comb.push_back({units[u].kvh, units[u].head0, units[u].nheads, units[u].q_tok, num_parts, unit_nseg[u], 0, 0});
+        comb.push_back({units[u].kvh, units[u].head0, units[u].nheads, units[u].q_tok, num_parts * hpu, unit_nseg[u], hpu, 0});
         num_parts += unit_nseg[u];
       }
     }
@@ -376,16 +377,72 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
       const int32_t khi = causal ? (L - ql + q1) : L;  // exclusive end of the last row's keys
       for (int32_t h = 0; h < p.num_kv_heads; ++h)
         for (int32_t h0 = 0; h0 < G; h0 += hpi)
-          pf.push_back({b, h, q0, q1, L, ql, qsl[b], khi, h0, std::min(hpi, G - h0), causal, 0});
+          pf.push_back({b, h, q0, q1, L, ql, qsl[b], khi, h0, std::min(hpi, G - h0), causal, 0, khi, -1, 0, 0});
+    }
+  }
+  // first key of an item's key loop: the 16-key tile holding its first query's window start (the
+  // prefill kernel starts its 32-key steps there)
+  auto key_begin = [&](const PfItem& it) {
+    const int32_t first = it.L - it.ql + it.q_lo;
+    const int32_t lo = (p.window > 0 && first - p.window + 1 > 0) ? first - p.window + 1 : 0;
+    return (lo / kTileKeys) * kTileKeys;
+  };
+  auto steps_of = [&](const PfItem& it) {
+    const int32_t kb = std::max(key_begin(it), it.split_lo), ke = std::min(it.k_hi_max, it.split_hi);
+    return ke > kb ? (ke - kb + kPfKvTile - 1) / kPfKvTile : 0;
+  };
+  // ---- prefill key splits: runs of whole 32-key steps; the rows of each run of a split item get
+  // partial-result slots after the decode parts' (num_parts x hpu) slots, and each query token of
+  // the item one merge item over its row in every run
+  const int64_t num_dec_comb = (int64_t)comb.size();
+  int64_t num_slots = (int64_t)num_parts * hpu;
+  int64_t num_pf_split = 0;
+  int32_t comb_heads = comb.empty() ? 0 : hpu;
+  {
+    int64_t total_steps = 0;
+    for (const PfItem& it : pf) total_steps += steps_of(it);
+    const int64_t cap = (int64_t)device_cu_count() * pf_wgs_per_cu(desc->head_dim, pf_rows, g.pf_lds_bytes);
+    // runs per item: its steps over the target run length (the batch's steps spread over the
+    // work-groups the device holds), rounded to nearest, each run at least min_steps long
+    int32_t max_runs = 1;
+    int64_t min_steps = kPfMinSplitSteps, target = 1;
+    if (p.prefill_kv_split > 1) {
+      max_runs = p.prefill_kv_split;
+      min_steps = 1;
+    } else if (p.prefill_kv_split == 0 && !pf.empty() && (int64_t)pf.size() < cap) {
+      max_runs = kPfMaxSplit;
+      target = std::max<int64_t>(1, (total_steps + cap - 1) / cap);
+    }
+    if (max_runs > 1) {
+      const size_t n0 = pf.size();
+      for (size_t i = 0; i < n0; ++i) {
+        const int32_t st = steps_of(pf[i]);
+        const int64_t want = (st + target / 2) / target;
+        const int32_t runs = (int32_t)std::max<int64_t>(1, std::min<int64_t>({(int64_t)max_runs, want, st / min_steps}));
+        if (runs < 2) continue;
+        const PfItem base = pf[i];
+        const int32_t kb = key_begin(base);
+        const int32_t rows = (base.q_hi - base.q_lo) * base.nheads;
+        const int64_t slot0 = num_slots;
+        for (int32_t r = 0; r < runs; ++r) {
+          PfItem it = base;
+          it.split_lo = kb + (int32_t)((int64_t)st * r / runs) * kPfKvTile;
+          it.split_hi = std::min(base.k_hi_max, kb + (int32_t)((int64_t)st * (r + 1) / runs) * kPfKvTile);
+          it.slot = (int32_t)(slot0 + (int64_t)r * rows);
+          if (r == 0) pf[i] = it; else pf.push_back(it);
+        }
+        for (int32_t t = base.q_lo; t < base.q_hi; ++t)
+          comb.push_back({base.kvh, base.head0, base.nheads, base.q_start + t,
+                          (int32_t)(slot0 + (int64_t)(t - base.q_lo) * base.nheads), runs, rows, 0});
+        comb_heads = std::max(comb_heads, base.nheads);
+        num_slots += (int64_t)runs * rows;
+        num_pf_split += runs;
+        if (num_slots > INT32_MAX / 2) return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: too many partial results");
+      }
     }
   }
   if (pf.size() > 1) std::stable_sort(pf.begin(), pf.end(), [&](const PfItem& x, const PfItem& y) {
-    auto work = [&](const PfItem& it) {
-      const int32_t first = it.L - it.ql + it.q_lo;
-      const int32_t lo = (p.window > 0 && first - p.window + 1 > 0) ? first - p.window + 1 : 0;
-      return (int64_t)it.k_hi_max - lo;
-    };
-    return work(x) > work(y);
+    return steps_of(x) > steps_of(y);
   });
 
   // ---- sizes and layout
@@ -401,7 +458,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   const int64_t off_sl = off;
   off = round_up(off + (int64_t)num_seqs * 4, 256);
   const int64_t need = off;
-  const int64_t scratch = (int64_t)num_parts * part_floats(hpu, desc->head_dim) * 4;
+  const int64_t scratch = num_slots * slot_floats(desc->head_dim) * 4;
   if (scratch_bytes) *scratch_bytes = (size_t)scratch;
   if (!meta_host) { *meta_bytes = (size_t)need; return AQP_OK; }
   if (*meta_bytes < (size_t)need) {
@@ -464,6 +521,10 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   h.block_bytes = g.block_bytes;
   h.dec_kv_keys = dec_keys;
   h.off_seq_lens = off_sl;
+  h.num_slots = num_slots;
+  h.comb_heads = comb_heads;
+  h.num_pf_split = num_pf_split;
+  h.num_dec_comb = num_dec_comb;
   std::memcpy(m, &h, sizeof h);
   if (!segs.empty()) std::memcpy(m + off_segs, segs.data(), segs.size() * sizeof(DecSeg));
   if (!wg_start.empty()) std::memcpy(m + off_wgs, wg_start.data(), wg_start.size() * sizeof(int32_t));
@@ -539,9 +600,16 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
   a.alibi_slopes = params->alibi_slopes;
   a.sinks = params->sinks;
   a.hdr = &h;
+  // decode, then the merge of its split ranges; the prefill runs' merge follows the prefill
+  const int32_t n_dec_comb = (int32_t)h.num_dec_comb, n_pf_comb = h.num_comb - n_dec_comb;
   auto run_decode = [&](void* st) -> int {
     int r = launch_decode(desc->dtype, desc->mode, a, st);
-    if (r == AQP_OK && h.num_comb > 0) r = launch_combine(a, st);
+    if (r == AQP_OK && n_dec_comb > 0) r = launch_combine(a, 0, n_dec_comb, st);
+    return r;
+  };
+  auto run_prefill = [&](void* st) -> int {
+    int r = launch_prefill(desc->dtype, desc->mode, a, st);
+    if (r == AQP_OK && n_pf_comb > 0) r = launch_combine(a, n_dec_comb, n_pf_comb, st);
     return r;
   };
   if (h.num_pf_items > 0 && h.num_dec_segs > 0) {
@@ -556,14 +624,14 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
       return fail(AQP_ERR_HIP, "aqp_paged_attention: fork to the side stream failed");
     rc = run_decode(ss->s);
     if (rc) return rc;
-    rc = launch_prefill(desc->dtype, desc->mode, a, stream);
+    rc = run_prefill(stream);
     if (rc) return rc;
     if (hipEventRecord(ss->join, ss->s) != hipSuccess || hipStreamWaitEvent(st, ss->join, 0) != hipSuccess)
       return fail(AQP_ERR_HIP, "aqp_paged_attention: join of the side stream failed");
     return AQP_OK;
   }
   if (h.num_pf_items > 0) {
-    rc = launch_prefill(desc->dtype, desc->mode, a, stream);
+    rc = run_prefill(stream);
     if (rc) return rc;
   }
   if (h.num_dec_segs > 0) {

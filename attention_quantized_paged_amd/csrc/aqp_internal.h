@@ -19,7 +19,7 @@
 namespace aqp {
 
 constexpr uint32_t kMagic = 0x53505141u;  // "AQPS"
-constexpr uint32_t kVersion = 3;
+constexpr uint32_t kVersion = 4;
 
 // ---- compile-time tile geometry of the kernels ----------------------------
 constexpr int kTileKeys = 16;        // keys per KV tile: one 16-row MFMA operand; block_size % 16 == 0
@@ -40,9 +40,22 @@ constexpr int kPfKvTile = 32;        // prefill: keys staged in LDS per step
 constexpr int kPfStages = 4;         // prefill: LDS ring stages of codes (two steps ahead of the widening)
 constexpr int kPfOperandBytes = 2;   // prefill: bf16 operand images in LDS
 constexpr int kMinRunTiles = 32;     // decode: fewest 16-key tiles a work-group is given
+// prefill key splits: when a batch has fewer prefill items than the device holds work-groups at
+// once, long items are cut into runs of at least this many kPfKvTile-key steps (at most
+// kPfMaxSplit runs each); the runs' partial results are merged like split decode ranges
+constexpr int kPfMinSplitSteps = 8;
+constexpr int kPfMaxSplit = 8;
 constexpr int kCwRowsPerLane = 4;    // cache write: rows each lane loads before converting
 constexpr int kCwWgsPerCu = 16;      // cache write: resident work-groups per CU (grid cap)
 constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per compute unit (gfx950)
+// Prefill work-groups a CU holds at once: the register limit of the compiled kernel (8 waves at two
+// per SIMD at head_dim 256; 4 waves at two per SIMD at 128 rows and head_dim 128, three below)
+// and the LDS limit.
+constexpr int pf_wgs_per_cu(int head_dim, int rows, int32_t lds_bytes) {
+  return (head_dim >= 256 ? 1 : (head_dim == 128 && rows > kPfRowsSmall ? 2 : 3)) < kLdsPerCu / lds_bytes
+             ? (head_dim >= 256 ? 1 : (head_dim == 128 && rows > kPfRowsSmall ? 2 : 3))
+             : kLdsPerCu / lds_bytes;
+}
 // fp32 scales stored per cache row: none per tensor, one per token-head, head_dim / 32 per group
 constexpr int row_scales(int head_dim, int mode) {
   return mode == AQP_SCALE_PER_TOKEN_HEAD ? 1 : (mode == AQP_SCALE_PER_GROUP ? head_dim / AQP_SCALE_GROUP : 0);
@@ -127,10 +140,16 @@ struct SchedHeader {
   int64_t page_bytes, block_bytes;
   int64_t dec_kv_keys;  // total visible (key, KV head) pairs of the decode work (for reporting)
   int64_t off_seq_lens;  // keys of each sequence (the decode query of sequence b sits at seq_lens[b] - 1)
+  // partial-result slots of the scratch: decode parts (num_parts x group_heads rows), then the
+  // rows of split prefill runs; O of slot s at float s * head_dim, (m, l) at num_slots * head_dim + 2 s
+  int64_t num_slots;
+  int64_t comb_heads;    // most heads of one merge item (the merge grid's second dimension)
+  int64_t num_pf_split;  // prefill runs that write partial results
+  int64_t num_dec_comb;  // merge items [0, num_dec_comb) merge decode parts, the rest prefill runs
 };
 
 static_assert(offsetof(SchedHeader, off_dec_segs) == 136, "SchedHeader layout is part of the metadata format");
-static_assert(sizeof(SchedHeader) == 216, "SchedHeader layout is part of the metadata format");
+static_assert(sizeof(SchedHeader) == 248, "SchedHeader layout is part of the metadata format");
 
 // Decode segment: keys [k_lo, k_hi) of (sequence, KV head, q heads
 // [head0, head0 + nheads) of that KV head's group), one query token.
@@ -140,10 +159,11 @@ struct DecSeg {
   int32_t seq, kvh, head0, nheads, k_lo, k_hi, q_tok, part;
 };
 
-// Merge of partial slots [first_part, first_part + num_parts) into the output
-// rows of q heads [head0, head0 + nheads) of KV head kvh, query token q_tok.
+// Merge of num_parts partial results into the output rows of q heads [head0, head0 + nheads)
+// of KV head kvh, query token q_tok: part s of head h is slot first_slot + s * part_stride + h
+// (a split decode unit: its parts' slots; a split prefill run: the token's row in each run).
 struct CombItem {
-  int32_t kvh, head0, nheads, q_tok, first_part, num_parts, pad0, pad1;
+  int32_t kvh, head0, nheads, q_tok, first_slot, num_parts, part_stride, pad0;
 };
 
 // Prefill item: query tokens [q_lo, q_hi) (indices within the sequence) of
@@ -151,14 +171,15 @@ struct CombItem {
 // queries; its first query is token q_start of q / out.
 // Prefill item: query tokens [q_lo, q_hi) of sequence seq times q heads [head0, head0 + nheads)
 // of KV head kvh; row r is token q_lo + r / nheads, head head0 + r % nheads.
+// Keys outside [split_lo, split_hi) are not this item's (a run of a split item); slot >= 0: the
+// item writes row r's partial result (O, m, l) to slot `slot + r` instead of the output.
 struct PfItem {
-  int32_t seq, kvh, q_lo, q_hi, L, ql, q_start, k_hi_max, head0, nheads, causal, pad1;
+  int32_t seq, kvh, q_lo, q_hi, L, ql, q_start, k_hi_max, head0, nheads, causal, split_lo;
+  int32_t split_hi, slot, pad0, pad1;
 };
 
-// Scratch of a partial slot: nh = min(G, 16) heads x (D floats of O, then m, l).
-inline int64_t part_floats(int32_t group_heads, int32_t head_dim) {
-  return (int64_t)group_heads * (head_dim + 2);
-}
+// Scratch of one partial-result slot (one query row): D floats of O, then m and l.
+inline int64_t slot_floats(int32_t head_dim) { return (int64_t)head_dim + 2; }
 
 // ---- kernel launchers (defined in the .hip files) ---------------------------
 struct CacheWriteArgs {
@@ -190,7 +211,8 @@ struct AttnArgs {
   const SchedHeader* hdr;  // host copy
 };
 int launch_decode(int dtype, int mode, const AttnArgs& a, void* stream);
-int launch_combine(const AttnArgs& a, void* stream);
+// merges items [first, first + count) of the schedule's merge items (one wave per (item, head))
+int launch_combine(const AttnArgs& a, int32_t first, int32_t count, void* stream);
 int launch_prefill(int dtype, int mode, const AttnArgs& a, void* stream);
 
 void set_error(const char* fmt, ...);

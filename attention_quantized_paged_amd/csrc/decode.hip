@@ -46,7 +46,8 @@ struct DecArgs {
   float* scratch;
   uint16_t* out;
   int64_t page_bytes, block_bytes;
-  int32_t block_size, num_kv_heads, num_q_heads, group, max_blocks, group_heads, num_blocks, num_parts;
+  int32_t block_size, num_kv_heads, num_q_heads, group, max_blocks, group_heads, num_blocks;
+  int64_t num_slots;  // partial-result slots of the scratch ((m, l) follow all slots' O)
   float logit_scale;  // sm_scale * k_scale (per tensor) or sm_scale (per token-head)
   float softcap, inv_softcap;
   float v_scale;      // per tensor; 1 per token-head
@@ -124,14 +125,14 @@ __device__ __forceinline__ void merge_store(const DecArgs& a, const float* mg, i
       *(uint2*)(op + t * 16 + 4 * kg) = w;
     }
   } else {
-    // partial slot: O at [part][head][D], (m, l) at [part][head][2] after all O slots
+    // partial slot part * group_heads + head: O at [slot][D], (m, l) at [slot][2] after all O slots
     float* pp = a.scratch + ((int64_t)sg.part * a.group_heads + r16) * D;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
       *(float4*)(pp + t * 16 + 4 * kg) = make_float4(o[t][0] * a.v_scale, o[t][1] * a.v_scale, o[t][2] * a.v_scale,
                                                      o[t][3] * a.v_scale);
     if (kg == 0) {
-      float* ml = a.scratch + (int64_t)a.num_parts * a.group_heads * D + ((int64_t)sg.part * a.group_heads + r16) * 2;
+      float* ml = a.scratch + a.num_slots * D + ((int64_t)sg.part * a.group_heads + r16) * 2;
       ml[0] = M;
       ml[1] = L;
     }
@@ -515,19 +516,19 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
   wait_vmcnt(0);
 }
 
-// Split-KV merge: one wave per (item, head). M = max_s m_s;
-// O = sum_s 2^(m_s - M) O_s / (sum_s 2^(m_s - M) l_s [+ 2^(sink - M)]).
+// Merge of partial results (split decode ranges, split prefill runs): one wave per (item, head).
+// M = max_s m_s; O = sum_s 2^(m_s - M) O_s / (sum_s 2^(m_s - M) l_s [+ 2^(sink - M)]).
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(const CombItem* items, const float* scratch, uint16_t* out,
-                                                     int32_t num_q_heads, int32_t group, int32_t group_heads,
-                                                     int32_t num_parts, const float* sinks) {
+                                                     int32_t num_q_heads, int32_t group, int64_t num_slots,
+                                                     const float* sinks) {
   const CombItem it = load_const(as_const(items) + blockIdx.x);
   const int h = blockIdx.y;
   if (h >= it.nheads) return;
   const int lane = threadIdx.x;
   const int P = it.num_parts;
-  const float* ml = scratch + (int64_t)num_parts * group_heads * D;
-  auto slot = [&](int s) { return (int64_t)(it.first_part + s) * group_heads + h; };
+  const float* ml = scratch + num_slots * D;
+  auto slot = [&](int s) { return (int64_t)it.first_slot + (int64_t)s * it.part_stride + h; };
   // (m, l) of the parts: lane s takes parts s, s + 64, ..., so their loads are all in flight at once
   float M = -INFINITY;
   for (int s = lane; s < P; s += 64) M = fmaxf(M, ml[slot(s) * 2]);
@@ -601,7 +602,7 @@ static int launch_dec(const AttnArgs& a, hipStream_t st) {
   d.max_blocks = a.max_blocks_per_seq;
   d.group_heads = h.group_heads;
   d.num_blocks = h.num_blocks;
-  d.num_parts = h.num_parts;
+  d.num_slots = h.num_slots;
   d.logit_scale = MODE == AQP_SCALE_PER_TENSOR ? a.sm_scale * a.k_scale : a.sm_scale;
   d.softcap = a.softcap;
   d.inv_softcap = a.softcap > 0.0f ? 1.0f / a.softcap : 0.0f;
@@ -651,15 +652,15 @@ int launch_decode(int dtype, int mode, const AttnArgs& a, void* stream) {
   return AQP_ERR_UNSUPPORTED;
 }
 
-int launch_combine(const AttnArgs& a, void* stream) {
+int launch_combine(const AttnArgs& a, int32_t first, int32_t count, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const SchedHeader& h = *a.hdr;
-  const CombItem* items = (const CombItem*)(a.meta_dev + h.off_comb);
-  dim3 grid(h.num_comb, h.group_heads);
+  const CombItem* items = (const CombItem*)(a.meta_dev + h.off_comb) + first;
+  dim3 grid(count, (uint32_t)h.comb_heads);
   switch (a.head_dim) {
-    case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(64), 0, st, items, a.scratch, a.out, a.num_q_heads, a.group, h.group_heads, h.num_parts, a.sinks); break;
-    case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(64), 0, st, items, a.scratch, a.out, a.num_q_heads, a.group, h.group_heads, h.num_parts, a.sinks); break;
-    case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(64), 0, st, items, a.scratch, a.out, a.num_q_heads, a.group, h.group_heads, h.num_parts, a.sinks); break;
+    case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(64), 0, st, items, a.scratch, a.out, a.num_q_heads, a.group, h.num_slots, a.sinks); break;
+    case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(64), 0, st, items, a.scratch, a.out, a.num_q_heads, a.group, h.num_slots, a.sinks); break;
+    case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(64), 0, st, items, a.scratch, a.out, a.num_q_heads, a.group, h.num_slots, a.sinks); break;
     default: set_error("aqp_paged_attention: unsupported head_dim"); return AQP_ERR_UNSUPPORTED;
   }
   hipError_t e = hipGetLastError();

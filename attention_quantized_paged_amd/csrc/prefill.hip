@@ -32,6 +32,8 @@ struct PfArgs {
   const int32_t* block_tables;
   const PfItem* items;
   uint16_t* out;
+  float* scratch;     // partial results of split items: O of slot s at s * D, (m, l) at num_slots * D + 2 s
+  int64_t num_slots;
   int64_t page_bytes, block_bytes;
   int32_t block_size, num_kv_heads, num_q_heads, group, max_blocks, num_blocks;
   int32_t window;
@@ -125,6 +127,9 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
     slope_r[rt] = a.alibi ? a.alibi[hq] * kLog2e : 0.0f;
     sink_r[rt] = a.sinks ? a.sinks[hq] * kLog2e : -INFINITY;
     lo_r[rt] = (a.window > 0 && p - a.window + 1 > 0) ? p - a.window + 1 : 0;
+    // a run of a split item sees only its own keys
+    lo_r[rt] = max(lo_r[rt], it.split_lo);
+    hi_r[rt] = min(hi_r[rt], it.split_hi);
     if (!row_ok[rt]) { lo_r[rt] = 0; hi_r[rt] = 0; }
     orow[rt] = ((int64_t)(it.q_start + t) * a.num_q_heads + it.kvh * G + g) * D;
     // (per group: depth 32*st + 8*kg + 0..7, so that MFMA step st covers scale group st)
@@ -141,13 +146,13 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   const int tw1 = min(ntok - 1, (wave * RPW + RPW - 1) / nh);
   const bool wave_rows_full = (wave * RPW + RPW - 1) / nh < ntok;
   const int pw0 = it.L - it.ql + it.q_lo + tw0, pw1 = it.L - it.ql + it.q_lo + tw1;
-  const int vis_hi = it.causal ? pw0 + 1 : it.L;
-  const int vis_lo = (a.window > 0 && pw1 - a.window + 1 > 0) ? pw1 - a.window + 1 : 0;
+  const int vis_hi = min(it.causal ? pw0 + 1 : it.L, it.split_hi);
+  const int vis_lo = max((a.window > 0 && pw1 - a.window + 1 > 0) ? pw1 - a.window + 1 : 0, it.split_lo);
   // ---- key range of the whole item: first token's window start .. last token's end
   const int p_first = it.L - it.ql + it.q_lo;
   const int k_first = (a.window > 0 && p_first - a.window + 1 > 0) ? p_first - a.window + 1 : 0;
-  const int k_begin = (k_first / kTileKeys) * kTileKeys;
-  const int k_end = it.k_hi_max;
+  const int k_begin = max((k_first / kTileKeys) * kTileKeys, it.split_lo);  // (split_lo: a step boundary)
+  const int k_end = min(it.k_hi_max, it.split_hi);
   const int n_steps = (k_end - k_begin + KT - 1) / KT;
   const float xscale = CAP ? a.logit_scale : a.logit_scale * kLog2e;
   const int last_tile = ((it.L - 1) / kTileKeys) * kTileKeys;  // first key of the tile holding key L-1
@@ -517,11 +522,25 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       for (int rt = 0; rt < RT; ++rt) s_cur[kt][rt] = s_next[kt][rt];
   }
 
-  // ---- normalise and write the rows
+  // ---- normalise and write the rows (a run of a split item: its partial results instead)
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     float lt = sum_over_rows(l[rt]);
     if (!row_ok[rt]) continue;
+    if (it.slot >= 0) {
+      const int64_t slot = (int64_t)it.slot + wave * RPW + rt * 16 + r16;
+      float* pp = a.scratch + slot * D;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        *(float4*)(pp + t * 16 + 4 * kg) = make_float4(acc[rt][t][0] * a.v_scale, acc[rt][t][1] * a.v_scale,
+                                                       acc[rt][t][2] * a.v_scale, acc[rt][t][3] * a.v_scale);
+      if (kg == 0) {
+        float* ml = a.scratch + a.num_slots * D + slot * 2;
+        ml[0] = m[rt];
+        ml[1] = lt;
+      }
+      continue;
+    }
     float f = 1.0f;
     if (a.sinks) {
       // the sink logit joins the normaliser: rescale to the larger of it and the row's reference
@@ -550,6 +569,8 @@ static int launch_pf(const AttnArgs& a, hipStream_t st) {
   p.block_tables = a.block_tables;
   p.items = (const PfItem*)(a.meta_dev + h.off_pf_items);
   p.out = a.out;
+  p.scratch = a.scratch;
+  p.num_slots = h.num_slots;
   p.page_bytes = a.page_bytes;
   p.block_bytes = a.block_bytes;
   p.block_size = a.block_size;

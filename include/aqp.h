@@ -119,6 +119,13 @@ typedef struct {
   const float* sinks;         /* device fp32 [num_q_heads], or NULL: one more logit per q head in the
                                  softmax with no value row (it only enlarges the normaliser). Read
                                  by aqp_paged_attention. */
+  int32_t prefill_kv_split;   /* key-range split of prefill work items ([P50194] Code excerpt:
+                                 enable_kv_split): 0 = automatic (when the batch has fewer prefill
+                                 items than the device runs at once, long items are cut into runs of
+                                 at least 8 key steps of 32 keys, at most 8 runs, sized so the runs
+                                 fill the device); 1 = never; n > 1 = every item with enough keys is
+                                 cut into up to n runs. The runs' partial results are merged into
+                                 the output like split decode ranges. */
 } aqp_attn_params;
 
 /* Parse a kv_cache_dtype string ([P50194] Code excerpt: parse_fp8_kv_dtype
@@ -196,7 +203,8 @@ int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_desc* desc, 
  *   block_tables: int32 [num_seqs, max_blocks_per_seq]: physical block of each logical block.
  *   meta_host / meta_dev: the same schedule bytes, in host and device memory.
  *   k_scale, v_scale: per-tensor mode only.
- *   scratch:      device buffer of at least the schedule's scratch_bytes (may be NULL if 0).
+ *   scratch:      device buffer of at least the schedule's scratch_bytes (may be NULL if 0): the
+ *                 partial results of split decode ranges and split prefill items.
  *   out:          bf16 [T_q, Hq, head_dim]; every row of every query token is written.
  * Per query row: z_j = sm_scale * q . k_j (k_j dequantised), soft-capped if
  * set, masked by causality and window; softmax over the visible keys; output

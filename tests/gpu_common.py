@@ -63,7 +63,7 @@ class Run:
     """One workload through both paths."""
 
     def __init__(self, w, torch, aqp, two_call_write=True, fill=0, par=0, alibi=None, sinks=None,
-                 causal_per_seq=None, prefill_rows=0):
+                 causal_per_seq=None, prefill_rows=0, prefill_kv_split=0):
         """alibi, sinks: float32 numpy arrays of one value per q head (or None); causal_per_seq:
         one flag per sequence (or None)."""
         self.w, self.torch, self.aqp = w, torch, aqp
@@ -95,7 +95,7 @@ class Run:
         self.params = aqp.attn_params(w.num_q_heads, w.num_kv_heads, w.head_dim, mb, causal=w.causal,
                                       window=w.window, softcap=w.softcap, decode_parallelism=par,
                                       causal_per_seq=causal_per_seq, alibi_slopes=dev32(alibi), sinks=dev32(sinks),
-                                      prefill_rows=prefill_rows)
+                                      prefill_rows=prefill_rows, prefill_kv_split=prefill_kv_split)
 
     def cache_matches(self):
         g = self.gcache.cpu().numpy()

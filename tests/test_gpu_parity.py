@@ -161,6 +161,34 @@ def test_prefill_rows_per_item(aqp, w, rows):
     compare(out[rows_idx], ref, f"{w.name} rows={rows}")
 
 
+@pytest.mark.parametrize("split", [1, 2, 5])
+@pytest.mark.parametrize("w", ROWS_CASES, ids=[w.name for w in ROWS_CASES])
+def test_prefill_kv_split(aqp, w, split):
+    """Prefill items cut into key runs (enable_kv_split of the scratch-sizing page's scheduler):
+    the runs' partial results merged into the output match the oracle, whole items too."""
+    r = Run(w, torch, aqp, prefill_kv_split=split)
+    out = r.gpu_attention(calls=2)
+    h = r.sched.header
+    if split == 1:
+        assert h["num_pf_split"] == 0  # (an item of a single 32-key step is never cut)
+    assert np.array_equal(r.meta_after, r.sched.meta)
+    ref, rows = r.oracle_attention()
+    compare(out[rows], ref, f"{w.name} split={split}")
+
+
+def test_prefill_kv_split_alibi_sinks(aqp):
+    """Split prefill runs with ALiBi slopes and sink logits (the merge adds the sink once)."""
+    w = W.Workload("split_alibi_sinks_mixed", "fp8_per_token_head", ((1, 90), (70, 300), (1, 33), (24, 24)), 8, 2,
+                   128, 16, 40, window=150, softcap=30.0, seed=131)
+    rng = np.random.default_rng(w.seed)
+    r = Run(w, torch, aqp, alibi=_alibi_slopes(w.num_q_heads),
+            sinks=(rng.standard_normal(w.num_q_heads) * 2.0).astype(np.float32), prefill_kv_split=4)
+    out = r.gpu_attention()
+    assert r.sched.header["num_pf_split"] > 0
+    ref, rows = r.oracle_attention()
+    compare(out[rows], ref, w.name)
+
+
 @pytest.mark.parametrize("par", [1, 3, 64, 4096])
 def test_decode_split_counts(aqp, par):
     """The same decode batch cut into 1 .. many work-groups gives the same result."""

@@ -12,8 +12,9 @@ import attention_quantized_paged_amd as aqp
 import workloads
 
 SEG = np.dtype([(n, "<i4") for n in "seq kvh head0 nheads k_lo k_hi q_tok part".split()])
-COMB = np.dtype([(n, "<i4") for n in "kvh head0 nheads q_tok first_part num_parts pad0 pad1".split()])
-PF = np.dtype([(n, "<i4") for n in "seq kvh q_lo q_hi L ql q_start k_hi_max head0 nheads causal pad1".split()])
+COMB = np.dtype([(n, "<i4") for n in "kvh head0 nheads q_tok first_slot num_parts part_stride pad0".split()])
+PF = np.dtype([(n, "<i4") for n in ("seq kvh q_lo q_hi L ql q_start k_hi_max head0 nheads causal split_lo split_hi slot "
+                                   "pad0 pad1").split()])
 
 
 def h_rows(s):
@@ -24,17 +25,18 @@ def _arrays(s):
     h, m = s.header, s.meta
     segs = m[h["off_dec_segs"]: h["off_dec_segs"] + 32 * h["num_dec_segs"]].view(SEG)
     wgs = m[h["off_dec_wg_start"]: h["off_dec_wg_start"] + 4 * (h["num_dec_wgs"] + 1)].view(np.int32)
-    comb = m[h["off_comb"]: h["off_comb"] + 32 * h["num_comb"]].view(COMB)
+    comb = m[h["off_comb"]: h["off_comb"] + COMB.itemsize * h["num_comb"]].view(COMB)
     pf = m[h["off_pf_items"]: h["off_pf_items"] + PF.itemsize * h["num_pf_items"]].view(PF)
     return segs, wgs, comb, pf
 
 
-def _sched(seqs, hq, hkv, d, bs, dtype="fp8_e4m3", window=0, causal=True, par=0, nb=None, rows=0):
+def _sched(seqs, hq, hkv, d, bs, dtype="fp8_e4m3", window=0, causal=True, par=0, nb=None, rows=0, split=0):
     sl = np.array([L for _, L in seqs], np.int32)
     qsl = np.concatenate([[0], np.cumsum([q for q, _ in seqs])]).astype(np.int32)
     mb = int(max(1, max((L + bs - 1) // bs for L in sl)))
     desc = aqp.cache_desc(nb or 4 * mb * len(seqs), bs, hkv, d, dtype)
-    params = aqp.attn_params(hq, hkv, d, mb, causal=causal, window=window, decode_parallelism=par, prefill_rows=rows)
+    params = aqp.attn_params(hq, hkv, d, mb, causal=causal, window=window, decode_parallelism=par, prefill_rows=rows,
+                             prefill_kv_split=split)
     return aqp.get_schedule(params, desc, sl, qsl), sl, qsl, params, desc
 
 
@@ -84,9 +86,15 @@ def test_decode_coverage_exact(seqs, hq, hkv, d, bs, window, par):
     # partial slots: each used exactly once and named by exactly one merge item
     parts = sorted(sg["part"] for sg in segs if sg["part"] >= 0)
     assert parts == list(range(h["num_parts"]))
-    from_comb = sorted(p for c in comb for p in range(c["first_part"], c["first_part"] + c["num_parts"]))
+    gh = min(G, 16 if d <= 128 else 8)
+    dcomb = comb[: h["num_dec_comb"]]
+    assert np.all(dcomb["part_stride"] == gh) and np.all(dcomb["first_slot"] % gh == 0)
+    from_comb = sorted(p for c in dcomb for p in range(c["first_slot"] // gh, c["first_slot"] // gh + c["num_parts"]))
     assert from_comb == parts
-    assert h["scratch_bytes"] == h["num_parts"] * min(G, 16 if d <= 128 else 8) * (d + 2) * 4 == s.scratch_bytes
+    # decode parts own the first num_parts x gh slots; split prefill runs the rest
+    pf_slots = sum((it["q_hi"] - it["q_lo"]) * it["nheads"] for it in pf if it["slot"] >= 0)
+    assert h["num_slots"] == h["num_parts"] * gh + pf_slots
+    assert h["scratch_bytes"] == h["num_slots"] * (d + 2) * 4 == s.scratch_bytes
     # balance: work-groups get equal numbers of 16-key tiles (the last may get fewer)
     if len(segs):
         tiles = []
@@ -99,36 +107,104 @@ def test_decode_coverage_exact(seqs, hq, hkv, d, bs, window, par):
         assert len(set(tiles[:-1])) <= 1 and tiles[-1] <= tiles[0]
 
 
+def _key_begin(it, window):
+    first = it["L"] - it["ql"] + it["q_lo"]
+    lo = max(0, first - window + 1) if window else 0
+    return lo // 16 * 16
+
+
+def _steps(it, window):
+    kb, ke = max(_key_begin(it, window), it["split_lo"]), min(it["k_hi_max"], it["split_hi"])
+    return max(0, -(-(ke - kb) // 32))
+
+
+@pytest.mark.parametrize("split", [0, 1, 3])
 @pytest.mark.parametrize("rows", [0, 64, 128])
 @pytest.mark.parametrize("seqs,hq,hkv,d,bs,window,par", CASES)
-def test_prefill_coverage_and_order(seqs, hq, hkv, d, bs, window, par, rows):
+def test_prefill_coverage_and_order(seqs, hq, hkv, d, bs, window, par, rows, split):
+    """Every (query token, q head) of every prefill sequence is in exactly one item; a split item's
+    runs tile its key range in whole 32-key steps, own consecutive blocks of partial-result slots
+    and have one merge item per query token; items run heaviest first."""
     if rows == 64 and d > 128:
         with pytest.raises(aqp.AqpError) as e:
-            _sched(seqs, hq, hkv, d, bs, window=window, par=par, rows=rows)
+            _sched(seqs, hq, hkv, d, bs, window=window, par=par, rows=rows, split=split)
         assert e.value.status == aqp.ERR_UNSUPPORTED
         return
-    s, sl, qsl, params, desc = _sched(seqs, hq, hkv, d, bs, window=window, par=par, rows=rows)
+    s, sl, qsl, params, desc = _sched(seqs, hq, hkv, d, bs, window=window, par=par, rows=rows, split=split)
+    h = s.header
     if rows:
         assert h_rows(s) == rows
-    _, _, _, pf = _arrays(s)
+    _, _, comb, pf = _arrays(s)
     G = hq // hkv
-    seen = {}
+    gh = min(G, 16 if d <= 128 else 8)
+    families = {}
     for it in pf:
         assert 0 <= it["q_lo"] < it["q_hi"] <= it["ql"]
         assert 0 <= it["head0"] < it["head0"] + it["nheads"] <= G
         assert (it["q_hi"] - it["q_lo"]) * it["nheads"] <= h_rows(s)
-        for t in range(it["q_lo"], it["q_hi"]):
-            for hh in range(it["head0"], it["head0"] + it["nheads"]):
-                key = (it["seq"], it["kvh"], t, hh)
-                assert key not in seen
-                seen[key] = 1
         assert it["k_hi_max"] == it["L"] - it["ql"] + it["q_hi"]
         assert it["causal"] == 1
+        families.setdefault((it["seq"], it["kvh"], it["q_lo"], it["head0"]), []).append(it)
+    seen = {}
+    pf_comb = comb[h["num_dec_comb"]:]
+    comb_by_first = {int(c["first_slot"]): c for c in pf_comb}
+    next_slot = h["num_parts"] * gh
+    n_split = 0
+    for key, runs in families.items():
+        it0 = runs[0]
+        for t in range(it0["q_lo"], it0["q_hi"]):
+            for hh in range(it0["head0"], it0["head0"] + it0["nheads"]):
+                k2 = (it0["seq"], it0["kvh"], t, hh)
+                assert k2 not in seen
+                seen[k2] = 1
+        if len(runs) == 1:
+            assert it0["slot"] == -1 and it0["split_lo"] == 0 and it0["split_hi"] == it0["k_hi_max"]
+            continue
+        assert split != 1
+        runs = sorted(runs, key=lambda r: r["split_lo"])
+        nrows = (it0["q_hi"] - it0["q_lo"]) * it0["nheads"]
+        assert runs[0]["split_lo"] == _key_begin(it0, window) and runs[-1]["split_hi"] == it0["k_hi_max"]
+        for a, b in zip(runs, runs[1:]):
+            assert a["split_hi"] == b["split_lo"] and (b["split_lo"] - runs[0]["split_lo"]) % 32 == 0
+        assert all(_steps(r, window) >= 1 for r in runs)
+        slot0 = runs[0]["slot"]
+        assert [r["slot"] for r in runs] == [slot0 + i * nrows for i in range(len(runs))]
+        assert slot0 >= h["num_parts"] * gh
+        for t in range(it0["q_lo"], it0["q_hi"]):
+            c = comb_by_first[slot0 + (t - it0["q_lo"]) * it0["nheads"]]
+            assert (c["kvh"], c["head0"], c["nheads"], c["q_tok"]) == (it0["kvh"], it0["head0"], it0["nheads"],
+                                                                      it0["q_start"] + t)
+            assert c["num_parts"] == len(runs) and c["part_stride"] == nrows
+        n_split += len(runs)
+        next_slot = max(next_slot, slot0 + len(runs) * nrows)
+    assert len(pf_comb) == sum(r[0]["q_hi"] - r[0]["q_lo"] for r in families.values() if len(r) > 1)
+    assert h["num_pf_split"] == n_split and h["num_slots"] == next_slot
     expect = {(b, k, t, hh) for b, (ql, L) in enumerate(seqs) if ql > 1 for k in range(hkv) for t in range(ql)
               for hh in range(G)}
     assert set(seen) == expect
-    work = [it["k_hi_max"] - (max(0, it["L"] - it["ql"] + it["q_lo"] - window + 1) if window else 0) for it in pf]
+    work = [_steps(it, window) for it in pf]
     assert work == sorted(work, reverse=True)
+
+
+def test_prefill_split_policy():
+    """Automatic key splits only when the batch's prefill items number fewer than the work-groups
+    the device holds at once (256 CUs without a device): the mixed batch's 256 items of 128 rows at
+    head_dim 128 (two per CU) become 512 runs; the large prefill (512 items, one per CU) and a
+    batch with enough items stay whole; 1 turns splitting off; n splits into at most n runs."""
+    w4 = workloads.CFG4
+    s, *_ = _sched(w4.seqs, 32, 8, 128, 16)
+    h = s.header
+    assert h["num_pf_items"] == 512 and h["num_pf_split"] == 512
+    assert h["comb_heads"] == 4 and h["num_comb"] - h["num_dec_comb"] == 256 * 32  # one per query token
+    assert _sched(w4.seqs, 32, 8, 128, 16, split=1)[0].header["num_pf_split"] == 0
+    s, *_ = _sched(workloads.CFG2.seqs, 16, 2, 256, 2176)
+    assert s.header["num_pf_split"] == 0 and s.header["num_pf_items"] == 512
+    many = ((1024, 1024),) * 4  # 1024 items of 128 rows
+    assert _sched(many, 32, 8, 128, 16)[0].header["num_pf_split"] == 0
+    s, *_ = _sched(((100, 300),), 8, 2, 128, 16, split=4)
+    _, _, _, pf = _arrays(s)
+    assert 1 < len(pf) and all(it["slot"] >= 0 for it in pf)
+    assert max(sum(1 for x in pf if (x["kvh"], x["q_lo"]) == (it["kvh"], it["q_lo"])) for it in pf) <= 4
 
 
 def test_schedule_records_element_sizes_and_is_checked():
