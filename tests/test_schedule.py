@@ -54,11 +54,19 @@ CASES = [
 
 @pytest.mark.parametrize("seqs,hq,hkv,d,bs,window,par", CASES)
 def test_decode_coverage_exact(seqs, hq, hkv, d, bs, window, par):
-    s, sl, qsl, params, desc = _sched(seqs, hq, hkv, d, bs, window=window, par=par)
+    _check_decode(seqs, hq, hkv, d, bs, window, par)
+
+
+def _check_decode(seqs, hq, hkv, d, bs, window, par, split=0):
+    s, sl, qsl, params, desc = _sched(seqs, hq, hkv, d, bs, window=window, par=par, split=split)
     h = s.header
     segs, wgs, comb, pf = _arrays(s)
     G = hq // hkv
     assert h["kv_elem_bytes"] == 1 and h["head_dim"] == d and h["block_size"] == bs
+    if h["num_dec_wgs"] == 0:
+        # no decode work: no segments, no work-group ranges, no parts (nothing is launched)
+        assert len(segs) == 0 and h["num_parts"] == 0 and h["num_dec_comb"] == 0
+        wgs = np.zeros(1, np.int32)
     assert wgs[0] == 0 and wgs[-1] == len(segs) and np.all(np.diff(wgs) >= 0)
     # coverage: for each decode (seq, kvh, head) the union of segment ranges is the visible range, disjoint
     cover = {}
@@ -125,6 +133,10 @@ def test_prefill_coverage_and_order(seqs, hq, hkv, d, bs, window, par, rows, spl
     """Every (query token, q head) of every prefill sequence is in exactly one item; a split item's
     runs tile its key range in whole 32-key steps, own consecutive blocks of partial-result slots
     and have one merge item per query token; items run heaviest first."""
+    _check_prefill(seqs, hq, hkv, d, bs, window, par, rows, split)
+
+
+def _check_prefill(seqs, hq, hkv, d, bs, window, par, rows, split):
     if rows == 64 and d > 128:
         with pytest.raises(aqp.AqpError) as e:
             _sched(seqs, hq, hkv, d, bs, window=window, par=par, rows=rows, split=split)
@@ -353,3 +365,37 @@ def test_per_group_geometry_and_mismatch(d, bs):
     rc = aqp._lib.aqp_paged_attention(ctypes.byref(params), ctypes.byref(desc), 16, 16, 16, s2.meta.ctypes.data, 16,
                                       1.0, 1.0, 16, 1 << 30, 16, None)
     assert rc == aqp.ERR_SCHEDULE_MISMATCH
+
+
+# ---- randomized batches: the same invariants over shapes no table lists
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@st.composite
+def _batches(draw):
+    d = draw(st.sampled_from([64, 128, 256]))
+    bs = draw(st.sampled_from([16, 32, 48, 2176] if d == 256 else [16, 32, 48, 64]))
+    hkv = draw(st.integers(1, 4))
+    g = draw(st.sampled_from([1, 2, 3, 4, 8, 16, 24, 40]))
+    n = draw(st.integers(1, 6))
+    seqs = []
+    for _ in range(n):
+        L = draw(st.integers(1, 3000))
+        kind = draw(st.sampled_from(["decode", "prefill", "chunk", "empty"]))
+        ql = {"decode": 1, "prefill": L, "chunk": draw(st.integers(1, L)), "empty": 0}[kind]
+        seqs.append((ql, L))
+    window = draw(st.sampled_from([0, 0, 1, 17, 300]))
+    par = draw(st.sampled_from([0, 1, 7, 100]))
+    rows = draw(st.sampled_from([0, 128] if d > 128 else [0, 64, 128]))
+    split = draw(st.sampled_from([0, 1, 2, 5]))
+    return tuple(seqs), g * hkv, hkv, d, bs, window, par, rows, split
+
+
+@settings(max_examples=150, deadline=None, derandomize=True)
+@given(_batches())
+def test_schedule_invariants_random_batches(batch):
+    """Decode coverage, partial slots and balance; prefill coverage, key runs, slots, merge items
+    and order: on random mixes of decode, prefill, chunked-prefill and empty sequences."""
+    seqs, hq, hkv, d, bs, window, par, rows, split = batch
+    _check_decode(seqs, hq, hkv, d, bs, window, par, split=split)
+    _check_prefill(seqs, hq, hkv, d, bs, window, par, rows, split)
