@@ -18,6 +18,9 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libaqp.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 SOURCES = ["aqp_host.cpp", "cache_write.hip", "decode.hip", "prefill.hip"]
+# measurement reference (achievable bf16 MFMA rate), a library of its own loaded only by bench.py
+PROBE_LIB = os.path.join(HERE, "libaqp_probe.so")
+PROBE_SOURCES = ["mfma_probe.hip"]
 
 
 def hipcc() -> str:
@@ -55,8 +58,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    probe_objs = [_compile(src) for src in PROBE_SOURCES]
+    r = subprocess.run([hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *probe_objs, "-o", PROBE_LIB + ".tmp"],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -345,6 +345,30 @@ def main():
         tf = 2 * n ** 3 / ms / 1e9
         print(json.dumps({"gemm": f"bf16 {n}x{n}x{n} torch.matmul", "ms": round(ms, 4), "tflops": round(tf, 1),
                           "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}))
+        # a hand-written loop of independent 16x16x32 bf16 MFMAs on every SIMD: the dense matrix
+        # rate the part reaches at the clock it holds under matrix load
+        import ctypes
+        lib = ctypes.CDLL(os.path.join(ROOT, "attention_quantized_paged_amd", "libaqp_probe.so"))
+        lib.aqp_probe_mfma_loop.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        cus = lib.aqp_probe_cu_count()
+        iters = 20000
+        st = torch.cuda.current_stream().cuda_stream
+        for wpc in (8, 16):  # waves per CU (2 and 4 per SIMD): the rate is saturated when both agree
+            blocks = wpc // 4 * cus
+            out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+            for _ in range(3):
+                assert lib.aqp_probe_mfma_loop(blocks, iters, out.data_ptr(), st) == 0
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(10):
+                lib.aqp_probe_mfma_loop(blocks, iters, out.data_ptr(), st)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            tf = blocks * 4 * iters * 8 * 16384 / ms / 1e9
+            print(json.dumps({"mfma_loop": f"independent v_mfma_f32_16x16x32_bf16, {wpc} waves per CU", "cus": cus,
+                              "ms": round(ms, 4), "tflops": round(tf, 1),
+                              "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}))
         return
     import attention_quantized_paged_amd as aqp
     import workloads as W
