@@ -237,7 +237,9 @@ def run_all_configs(torch, aqp, W, args):
     q head. Mixed batches report the one call's time against both units."""
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
 
-    def timed(fn, reps):
+    spread = {}
+
+    def timed(fn, reps, key=None):
         ts = []
         for _ in range(reps):
             flush.sum()
@@ -247,7 +249,12 @@ def run_all_configs(torch, aqp, W, args):
             e1.record()
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
+        if key:
+            spread[key] = [round(float(np.percentile(ts, 10)), 4), round(float(np.percentile(ts, 90)), 4)]
         return float(np.median(ts))
+
+    import oracle
+    ofmt = {0: oracle.FMT_BF16, 1: oracle.FMT_E4M3, 2: oracle.FMT_E5M2, 3: oracle.FMT_INT8}
 
     # the decode batch once more over an unquantised (bf16, "auto") cache: the same kernels with
     # two-byte elements, for the quantisation's bandwidth saving side by side
@@ -271,6 +278,8 @@ def run_all_configs(torch, aqp, W, args):
         cw()
         cw_ms = timed(cw, 5)
         cw_bytes = n * w.num_kv_heads * w.head_dim * 2 * (2 + eb) + n * 8 + (n * w.num_kv_heads * 8 if pth else 0)
+        host16 = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+        kh, vh = host16(k), host16(v)
         del k, v
         q = (torch.randn((int(b.query_start_loc[-1]), w.num_q_heads, w.head_dim), device="cuda", generator=g)
              * w.sigma).to(torch.bfloat16)
@@ -284,12 +293,34 @@ def run_all_configs(torch, aqp, W, args):
         att = lambda: aqp.paged_attention(params, desc, cache, q, bt, sch.meta, md, ks, vs, scr, scr.numel(), out)
         for _ in range(3):
             att()
-        att_ms = timed(att, 20)
+        att_ms = timed(att, 20, key="attention")
         kvb = W.kv_read_bytes(w, per_token_head=pth) * eb
         fl = W.prefill_flops(w)
+        # the oracle on the host's cores: its own cache write of the same history, then one
+        # attention call over the whole batch (three when the first takes under three seconds)
+        od = oracle.CacheDesc(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, ofmt[desc.dtype], desc.mode)
+        ocache = np.zeros(od.total_bytes, dtype=np.uint8)
+        oracle.cache_write(od, ocache, kh, vh, b.slots_hist, ks, vs)
+        del kh, vh
+        qh = host16(q)
+        ots = []
+        while len(ots) < 3 and (not ots or ots[0] < 3.0):
+            t0 = time.perf_counter()
+            oracle.attention(od, ocache, qh, b.block_tables, b.seq_lens, b.query_start_loc, w.num_q_heads,
+                             causal=w.causal, window=w.window, softcap=w.softcap, k_scale=ks, v_scale=vs)
+            ots.append(time.perf_counter() - t0)
+        del ocache
+        o_s = float(np.median(ots))
         row = {"workload": w.name, "kv_cache_dtype": w.kv_dtype, "attention_ms": round(att_ms, 4),
+               "attention_ms_p10_p90": spread["attention"],
                "cache_write": {"tokens": n, "ms": round(cw_ms, 4), "gbs": round(cw_bytes / cw_ms / 1e6, 1),
-                               "frac_of_hbm_peak": round(cw_bytes / cw_ms / 1e6 / HBM_PEAK_GBS, 4)}}
+                               "frac_of_hbm_peak": round(cw_bytes / cw_ms / 1e6 / HBM_PEAK_GBS, 4)},
+               "oracle_cpu": {"attention_s": round(o_s, 3), "calls": len(ots), "cores": oracle.num_threads(),
+                              "kind": "oracle"}}
+        if kvb:
+            row["oracle_cpu"]["decode_gbs"] = round(kvb / o_s / 1e9, 3)
+        if fl:
+            row["oracle_cpu"]["prefill_gflops"] = round(fl / o_s / 1e9, 2)
         if kvb:
             row["decode_kv_bytes"] = kvb
             row["decode_gbs"] = round(kvb / att_ms / 1e6, 1)
