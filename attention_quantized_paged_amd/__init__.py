@@ -94,11 +94,30 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def _dev_ok(t, name: str) -> None:
+def _dev_ok(t, name: str, contiguous: bool = True) -> None:
     if hasattr(t, "is_cuda") and not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if hasattr(t, "is_contiguous") and not t.is_contiguous():
+    if contiguous and hasattr(t, "is_contiguous") and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _nbytes(t) -> Optional[int]:
+    """Bytes a buffer argument spans (None for raw pointers, which are taken as given)."""
+    if t is None or isinstance(t, int):
+        return None
+    if isinstance(t, np.ndarray):
+        return t.nbytes
+    if hasattr(t, "untyped_storage"):
+        # a view may start inside its storage: the bytes from its first element to the storage end
+        st = t.untyped_storage()
+        return st.nbytes() - (t.data_ptr() - st.data_ptr())
+    return None
+
+
+def _need(t, nbytes: int, name: str) -> None:
+    have = _nbytes(t)
+    if have is not None and have < nbytes:
+        raise ValueError(f"{name} spans {have} bytes, the call needs {nbytes}")
 
 
 def parse_kv_dtype(s: str) -> Tuple[int, int]:
@@ -152,6 +171,20 @@ def cache_write(desc: CacheDesc, cache, k, v, slot_mapping, k_scale: float = 1.0
         token_stride = int(k.stride(0)) if hasattr(k, "stride") else desc.num_kv_heads * desc.head_dim
     for t, nm in ((cache, "cache"), (slot_mapping, "slot_mapping")):
         _dev_ok(t, nm)
+    for t, nm in ((k, "k"), (v, "v")):
+        _dev_ok(t, nm, contiguous=False)
+    # every buffer spans what the kernel reads or writes, so a mis-sized tensor is refused on the
+    # host instead of becoming an out-of-range access on the device
+    _need(cache, cache_bytes(desc)[2], "cache")
+    if n > 0:
+        row = desc.num_kv_heads * desc.head_dim
+        if token_stride < row:
+            raise ValueError(f"token_stride {token_stride} < num_kv_heads * head_dim = {row}")
+        _need(k, 2 * ((n - 1) * token_stride + row), "k")
+        _need(v, 2 * ((n - 1) * token_stride + row), "v")
+        _need(slot_mapping, 8 * n, "slot_mapping")
+        if hasattr(slot_mapping, "element_size") and slot_mapping.element_size() != 8:
+            raise ValueError("slot_mapping must be int64")
     _check(_lib.aqp_cache_write(ctypes.byref(desc), _ptr(cache), _ptr(k), _ptr(v), n, token_stride,
                                 _ptr(slot_mapping), float(k_scale), float(v_scale), _stream(stream)))
 
@@ -231,6 +264,18 @@ def paged_attention(params: AttnParams, desc: CacheDesc, cache, q, block_tables,
                     k_scale: float, v_scale: float, scratch, scratch_bytes: int, out, stream=None) -> None:
     for t, nm in ((cache, "cache"), (q, "q"), (block_tables, "block_tables"), (meta_dev, "meta_dev"), (out, "out")):
         _dev_ok(t, nm)
+    if isinstance(meta_host, np.ndarray) and meta_host.nbytes >= 256:
+        # sizes the kernels assume, from the schedule they will run (the library itself checks the
+        # schedule against desc and params; it cannot see how large the caller's buffers are)
+        h = parse_header(meta_host)
+        if h["magic"] == 0x53505141:
+            rowb = 2 * h["num_q_heads"] * h["head_dim"]
+            _need(q, h["total_q_tokens"] * rowb, "q")
+            _need(out, h["total_q_tokens"] * rowb, "out")
+            _need(block_tables, 4 * h["num_seqs"] * h["max_blocks_per_seq"], "block_tables")
+            _need(meta_dev, h["meta_bytes"], "meta_dev")
+            _need(cache, cache_bytes(desc)[2], "cache")
+            _need(scratch, int(scratch_bytes), "scratch")
     _check(_lib.aqp_paged_attention(ctypes.byref(params), ctypes.byref(desc), _ptr(cache), _ptr(q),
                                     _ptr(block_tables), _ptr(meta_host), _ptr(meta_dev), float(k_scale),
                                     float(v_scale), _ptr(scratch), int(scratch_bytes), _ptr(out), _stream(stream)))

@@ -139,3 +139,36 @@ def test_unquantised_cache_geometry_and_limits():
     with pytest.raises(aqp.AqpError) as e:
         aqp.get_schedule(aqp.attn_params(8, 2, 256, 4), d256, sl, qsl)
     assert e.value.status == aqp.ERR_UNSUPPORTED
+
+
+def test_binding_refuses_mis_sized_buffers():
+    """The binding checks every buffer's extent against what the kernels will touch (the C ABI
+    takes raw pointers and cannot): too-small q, out, block tables, device schedule, scratch,
+    cache, keys, values or slots are refused on the host, before any launch."""
+    import numpy as np
+    desc = aqp.cache_desc(8, 16, 2, 64, "fp8_e4m3")
+    total = aqp.cache_bytes(desc)[2]
+    sl, qsl = np.array([40, 9], np.int32), np.array([0, 1, 10], np.int32)
+    params = aqp.attn_params(4, 2, 64, 3)
+    s = aqp.get_schedule(params, desc, sl, qsl)
+    cache = np.zeros(total, np.uint8)
+    q = np.zeros((10, 4, 64), np.uint16)
+    out = np.zeros((10, 4, 64), np.uint16)
+    bt = np.zeros((2, 3), np.int32)
+    md = s.meta.copy()
+    scr = np.zeros(max(4, s.scratch_bytes), np.uint8)
+    good = dict(cache=cache, q=q, block_tables=bt, meta_dev=md, scratch=scr, out=out)
+    for name, small in (("q", q[:9]), ("out", out[:9]), ("block_tables", bt[:1]), ("meta_dev", md[:100]),
+                        ("cache", cache[:-1]), ("scratch", scr[:1] if s.scratch_bytes > 1 else None)):
+        if small is None:
+            continue
+        a = dict(good, **{name: small})
+        with pytest.raises(ValueError, match=name):
+            aqp.paged_attention(params, desc, a["cache"], a["q"], a["block_tables"], s.meta, a["meta_dev"], 1.0, 1.0,
+                                a["scratch"], s.scratch_bytes, a["out"], stream=0)
+    k = np.zeros((5, 2, 64), np.uint16)
+    slots = np.arange(5, dtype=np.int64)
+    for kk, vv, ss, cc, what in ((k[:, :, :63], k, slots, cache, "k"), (k, k[:, :1], slots, cache, "v"),
+                                 (k, k, slots[:4], cache, "slot_mapping"), (k, k, slots, cache[:10], "cache")):
+        with pytest.raises(ValueError, match=what):
+            aqp.cache_write(desc, cc, kk, vv, ss, 1.0, 1.0, stream=0)
