@@ -52,6 +52,9 @@ def test_full_size_parity(aqp, w):
     say(f"  {w.name}: cache pool {r.ocache.size / 1e6:.0f} MB, {len(r.b.slots_hist)} tokens written")
     r.cache_matches()
     out = r.gpu_attention()
+    # every row of every query token was written (the output starts as a NaN pattern), whichever
+    # work-group ran its item
+    assert np.all(np.isfinite(W.bf16_to_f32(out))), f"{w.name}: output rows left unwritten"
     h = r.sched.header
     say(f"  {w.name}: decode work-groups {h['num_dec_wgs']}, partials {h['num_parts']}, "
         f"prefill items {h['num_pf_items']} of {h['pf_rows']} rows")
