@@ -210,7 +210,7 @@ _HDR_FIELDS = ("magic version dtype mode kv_elem_bytes staged_elem_bytes scale_b
                "tile_keys dec_iter_keys dec_waves pf_rows pf_kv_tile heads_per_unit dec_lds_bytes pf_lds_bytes "
                "num_dec_wgs num_dec_segs num_parts num_comb num_pf_items group_heads").split()
 _HDR_FIELDS64 = ("off_dec_segs off_dec_wg_start off_comb off_pf_items meta_bytes scratch_bytes page_bytes block_bytes "
-                 "dec_kv_keys off_seq_lens num_slots comb_heads num_pf_split num_dec_comb").split()
+                 "dec_kv_keys off_seq_lens num_slots comb_heads num_pf_split num_dec_comb off_dec_first").split()
 
 
 def parse_header(meta: np.ndarray) -> dict:

@@ -451,6 +451,10 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   off = round_up(off + (int64_t)segs.size() * sizeof(DecSeg), 256);
   const int64_t off_wgs = off;
   off = round_up(off + (int64_t)wg_start.size() * sizeof(int32_t), 256);
+  // each decode work-group's first segment once more, indexed by work-group, so a work-group's
+  // first copies wait on one record load instead of its range and then its segment
+  const int64_t off_first = off;
+  off = round_up(off + (int64_t)num_wgs * (int64_t)sizeof(DecSeg), 256);
   const int64_t off_comb = off;
   off = round_up(off + (int64_t)comb.size() * sizeof(CombItem), 256);
   const int64_t off_pf = off;
@@ -472,7 +476,8 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   auto zero_gap = [&](int64_t from, int64_t to) { if (to > from) std::memset(m + from, 0, (size_t)(to - from)); };
   zero_gap(sizeof(SchedHeader), off_segs);
   zero_gap(off_segs + (int64_t)segs.size() * (int64_t)sizeof(DecSeg), off_wgs);
-  zero_gap(off_wgs + (int64_t)wg_start.size() * 4, off_comb);
+  zero_gap(off_wgs + (int64_t)wg_start.size() * 4, off_first);
+  zero_gap(off_first + (int64_t)num_wgs * (int64_t)sizeof(DecSeg), off_comb);
   zero_gap(off_comb + (int64_t)comb.size() * (int64_t)sizeof(CombItem), off_pf);
   zero_gap(off_pf + (int64_t)pf.size() * (int64_t)sizeof(PfItem), off_sl);
   zero_gap(off_sl + (int64_t)num_seqs * 4, need);
@@ -513,6 +518,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   h.group_heads = hpu;
   h.off_dec_segs = off_segs;
   h.off_dec_wg_start = off_wgs;
+  h.off_dec_first = off_first;
   h.off_comb = off_comb;
   h.off_pf_items = off_pf;
   h.meta_bytes = need;
@@ -528,6 +534,12 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   std::memcpy(m, &h, sizeof h);
   if (!segs.empty()) std::memcpy(m + off_segs, segs.data(), segs.size() * sizeof(DecSeg));
   if (!wg_start.empty()) std::memcpy(m + off_wgs, wg_start.data(), wg_start.size() * sizeof(int32_t));
+  for (int32_t w = 0; w < num_wgs; ++w) {
+    DecSeg f;
+    std::memset(&f, 0, sizeof f);
+    if (wg_start[w] < wg_start[w + 1]) f = segs[wg_start[w]];
+    std::memcpy(m + off_first + (int64_t)w * (int64_t)sizeof(DecSeg), &f, sizeof f);
+  }
   if (!comb.empty()) std::memcpy(m + off_comb, comb.data(), comb.size() * sizeof(CombItem));
   if (!pf.empty()) std::memcpy(m + off_pf, pf.data(), pf.size() * sizeof(PfItem));
   if (num_seqs > 0) std::memcpy(m + off_sl, seq_lens, (size_t)num_seqs * 4);

@@ -120,8 +120,8 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why);
 
 // ---- schedule metadata -----------------------------------------------------
 // Layout: [SchedHeader][DecSeg x num_dec_segs][int32 dec_wg_start x (num_dec_wgs + 1)]
-//         [CombItem x num_comb][PfItem x num_pf_items][int32 seq_lens x num_seqs], each array
-//         256-byte aligned.
+//         [DecSeg x num_dec_wgs: first segment of each work-group][CombItem x num_comb]
+//         [PfItem x num_pf_items][int32 seq_lens x num_seqs], each array 256-byte aligned.
 struct SchedHeader {
   uint32_t magic, version;
   // what the schedule was built for
@@ -146,10 +146,11 @@ struct SchedHeader {
   int64_t comb_heads;    // most heads of one merge item (the merge grid's second dimension)
   int64_t num_pf_split;  // prefill runs that write partial results
   int64_t num_dec_comb;  // merge items [0, num_dec_comb) merge decode parts, the rest prefill runs
+  int64_t off_dec_first; // DecSeg x num_dec_wgs: each work-group's first segment (zeros if it has none)
 };
 
 static_assert(offsetof(SchedHeader, off_dec_segs) == 136, "SchedHeader layout is part of the metadata format");
-static_assert(sizeof(SchedHeader) == 248, "SchedHeader layout is part of the metadata format");
+static_assert(sizeof(SchedHeader) == 256, "SchedHeader layout is part of the metadata format");
 
 // Decode segment: keys [k_lo, k_hi) of (sequence, KV head, q heads
 // [head0, head0 + nheads) of that KV head's group), one query token.

@@ -43,6 +43,7 @@ struct DecArgs {
   const int32_t* block_tables;
   const DecSeg* segs;
   const int32_t* wg_start;  // segments of work-group b: [wg_start[b], wg_start[b + 1])
+  const DecSeg* first;      // first segment of work-group b (segs[wg_start[b]])
   float* scratch;
   uint16_t* out;
   int64_t page_bytes, block_bytes;
@@ -171,6 +172,7 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
   float* mg = (float*)(smem + kDecWaves * NS * SLOT + kDecWaves * NQ * QB);  // [wave][head][merge_stride(D)]
   const uint32_t ring_lds = lds_addr(ring), q_lds = lds_addr(qslots);
   const int s_begin = as_const(a.wg_start)[blockIdx.x], s_end = as_const(a.wg_start)[blockIdx.x + 1];
+  const DecSeg first_sg = load_const(as_const(a.first) + blockIdx.x);
 
   if (wave == kDecWaves) {
     // ---- the merging wave: takes part in the two barriers of every segment, merges the compute
@@ -304,7 +306,20 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
     }
   };
 
-  seek(s_begin);
+  // the work-group's first segment comes from its own record (loaded at the start, beside the
+  // segment range), so the first copies do not wait on the range and then the segment; every
+  // work-group has at least one segment
+  is_sg = first_sg;
+  is_left = first_pos(is_sg, is_p);
+  if (is_left > 0) {
+    is_si = s_begin;
+    is_new = true;
+    is_bt = as_const(a.block_tables) + (int64_t)is_sg.seq * a.max_blocks;
+    is_kv = a.cache + (int64_t)is_sg.kvh * a.page_bytes;
+    is_blk = is_bt[is_p.bi];
+  } else {
+    seek(s_begin + 1);
+  }
 #pragma unroll
   for (int k = 0; k < NS; ++k) issue_next(0, 0);
 
@@ -591,6 +606,7 @@ static int launch_dec(const AttnArgs& a, hipStream_t st) {
   d.block_tables = a.block_tables;
   d.segs = (const DecSeg*)(a.meta_dev + h.off_dec_segs);
   d.wg_start = (const int32_t*)(a.meta_dev + h.off_dec_wg_start);
+  d.first = (const DecSeg*)(a.meta_dev + h.off_dec_first);
   d.scratch = a.scratch;
   d.out = a.out;
   d.page_bytes = a.page_bytes;

@@ -68,6 +68,10 @@ def _check_decode(seqs, hq, hkv, d, bs, window, par, split=0):
         assert len(segs) == 0 and h["num_parts"] == 0 and h["num_dec_comb"] == 0
         wgs = np.zeros(1, np.int32)
     assert wgs[0] == 0 and wgs[-1] == len(segs) and np.all(np.diff(wgs) >= 0)
+    # each work-group's own copy of its first segment
+    first = s.meta[h["off_dec_first"]: h["off_dec_first"] + SEG.itemsize * h["num_dec_wgs"]].view(SEG)
+    for w_ in range(h["num_dec_wgs"]):
+        assert wgs[w_] < wgs[w_ + 1] and first[w_].tobytes() == segs[wgs[w_]].tobytes()
     # coverage: for each decode (seq, kvh, head) the union of segment ranges is the visible range, disjoint
     cover = {}
     for sg in segs:
