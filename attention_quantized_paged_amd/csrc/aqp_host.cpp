@@ -346,40 +346,24 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
 
   // ---- prefill items: (sequence, KV head, run of query tokens, run of its q heads): all G
   // heads of the KV head when G <= rows, else one token and `rows` heads at a time;
-  // heaviest (most keys) first. rows = kPfRows, or kPfRowsSmall at head_dim <= 128 when
-  // kPfRows-row items would give the CUs fewer than two work-groups each and the batch has no
-  // decode work (decode runs beside the prefill and needs the room the second work-group takes).
-  auto count_items = [&](int32_t rows) {
-    const int32_t hp = std::min<int32_t>(G, rows), tp = std::max<int32_t>(1, rows / G);
-    int64_t n = 0;
+  // heaviest (most keys) first.
+  auto build_items = [&](int32_t rows) {
+    pf.clear();
+    const int32_t hpi = std::min<int32_t>(G, rows);
+    const int32_t tpi = std::max<int32_t>(1, rows / G);
     for (int32_t b = 0; b < num_seqs; ++b) {
-      const int32_t ql = qsl[b + 1] - qsl[b];
-      if (ql > 1) n += (int64_t)((ql + tp - 1) / tp) * p.num_kv_heads * ((G + hp - 1) / hp);
+      const int32_t L = seq_lens[b], ql = qsl[b + 1] - qsl[b];
+      if (ql <= 1) continue;
+      const int32_t causal = p.causal_per_seq ? p.causal_per_seq[b] : p.causal;
+      for (int32_t q0 = 0; q0 < ql; q0 += tpi) {
+        const int32_t q1 = std::min(ql, q0 + tpi);
+        const int32_t khi = causal ? (L - ql + q1) : L;  // exclusive end of the last row's keys
+        for (int32_t h = 0; h < p.num_kv_heads; ++h)
+          for (int32_t h0 = 0; h0 < G; h0 += hpi)
+            pf.push_back({b, h, q0, q1, L, ql, qsl[b], khi, h0, std::min(hpi, G - h0), causal, 0, khi, -1, 0, 0});
+      }
     }
-    return n;
   };
-  int32_t pf_rows = kPfRows;
-  if (p.prefill_rows > 0) {
-    pf_rows = p.prefill_rows;
-  } else if (desc->head_dim <= 128 && total_tiles == 0 && total_q > 0 && count_items(kPfRows) < 2 * (int64_t)device_cu_count()) {
-    pf_rows = kPfRowsSmall;
-  }
-  if (pf_rows < pf_waves(desc->head_dim) * 16)
-    return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: %d rows per prefill item at head_dim %d is not built", pf_rows, desc->head_dim);
-  const int32_t hpi = std::min<int32_t>(G, pf_rows);
-  const int32_t tpi = std::max<int32_t>(1, pf_rows / G);
-  for (int32_t b = 0; b < num_seqs; ++b) {
-    const int32_t L = seq_lens[b], ql = qsl[b + 1] - qsl[b];
-    if (ql <= 1) continue;
-    const int32_t causal = p.causal_per_seq ? p.causal_per_seq[b] : p.causal;
-    for (int32_t q0 = 0; q0 < ql; q0 += tpi) {
-      const int32_t q1 = std::min(ql, q0 + tpi);
-      const int32_t khi = causal ? (L - ql + q1) : L;  // exclusive end of the last row's keys
-      for (int32_t h = 0; h < p.num_kv_heads; ++h)
-        for (int32_t h0 = 0; h0 < G; h0 += hpi)
-          pf.push_back({b, h, q0, q1, L, ql, qsl[b], khi, h0, std::min(hpi, G - h0), causal, 0, khi, -1, 0, 0});
-    }
-  }
   // first key of an item's key loop: the 16-key tile holding its first query's window start (the
   // prefill kernel starts its 32-key steps there)
   auto key_begin = [&](const PfItem& it) {
@@ -391,6 +375,46 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
     const int32_t kb = std::max(key_begin(it), it.split_lo), ke = std::min(it.k_hi_max, it.split_hi);
     return ke > kb ? (ke - kb + kPfKvTile - 1) / kPfKvTile : 0;
   };
+  // Key-split plan of the items in pf at `rows` rows per item: runs per item = its steps over the
+  // target run length (the batch's steps spread over the work-groups the device holds), rounded to
+  // nearest, at most max_runs, each run at least min_steps long. Split only when the batch has
+  // fewer items than the device holds at once (or when the caller asks for it).
+  struct SplitPlan { int32_t max_runs; int64_t min_steps, target; };
+  auto split_plan = [&](int32_t rows) {
+    SplitPlan sp{1, kPfMinSplitSteps, 1};
+    int64_t total_steps = 0;
+    for (const PfItem& it : pf) total_steps += steps_of(it);
+    const int64_t cap = (int64_t)device_cu_count() * pf_wgs_per_cu(desc->head_dim, rows, g.pf_lds_bytes);
+    if (p.prefill_kv_split > 1) {
+      sp.max_runs = p.prefill_kv_split;
+      sp.min_steps = 1;
+    } else if (p.prefill_kv_split == 0 && !pf.empty() && (int64_t)pf.size() < cap) {
+      sp.max_runs = kPfMaxSplit;
+      sp.target = std::max<int64_t>(1, (total_steps + cap - 1) / cap);
+    }
+    return sp;
+  };
+  auto runs_of = [&](const SplitPlan& sp, int32_t st) {
+    if (sp.max_runs < 2) return 1;
+    const int64_t want = (st + sp.target / 2) / sp.target;
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>({(int64_t)sp.max_runs, want, st / sp.min_steps}));
+  };
+  // rows per item: kPfRows; at head_dim <= 128, for a batch with no decode work (decode runs beside
+  // the prefill and needs the room a second work-group takes), kPfRowsSmall when kPfRows-row items,
+  // even after key splits, would give the CUs fewer than two work-groups each
+  int32_t pf_rows = p.prefill_rows > 0 ? p.prefill_rows : kPfRows;
+  if (pf_rows < pf_waves(desc->head_dim) * 16)
+    return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: %d rows per prefill item at head_dim %d is not built", pf_rows, desc->head_dim);
+  build_items(pf_rows);
+  if (p.prefill_rows == 0 && desc->head_dim <= 128 && total_tiles == 0 && !pf.empty()) {
+    const SplitPlan sp = split_plan(pf_rows);
+    int64_t runs = 0;
+    for (const PfItem& it : pf) runs += runs_of(sp, steps_of(it));
+    if (runs < 2 * (int64_t)device_cu_count()) {
+      pf_rows = kPfRowsSmall;
+      build_items(pf_rows);
+    }
+  }
   // ---- prefill key splits: runs of whole 32-key steps; the rows of each run of a split item get
   // partial-result slots after the decode parts' (num_parts x hpu) slots, and each query token of
   // the item one merge item over its row in every run
@@ -399,26 +423,12 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   int64_t num_pf_split = 0;
   int32_t comb_heads = comb.empty() ? 0 : hpu;
   {
-    int64_t total_steps = 0;
-    for (const PfItem& it : pf) total_steps += steps_of(it);
-    const int64_t cap = (int64_t)device_cu_count() * pf_wgs_per_cu(desc->head_dim, pf_rows, g.pf_lds_bytes);
-    // runs per item: its steps over the target run length (the batch's steps spread over the
-    // work-groups the device holds), rounded to nearest, each run at least min_steps long
-    int32_t max_runs = 1;
-    int64_t min_steps = kPfMinSplitSteps, target = 1;
-    if (p.prefill_kv_split > 1) {
-      max_runs = p.prefill_kv_split;
-      min_steps = 1;
-    } else if (p.prefill_kv_split == 0 && !pf.empty() && (int64_t)pf.size() < cap) {
-      max_runs = kPfMaxSplit;
-      target = std::max<int64_t>(1, (total_steps + cap - 1) / cap);
-    }
-    if (max_runs > 1) {
+    const SplitPlan sp = split_plan(pf_rows);
+    if (sp.max_runs > 1) {
       const size_t n0 = pf.size();
       for (size_t i = 0; i < n0; ++i) {
         const int32_t st = steps_of(pf[i]);
-        const int64_t want = (st + target / 2) / target;
-        const int32_t runs = (int32_t)std::max<int64_t>(1, std::min<int64_t>({(int64_t)max_runs, want, st / min_steps}));
+        const int32_t runs = runs_of(sp, st);
         if (runs < 2) continue;
         const PfItem base = pf[i];
         const int32_t kb = key_begin(base);

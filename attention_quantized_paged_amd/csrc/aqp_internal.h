@@ -43,7 +43,7 @@ constexpr int kMinRunTiles = 32;     // decode: fewest 16-key tiles a work-group
 // prefill key splits: when a batch has fewer prefill items than the device holds work-groups at
 // once, long items are cut into runs of at least this many kPfKvTile-key steps (at most
 // kPfMaxSplit runs each); the runs' partial results are merged like split decode ranges
-constexpr int kPfMinSplitSteps = 8;
+constexpr int kPfMinSplitSteps = 16;
 constexpr int kPfMaxSplit = 8;
 constexpr int kCwRowsPerLane = 4;    // cache write: rows each lane loads before converting
 constexpr int kCwWgsPerCu = 16;      // cache write: resident work-groups per CU (grid cap)

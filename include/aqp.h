@@ -107,8 +107,8 @@ typedef struct {
                                  work-groups on the current device (CUs x 3 for head_dim <= 128, x 2 above) */
   int32_t prefill_rows;       /* query rows (token, q head) per prefill work-group: 64 or 128 (64 needs
                                  head_dim <= 128); 0 = 128, or 64 at head_dim <= 128 for a batch with no
-                                 decode sequence whose 128-row items would number fewer than two per
-                                 CU of the current device */
+                                 decode sequence whose 128-row items, after key splits, would number
+                                 fewer than two per CU of the current device */
   /* The harness parameters the page names without defining them; the readings taken: */
   const int32_t* causal_per_seq; /* host int32 [num_seqs] of 0/1, or NULL (= `causal` for every
                                     sequence). Read by aqp_get_schedule only: the schedule carries
@@ -122,7 +122,7 @@ typedef struct {
   int32_t prefill_kv_split;   /* key-range split of prefill work items ([P50194] Code excerpt:
                                  enable_kv_split): 0 = automatic (when the batch has fewer prefill
                                  items than the device runs at once, long items are cut into runs of
-                                 at least 8 key steps of 32 keys, at most 8 runs, sized so the runs
+                                 at least 16 key steps of 32 keys, at most 8 runs, sized so the runs
                                  fill the device); 1 = never; n > 1 = every item with enough keys is
                                  cut into up to n runs. The runs' partial results are merged into
                                  the output like split decode ranges. */

@@ -334,6 +334,12 @@ def test_prefill_rows_choice():
     assert h_rows(_sched(few, 8, 2, 64, 16)[0]) == 64
     assert h_rows(_sched(few + ((1, 500),), 32, 8, 128, 16)[0]) == 128  # decode runs beside the prefill
     assert h_rows(_sched(few, 16, 2, 256, 64)[0]) == 128
+    # the mixed batch's prefill chunks alone: 256 items of 128 rows split into 512 key runs (two
+    # per CU), so the items keep 128 rows
+    half = tuple(x for x in workloads.CFG4.seqs if x[0] > 1)
+    s_half = _sched(half, 32, 8, 128, 16)[0]
+    assert h_rows(s_half) == 128 and s_half.header["num_pf_split"] == 512
+    assert h_rows(_sched(half, 32, 8, 128, 16, split=1)[0]) == 64  # without splits: 64-row items
     many = ((1024, 1024),) * 4  # 4 x 32 x 8 = 1024 items of 128 rows
     assert h_rows(_sched(many, 32, 8, 128, 16)[0]) == 128
     assert h_rows(_sched(few, 32, 8, 128, 16, rows=128)[0]) == 128
