@@ -190,6 +190,7 @@ extern "C" int aqp_cache_write(const aqp_cache_desc* desc, void* cache, const vo
   a.block_size = desc->block_size;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.narrow = 2 * num_tokens * desc->num_kv_heads < ((int64_t)1 << 31) && a.total_slots < ((int64_t)1 << 31);
   return launch_cache_write(desc->dtype, desc->mode, a, stream);
 }
 

@@ -193,6 +193,7 @@ struct CacheWriteArgs {
   int64_t total_slots;
   int32_t num_kv_heads, head_dim, block_size;
   float k_scale, v_scale;
+  int32_t narrow;  // rows (2 x tokens x KV heads) and slots below 2^31: 32-bit index arithmetic
 };
 int launch_cache_write(int dtype, int mode, const CacheWriteArgs& a, void* stream);
 

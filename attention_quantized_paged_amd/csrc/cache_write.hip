@@ -51,6 +51,27 @@ __device__ __forceinline__ uint32_t encode4(float y0, float y1, float y2, float 
   }
 }
 
+// Max over aligned runs of SPAN lanes (SPAN = 4, 8, 16, 32), in VALU: DPP quad permutes (lane ^ 1,
+// lane ^ 2), then mirrors within 8 and 16 lanes (after the quad steps every lane of a quad holds
+// its maximum, so pairing quad q with its mirror covers the run), then the 16-lane row swap.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int SPAN>
+__device__ __forceinline__ float max_in_span(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));                             // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));                             // quad_perm [2,3,0,1]
+  if constexpr (SPAN >= 8) v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+  if constexpr (SPAN >= 16) v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+  if constexpr (SPAN >= 32) {
+    auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), false, false);
+    v = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+  }
+  static_assert(SPAN >= 4 && SPAN <= 32, "span");
+  return v;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
@@ -76,7 +97,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
       const int64_t rr = active[u] ? r : rows - 1;  // keep every lane in the row's butterfly
       kv[u] = rr >= per_kv ? 1 : 0;
       const int64_t rem = rr - kv[u] * per_kv;
-      const int64_t t = rem / a.num_kv_heads;
+      // token and head of the row: a 32-bit division whenever the rows fit (uniform branch)
+      const int64_t t = a.narrow ? (int64_t)((uint32_t)rem / (uint32_t)a.num_kv_heads) : rem / a.num_kv_heads;
       h[u] = (int)(rem - t * a.num_kv_heads);
       in[u] = *(const uint4*)((kv[u] ? a.v : a.k) + t * a.token_stride + (int64_t)h[u] * D + sub * 8);
       slot[u] = a.slots[t];
@@ -93,15 +115,14 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-#pragma unroll
-        for (int o = SPAN / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        amax = max_in_span<SPAN>(amax);
         s = amax / QMAX;  // correctly rounded fp32 division
       } else {
         s = kv[u] ? a.v_scale : a.k_scale;
       }
       const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
       if (!active[u] || slot[u] < 0 || slot[u] >= a.total_slots) continue;
-      const int64_t blk = slot[u] / a.block_size;
+      const int64_t blk = a.narrow ? (int64_t)((uint32_t)slot[u] / (uint32_t)a.block_size) : slot[u] / a.block_size;
       const int off = (int)(slot[u] - blk * a.block_size);
       uint8_t* page = a.cache + blk * a.block_bytes + (int64_t)(kv[u] * a.num_kv_heads + h[u]) * a.page_bytes;
       if constexpr (DT == AQP_KV_AUTO) {
