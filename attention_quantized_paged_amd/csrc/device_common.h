@@ -168,6 +168,21 @@ __device__ __forceinline__ T load_const(cptr<T> p) {
   return r;
 }
 
+// Unsigned division by a divisor d >= 2 fixed for the launch, exact for every 32-bit n (division
+// by an invariant integer with a multiply-high, the "round-up" method of Granlund and Montgomery):
+// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1; n / d = (t + ((n - t) >> 1)) >> (l - 1) with
+// t = mulhi(n, m). Uniform operands keep it on the scalar unit.
+inline void invariant_divisor(uint32_t d, uint32_t* m, int32_t* shift) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  *m = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);
+  *shift = l - 1;
+}
+__device__ __forceinline__ uint32_t div_invariant(uint32_t n, uint32_t m, int32_t shift) {
+  const uint32_t t = __umulhi(n, m);
+  return (t + ((n - t) >> 1)) >> shift;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // tanh from its definition via exp: tanh(t) = sign(t) * (1 - e^{-2|t|}) / (1 + e^{-2|t|}),

@@ -42,6 +42,8 @@ struct PfArgs {
   float v_scale;
   const float* alibi;  // [num_q_heads] slopes or null
   const float* sinks;  // [num_q_heads] sink logits or null
+  uint32_t bs_magic;   // key / block_size = div_invariant(key, bs_magic, bs_shift)
+  int32_t bs_shift;
 };
 
 // 16-byte chunk swizzle of a staged row: chunk c of row `row` is stored at chunk
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       const int lc = (q % CPR) ^ swz<ROWB>(row);
       // tile of this copy (uniform), clamped to the tile of key L-1
       const int tile_k0 = min(kb0 + ((q0 / CPR) & ~15), last_tile);
-      const int tbi = tile_k0 / a.block_size;
+      const int tbi = (int)div_invariant((uint32_t)tile_k0, a.bs_magic, a.bs_shift);
       const int tr0 = tile_k0 - tbi * a.block_size;
       int32_t blk = bt[tbi];
       if ((uint32_t)blk >= (uint32_t)a.num_blocks) blk = 0;  // invalid table entry: stay in the pool
@@ -201,7 +203,8 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
         // 16 lanes x 16 bytes: [K scales of the 32 keys][V scales], 4 scales per lane
         const int tl = (lane >> 2) & 1, part = lane & 3, kv = lane >> 3;
         const int t0 = min(kb0, last_tile), t1 = min(kb0 + 16, last_tile);
-        const int bi0 = t0 / a.block_size, bi1 = t1 / a.block_size;
+        const int bi0 = (int)div_invariant((uint32_t)t0, a.bs_magic, a.bs_shift);
+        const int bi1 = (int)div_invariant((uint32_t)t1, a.bs_magic, a.bs_shift);
         int32_t b0 = bt[bi0], b1 = bt[bi1];
         if ((uint32_t)b0 >= (uint32_t)a.num_blocks) b0 = 0;
         if ((uint32_t)b1 >= (uint32_t)a.num_blocks) b1 = 0;
@@ -217,7 +220,8 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       if (wave == WAVES - 1) {
         // [K scales of key tile 0][K tile 1][V tile 0][V tile 1]: 16 rows x NG floats each
         const int t0 = min(kb0, last_tile), t1 = min(kb0 + 16, last_tile);
-        const int bi0 = t0 / a.block_size, bi1 = t1 / a.block_size;
+        const int bi0 = (int)div_invariant((uint32_t)t0, a.bs_magic, a.bs_shift);
+        const int bi1 = (int)div_invariant((uint32_t)t1, a.bs_magic, a.bs_shift);
         int32_t b0 = bt[bi0], b1 = bt[bi1];
         if ((uint32_t)b0 >= (uint32_t)a.num_blocks) b0 = 0;
         if ((uint32_t)b1 >= (uint32_t)a.num_blocks) b1 = 0;
@@ -385,7 +389,10 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   for (int step = 0; step < n_steps; ++step) {
     // stage step + 2 landed once only the copies of later stages are outstanding
     const int issued = min(n_steps, step + NS);
-    wait_vmcnt(max(0, issued - step - 3) * ipw_me);
+    // (issued - step - 3 is 1, or 0 at the last steps: compile-time counts, no runtime switch)
+    if (issued - step - 3 <= 0) wait_vmcnt_c<0>();
+    else if (SCI > 0 && wave == WAVES - 1) wait_vmcnt_c<IPW + SCI>();
+    else wait_vmcnt_c<IPW>();
     __syncthreads();  // every wave's copies of stage step + 2 landed; every wave left iteration step - 1
     // the copies of step + NS go into the stage of step, whose codes are widened: even waves issue
     // theirs here, odd waves before the PV product, so the memory pipeline takes them in two
@@ -574,6 +581,7 @@ static int launch_pf(const AttnArgs& a, hipStream_t st) {
   p.page_bytes = a.page_bytes;
   p.block_bytes = a.block_bytes;
   p.block_size = a.block_size;
+  invariant_divisor((uint32_t)a.block_size, &p.bs_magic, &p.bs_shift);
   p.num_kv_heads = a.num_kv_heads;
   p.num_q_heads = a.num_q_heads;
   p.group = a.group;
