@@ -190,7 +190,14 @@ extern "C" int aqp_cache_write(const aqp_cache_desc* desc, void* cache, const vo
   a.block_size = desc->block_size;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
-  a.narrow = 2 * num_tokens * desc->num_kv_heads < ((int64_t)1 << 31) && a.total_slots < ((int64_t)1 << 31);
+  a.narrow = 2 * num_tokens * desc->num_kv_heads < ((int64_t)1 << 31) && a.total_slots < ((int64_t)1 << 31) &&
+             desc->num_kv_heads >= 2;
+  a.heads_magic = a.bs_magic = 0;
+  a.heads_shift = a.bs_shift = 0;
+  if (a.narrow) {
+    invariant_divisor((uint32_t)desc->num_kv_heads, &a.heads_magic, &a.heads_shift);
+    invariant_divisor((uint32_t)desc->block_size, &a.bs_magic, &a.bs_shift);
+  }
   return launch_cache_write(desc->dtype, desc->mode, a, stream);
 }
 

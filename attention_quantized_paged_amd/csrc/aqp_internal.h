@@ -91,6 +91,17 @@ constexpr int decode_wgs_per_cu(int head_dim, int32_t lds_bytes) {
              ? 4 * dec_waves_per_simd(head_dim) / (kDecWaves + 1)
              : kLdsPerCu / lds_bytes;
 }
+// Unsigned division by a divisor d >= 2 fixed for a launch, exact for every 32-bit n (division
+// by an invariant integer with a multiply-high, the "round-up" method of Granlund and Montgomery):
+// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1; n / d = (t + ((n - t) >> 1)) >> (l - 1) with
+// t = mulhi(n, m). The host computes (m, l - 1); the kernels apply it (div_invariant).
+inline void invariant_divisor(uint32_t d, uint32_t* m, int32_t* shift) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  *m = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);
+  *shift = l - 1;
+}
+
 // Compute units of the current device (256 on MI355X; 256 when no device is visible).
 int device_cu_count();
 struct SideStream {
@@ -194,6 +205,10 @@ struct CacheWriteArgs {
   int32_t num_kv_heads, head_dim, block_size;
   float k_scale, v_scale;
   int32_t narrow;  // rows (2 x tokens x KV heads) and slots below 2^31: 32-bit index arithmetic
+  // n / num_kv_heads and n / block_size for 32-bit n by multiply-high (set when narrow; the head
+  // count may be 1, which the method does not cover: then narrow is 0)
+  uint32_t heads_magic, bs_magic;
+  int32_t heads_shift, bs_shift;
 };
 int launch_cache_write(int dtype, int mode, const CacheWriteArgs& a, void* stream);
 

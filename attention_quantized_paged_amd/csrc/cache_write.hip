@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
       kv[u] = rr >= per_kv ? 1 : 0;
       const int64_t rem = rr - kv[u] * per_kv;
       // token and head of the row: a 32-bit division whenever the rows fit (uniform branch)
-      const int64_t t = a.narrow ? (int64_t)((uint32_t)rem / (uint32_t)a.num_kv_heads) : rem / a.num_kv_heads;
+      const int64_t t = a.narrow ? (int64_t)div_invariant((uint32_t)rem, a.heads_magic, a.heads_shift) : rem / a.num_kv_heads;
       h[u] = (int)(rem - t * a.num_kv_heads);
       in[u] = *(const uint4*)((kv[u] ? a.v : a.k) + t * a.token_stride + (int64_t)h[u] * D + sub * 8);
       slot[u] = a.slots[t];
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
       }
       const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
       if (!active[u] || slot[u] < 0 || slot[u] >= a.total_slots) continue;
-      const int64_t blk = a.narrow ? (int64_t)((uint32_t)slot[u] / (uint32_t)a.block_size) : slot[u] / a.block_size;
+      const int64_t blk = a.narrow ? (int64_t)div_invariant((uint32_t)slot[u], a.bs_magic, a.bs_shift) : slot[u] / a.block_size;
       const int off = (int)(slot[u] - blk * a.block_size);
       uint8_t* page = a.cache + blk * a.block_bytes + (int64_t)(kv[u] * a.num_kv_heads + h[u]) * a.page_bytes;
       if constexpr (DT == AQP_KV_AUTO) {

@@ -168,16 +168,7 @@ __device__ __forceinline__ T load_const(cptr<T> p) {
   return r;
 }
 
-// Unsigned division by a divisor d >= 2 fixed for the launch, exact for every 32-bit n (division
-// by an invariant integer with a multiply-high, the "round-up" method of Granlund and Montgomery):
-// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1; n / d = (t + ((n - t) >> 1)) >> (l - 1) with
-// t = mulhi(n, m). Uniform operands keep it on the scalar unit.
-inline void invariant_divisor(uint32_t d, uint32_t* m, int32_t* shift) {
-  int l = 0;
-  while ((1ull << l) < d) ++l;
-  *m = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);
-  *shift = l - 1;
-}
+// n / d for the constants of invariant_divisor (uniform operands keep it on the scalar unit)
 __device__ __forceinline__ uint32_t div_invariant(uint32_t n, uint32_t m, int32_t shift) {
   const uint32_t t = __umulhi(n, m);
   return (t + ((n - t) >> 1)) >> shift;
