@@ -163,13 +163,14 @@ int aqp_cache_bytes(const aqp_cache_desc* desc, size_t* page_bytes, size_t* bloc
  *                  value = code * scale.
  * Per row (token, head, K or V), in fp32:
  *   s    = per tensor: the given scale; per token-head: max_d |x_d| / qmax
- *          (qmax = 448 for E4M3, 127 for INT8), stored inline;
+ *          (qmax = 448 for E4M3, 57344 for E5M2, 127 for INT8), stored inline; per
+ *          group: the same over each run of AQP_SCALE_GROUP channels, one scale per run;
  *   inv  = (s == 0) ? 0 : 1 / s  (correctly rounded);
  *   code = fp8: round-to-nearest-even of x_d * inv, saturated to the largest finite code;
  *          int8: round-to-nearest-even, clamped to [-128, 127].
  * AUTO copies the bf16 values unchanged (no scale).
  * Errors: INVALID (null pointers, negative sizes, stride too small), UNSUPPORTED
- * (AUTO with per-token-head mode), HIP. */
+ * (AUTO with a per-token-head or per-group mode), HIP. */
 int aqp_cache_write(const aqp_cache_desc* desc, void* cache, const void* k, const void* v, int64_t num_tokens,
                     int64_t token_stride, const int64_t* slot_mapping, float k_scale, float v_scale, void* stream);
 
@@ -184,8 +185,12 @@ int aqp_cache_write(const aqp_cache_desc* desc, void* cache, const void* k, cons
  *   meta_host:            output buffer of *meta_bytes bytes; NULL = size query only.
  *   meta_bytes:           in: capacity of meta_host; out: bytes needed/written.
  *   scratch_bytes:        out: device scratch aqp_paged_attention needs with this schedule.
- * Sequences with q_len == 1 become decode work, the others prefill work. The
- * metadata is self-contained: it records the parameters and element sizes it
+ * Sequences with q_len == 1 become decode work, the others prefill work.
+ * Decode key ranges are cut into equal runs of 16-key tiles, one per resident
+ * work-group; prefill items (a run of query tokens times a run of one KV head's
+ * q heads) may be cut into key runs (params->prefill_kv_split); split ranges
+ * write partial results to the scratch, merged into the output in the same
+ * call. The metadata is self-contained: it records the parameters and element sizes it
  * was built for, the geometry, and every work item. The caller copies the
  * meta_bytes bytes to device memory unchanged and passes both copies to
  * aqp_paged_attention.
