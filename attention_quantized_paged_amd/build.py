@@ -18,9 +18,9 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libaqp.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 SOURCES = ["aqp_host.cpp", "cache_write.hip", "decode.hip", "prefill.hip"]
-# measurement reference (achievable bf16 MFMA rate), a library of its own loaded only by bench.py
+# measurement references (MFMA rate and clock, gather rate), a library of its own loaded only by bench.py
 PROBE_LIB = os.path.join(HERE, "libaqp_probe.so")
-PROBE_SOURCES = ["mfma_probe.hip"]
+PROBE_SOURCES = ["probes.hip"]
 
 
 def hipcc() -> str:

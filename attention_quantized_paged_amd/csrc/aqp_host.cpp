@@ -653,11 +653,12 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
     if (hipEventRecord(ss->fork, st) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
       return fail(AQP_ERR_HIP, "aqp_paged_attention: fork to the side stream failed");
     rc = run_decode(ss->s);
+    if (rc == AQP_OK) rc = run_prefill(stream);
+    // joined whatever happened after the fork: work already enqueued on the side stream may still
+    // be writing `out` and `scratch`, and the caller's stream must not run ahead of it
+    const bool joined = hipEventRecord(ss->join, ss->s) == hipSuccess && hipStreamWaitEvent(st, ss->join, 0) == hipSuccess;
     if (rc) return rc;
-    rc = run_prefill(stream);
-    if (rc) return rc;
-    if (hipEventRecord(ss->join, ss->s) != hipSuccess || hipStreamWaitEvent(st, ss->join, 0) != hipSuccess)
-      return fail(AQP_ERR_HIP, "aqp_paged_attention: join of the side stream failed");
+    if (!joined) return fail(AQP_ERR_HIP, "aqp_paged_attention: join of the side stream failed");
     return AQP_OK;
   }
   if (h.num_pf_items > 0) {

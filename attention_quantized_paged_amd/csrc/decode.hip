@@ -116,7 +116,8 @@ __device__ __forceinline__ void merge_store(const DecArgs& a, const float* mg, i
       fs = fast_exp2(M_use - Mx);
       L = L * fs + fast_exp2(s2 - Mx);
     }
-    const float norm = a.v_scale * fs / L;
+    // a head with no key left (every block of its range outside the pool) and no sink writes 0
+    const float norm = L > 0.0f ? a.v_scale * fs / L : 0.0f;
     uint16_t* op = a.out + ((int64_t)sg.q_tok * a.num_q_heads + hq) * D;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -274,7 +275,7 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
     }
     // an entry outside the pool masks its tile instead of reading outside the cache
     const bool ok = (uint32_t)is_blk < (uint32_t)a.num_blocks;
-    ok_bits |= (uint64_t)ok << (n_issued & 63);
+    ok_bits = (ok_bits & ~(1ull << (n_issued & 63))) | ((uint64_t)ok << (n_issued & 63));
     const uint8_t* kpage = is_kv + (uint64_t)(ok ? (uint32_t)is_blk : 0u) * (uint64_t)a.block_bytes +
                            (int64_t)is_p.r0 * ROWB;
     const uint8_t* vpage = kpage + (int64_t)a.num_kv_heads * a.page_bytes;
@@ -591,7 +592,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const CombItem* items, cons
     fs = fast_exp2(M_use - Mx);
     L = L * fs + fast_exp2(s2 - Mx);
   }
-  const float inv = fs / L;
+  const float inv = L > 0.0f ? fs / L : 0.0f;  // no key in any part and no sink: 0
   uint16_t* op = out + ((int64_t)it.q_tok * num_q_heads + hq) * D;
 #pragma unroll
   for (int j = 0; j < PER; ++j) op[lane + 64 * j] = f32_to_bf16_rne(o[j] * inv);

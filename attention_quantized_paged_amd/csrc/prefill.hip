@@ -158,6 +158,13 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   const int n_steps = (k_end - k_begin + KT - 1) / KT;
   const float xscale = CAP ? a.logit_scale : a.logit_scale * kLog2e;
   const int last_tile = ((it.L - 1) / kTileKeys) * kTileKeys;  // first key of the tile holding key L-1
+  // whether the block-table entry of the 16-key tile starting at key k0 names a block of the pool
+  // (keys of a tile whose entry lies outside it are absent: masked like keys out of range, and
+  // their codes, read from block 0 instead, never reach a product)
+  auto tile_ok = [&](int k0) {
+    const int t = min(k0, last_tile);
+    return (uint32_t)bt[(int)div_invariant((uint32_t)t, a.bs_magic, a.bs_shift)] < (uint32_t)a.num_blocks;
+  };
 
   float m[RT], l[RT];
   f32x4 acc[RT][NT];
@@ -273,15 +280,20 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   // ---- widen the V codes of one step into its V image: block t holds, for lane l, dim
   // t * 16 + l % 16 of the 8 keys of lane group kg (the A operand of O^T += V^T P^T); the step's
   // K and V scales are copied next to it, so they outlive the ring stage
-  auto convert_v = [&](int step) {
+  // (ok0, ok1: the step's two 16-key tiles lie in blocks of the pool; the codes of an absent tile
+  // become zeros)
+  auto convert_v = [&](int step, bool ok0, bool ok1) {
     const uint8_t* kl = smem + (step % NS) * STAGE;
     uint8_t* slot = smem + VIMG + (step & 1) * VSLOT;
+    const uint32_t msk0 = ok0 ? 0xFFFFFFFFu : 0u, msk1 = ok1 ? 0xFFFFFFFFu : 0u;
     if constexpr (EB == 1) {
       const uint8_t* rp = kl + KT * ROWB + tr_row * ROWB + (r16 & 1) * 8;
 #pragma unroll
       for (int j = 0; j < VB_PW; ++j) {
         const int t = wave * VB_PW + j;
-        const i32x2 c = lds_read_tr8(rp + ((t ^ tr_swz) << 4));
+        i32x2 c = lds_read_tr8(rp + ((t ^ tr_swz) << 4));
+        c.x &= (int)msk0;  // rows i < 4: keys of the first tile
+        c.y &= (int)msk1;
         if constexpr (PG) {
           // element i is key row (i < 4 ? 4kg + i : 16 + 4kg + i - 4) at a head-dim column of
           // group t / 2: bf16(code * that key's scale); keys past L get 0
@@ -291,7 +303,8 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int row = i < 4 ? 4 * kg + i : 16 + 4 * kg + i - 4;
-            const float sc = k_begin + step * KT + row < it.L ? vsc[row * NG + (t >> 1)] : 0.0f;
+            const bool present = k_begin + step * KT + row < it.L && (i < 4 ? ok0 : ok1);
+            const float sc = present ? vsc[row * NG + (t >> 1)] : 0.0f;
             r[i] = (__bf16)((float)e[i] * sc);
           }
           *(bf16x8*)(slot + t * 1024 + lane * 16) = r;
@@ -309,7 +322,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int row = i < 4 ? 4 * kg + i : 16 + 4 * kg + i - 4;
-          e[i] = *(const uint16_t*)(vl + row * ROWB + (((2 * t + (r16 >> 3)) ^ swz<ROWB>(row)) << 4));
+          e[i] = *(const uint16_t*)(vl + row * ROWB + (((2 * t + (r16 >> 3)) ^ swz<ROWB>(row)) << 4)) & (i < 4 ? msk0 : msk1);
         }
         *(uint4*)(slot + t * 1024 + lane * 16) =
             make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
@@ -379,14 +392,18 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
     __syncthreads();  // stages 0 and 1 landed for every wave
     convert_k(0);
     convert_k(1);
-    convert_v(0);
+    convert_v(0, tile_ok(k_begin), tile_ok(k_begin + kTileKeys));
     __syncthreads();
     bf16x8 kw[2][QS];
     read_k(0, kw);
     qk_half(0, kw, s_cur, 0);
     qk_half(1, kw, s_cur, 0);
   }
+  bool cur_ok0 = n_steps > 0 && tile_ok(k_begin), cur_ok1 = n_steps > 0 && tile_ok(k_begin + kTileKeys);
   for (int step = 0; step < n_steps; ++step) {
+    // validity of the next step's tiles (its V codes are widened in this iteration; its keys are
+    // masked in the next)
+    const bool nxt_ok0 = tile_ok(k_begin + (step + 1) * KT), nxt_ok1 = tile_ok(k_begin + (step + 1) * KT + kTileKeys);
     // stage step + 2 landed once only the copies of later stages are outstanding
     const int issued = min(n_steps, step + NS);
     // (issued - step - 3 is 1, or 0 at the last steps: compile-time counts, no runtime switch)
@@ -435,14 +452,14 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
         for (int e = 0; e < 8; ++e) x[rt][e] += slope_r[rt] * (float)(base + (e >> 2) * 16 + (e & 3));
       }
     }
-    const bool full = wave_rows_full && kb0 >= vis_lo && kb0 + KT <= vis_hi && kb0 + KT <= it.L;
+    const bool full = wave_rows_full && kb0 >= vis_lo && kb0 + KT <= vis_hi && kb0 + KT <= it.L && cur_ok0 && cur_ok1;
     if (!full) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = kb0 + (e >> 2) * 16 + 4 * kg + (e & 3);
-          if (!(j >= lo_r[rt] && j < hi_r[rt])) x[rt][e] = -INFINITY;
+          if (!(j >= lo_r[rt] && j < hi_r[rt] && ((e >> 2) == 0 ? cur_ok0 : cur_ok1))) x[rt][e] = -INFINITY;
         }
     }
 
@@ -507,7 +524,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) acc[rt][t] = mfma16x16x32(vw[t], pb[rt], acc[rt][t]);
     convert_k(step + 2);
-    convert_v(step + 1);
+    convert_v(step + 1, nxt_ok0, nxt_ok1);
     // issue order of this block: half the V reads, then each matrix op of S with four vector ops
     // of the softmax, then each PV matrix op with one LDS read and one vector op
     __builtin_amdgcn_sched_group_barrier(0x100, NT / 2, 0);
@@ -527,6 +544,8 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) s_cur[kt][rt] = s_next[kt][rt];
+    cur_ok0 = nxt_ok0;
+    cur_ok1 = nxt_ok1;
   }
 
   // ---- normalise and write the rows (a run of a split item: its partial results instead)
@@ -555,7 +574,8 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       f = fast_exp2(m[rt] - M);
       lt = lt * f + fast_exp2(sink_r[rt] - M);
     }
-    const float norm = a.v_scale * f / lt;
+    // a row with no key left (every block of its range outside the pool) and no sink writes 0
+    const float norm = lt > 0.0f ? a.v_scale * f / lt : 0.0f;
     uint16_t* op = a.out + orow[rt];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {

@@ -3,7 +3,10 @@
  *
  * C ABI of the library (libaqp.so). Plain pointers and sizes only; every
  * device buffer is allocated and owned by the caller; the library allocates no
- * device memory and keeps no state beyond a per-thread last-error message.
+ * device memory. State it keeps: a per-thread last-error message, and per device
+ * one second stream with two events (hipStreamNonBlocking, default priority),
+ * created by the first mixed decode + prefill batch on that device and kept
+ * until the process ends (see aqp_paged_attention).
  *
  * The operations follow three pages summarising vLLM pull requests:
  *  [P39445] "CPU backend adds FP8 KV-cache quantisation" (PR 39445)
@@ -206,7 +209,14 @@ int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_desc* desc, 
  * unified varlen attention).
  *   q:            bf16 [T_q, Hq, head_dim] contiguous, T_q = qsl[num_seqs].
  *   block_tables: int32 [num_seqs, max_blocks_per_seq]: physical block of each logical block.
- *   meta_host / meta_dev: the same schedule bytes, in host and device memory.
+ *                 Only the entries of blocks that hold a sequence's keys are read. An entry
+ *                 outside [0, num_blocks) names no block: the keys of that logical block are
+ *                 absent and take no part in the softmax (as if masked); the kernels read block
+ *                 0 in its place and discard it, so no address leaves the cache. A row left with
+ *                 no key and no sink is written as zeros.
+ *   meta_host / meta_dev: the same schedule bytes, in host and device memory. The schedule
+ *                 carries the batch's sequence lengths and query start locations (it was built
+ *                 from them by aqp_get_schedule), so they are not passed again here.
  *   k_scale, v_scale: per-tensor mode only.
  *   scratch:      device buffer of at least the schedule's scratch_bytes (may be NULL if 0): the
  *                 partial results of split decode ranges and split prefill items.
@@ -214,6 +224,10 @@ int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_desc* desc, 
  * Per query row: z_j = sm_scale * q . k_j (k_j dequantised), soft-capped if
  * set, masked by causality and window; softmax over the visible keys; output
  * = sum_j p_j v_j rounded to bf16.
+ * A batch with both decode and prefill sequences runs its decode kernel on the
+ * device's second stream (see the top of this file), forked from `stream` by an
+ * event and joined back into it before the call returns, also when a launch
+ * fails; the work is complete when `stream`'s work up to this call is.
  * Errors: INVALID, SCHEDULE_MISMATCH (schedule built for another cache
  * descriptor, dtype, element size or parameter set), SCRATCH_TOO_SMALL, HIP. */
 int aqp_paged_attention(const aqp_attn_params* params, const aqp_cache_desc* desc, const void* cache,

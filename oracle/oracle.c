@@ -325,17 +325,27 @@ static int check_args(const orc_cache_desc* d, const int32_t* seq_lens, const in
   return 0;
 }
 
-/* Gather dequantised K and V rows [lo, L) of (b, kvh) into kk, vv ([n][D]). */
-static int gather(const orc_ctx* c, int b, int kvh, int32_t lo, int32_t L, double* kk, double* vv) {
+/* Gather dequantised K and V rows [lo, L) of (b, kvh) into kk, vv ([n][D]). A key whose
+ * block-table entry lies outside the pool [0, num_blocks) has no row to read: its flag in
+ * `present` is 0 and its rows are zeros; such keys take no part in the softmax (reading: a
+ * table entry that names no block of the pool marks that block's keys as absent, the same as
+ * a masked key). */
+static void gather(const orc_ctx* c, int b, int kvh, int32_t lo, int32_t L, double* kk, double* vv,
+                   unsigned char* present) {
   const orc_cache_desc* d = c->d;
   for (int32_t j = lo; j < L; ++j) {
     int32_t blk = c->block_tables[(int64_t)b * c->max_blocks + j / d->block_size];
-    if (blk < 0 || blk >= d->num_blocks) return -1;
+    double* kr = kk + (int64_t)(j - lo) * d->head_dim;
+    double* vr = vv + (int64_t)(j - lo) * d->head_dim;
+    present[j - lo] = blk >= 0 && blk < d->num_blocks;
+    if (!present[j - lo]) {
+      for (int dd = 0; dd < d->head_dim; ++dd) kr[dd] = vr[dd] = 0.0;
+      continue;
+    }
     int off = j % d->block_size;
-    orc_read_row(d, c->cache, 0, blk, kvh, off, c->k_scale, c->v_scale, kk + (int64_t)(j - lo) * d->head_dim);
-    orc_read_row(d, c->cache, 1, blk, kvh, off, c->k_scale, c->v_scale, vv + (int64_t)(j - lo) * d->head_dim);
+    orc_read_row(d, c->cache, 0, blk, kvh, off, c->k_scale, c->v_scale, kr);
+    orc_read_row(d, c->cache, 1, blk, kvh, off, c->k_scale, c->v_scale, vr);
   }
-  return 0;
 }
 
 static void key_range(int32_t L, int32_t ql, int32_t i, int32_t causal, int32_t window, int32_t* lo, int32_t* hi) {
@@ -347,14 +357,16 @@ static void key_range(int32_t L, int32_t ql, int32_t i, int32_t causal, int32_t 
 /* Weights of one row (query at position p) over the gathered keys [lo0, ...): w has (L - lo0)
  * entries. Logit of key j: z = sm_scale * q.k_j, soft-capped (cap * tanh(z / cap)) if cap > 0,
  * plus the linear position bias slope * (j - p) (ALiBi; slope 0 = none). The softmax runs over
- * the visible keys and, if sink is finite, one more logit `sink` that has no value row: it only
- * adds exp(sink - m) to the normaliser, so the key weights sum to less than one. */
-static void row_weights(const double* qrow, const double* kk, int32_t lo0, int32_t lo, int32_t hi, int D,
-                        double sm_scale, double softcap, double slope, int32_t p, double sink, double* w,
-                        int32_t n) {
+ * the visible keys that are present (see gather) and, if sink is finite, one more logit `sink`
+ * that has no value row: it only adds exp(sink - m) to the normaliser, so the key weights sum to
+ * less than one. A row left with no key and no sink has all weights 0 (its output is 0). */
+static void row_weights(const double* qrow, const double* kk, const unsigned char* present, int32_t lo0,
+                        int32_t lo, int32_t hi, int D, double sm_scale, double softcap, double slope, int32_t p,
+                        double sink, double* w, int32_t n) {
   double m = sink;  /* -inf when there is no sink */
   for (int32_t j = 0; j < n; ++j) w[j] = 0.0;
   for (int32_t j = lo; j <= hi; ++j) {
+    if (!present[j - lo0]) continue;
     const double* kr = kk + (int64_t)(j - lo0) * D;
     double dot = 0.0;
     for (int dd = 0; dd < D; ++dd) dot += qrow[dd] * kr[dd];
@@ -364,8 +376,16 @@ static void row_weights(const double* qrow, const double* kk, int32_t lo0, int32
     w[j - lo0] = z;
     if (z > m) m = z;
   }
+  if (isinf(m) && m < 0) {  /* nothing to attend to */
+    for (int32_t j = 0; j < n; ++j) w[j] = 0.0;
+    return;
+  }
   double l = isinf(sink) ? 0.0 : exp(sink - m);
-  for (int32_t j = lo; j <= hi; ++j) { w[j - lo0] = exp(w[j - lo0] - m); l += w[j - lo0]; }
+  for (int32_t j = lo; j <= hi; ++j) {
+    if (!present[j - lo0]) continue;
+    w[j - lo0] = exp(w[j - lo0] - m);
+    l += w[j - lo0];
+  }
   for (int32_t j = lo; j <= hi; ++j) w[j - lo0] /= l;
 }
 
@@ -407,10 +427,12 @@ int orc_attention_ext(const orc_cache_desc* d, const uint8_t* cache, const uint1
     double* w = (double*)malloc(sizeof(double) * (size_t)n);
     double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
     double* o = (double*)malloc(sizeof(double) * (size_t)D);
-    if (!kk || !vv || !w || !qrow || !o || gather(&c, b, kvh, lo0, L, kk, vv)) {
+    unsigned char* present = (unsigned char*)malloc((size_t)(n > 0 ? n : 1));
+    if (!kk || !vv || !w || !qrow || !o || !present) {
 #pragma omp atomic write
       failed = 1;
     } else {
+      gather(&c, b, kvh, lo0, L, kk, vv, present);
       for (int32_t i = 0; i < ql; ++i) {
         int32_t lo, hi;
         key_range(L, ql, i, cz, window, &lo, &hi);
@@ -419,7 +441,7 @@ int orc_attention_ext(const orc_cache_desc* d, const uint8_t* cache, const uint1
           const int hq = kvh * G + g;
           const uint16_t* qsrc = q + (tok * Hq + hq) * D;
           for (int dd = 0; dd < D; ++dd) qrow[dd] = (double)orc_bf16_to_f32(qsrc[dd]);
-          row_weights(qrow, kk, lo0, lo, hi, D, sm_scale, softcap, alibi_slopes ? alibi_slopes[hq] : 0.0,
+          row_weights(qrow, kk, present, lo0, lo, hi, D, sm_scale, softcap, alibi_slopes ? alibi_slopes[hq] : 0.0,
                       L - ql + i, sinks ? sinks[hq] : -INFINITY, w, n);
           for (int dd = 0; dd < D; ++dd) o[dd] = 0.0;
           for (int32_t j = lo; j <= hi; ++j) {
@@ -434,7 +456,7 @@ int orc_attention_ext(const orc_cache_desc* d, const uint8_t* cache, const uint1
         }
       }
     }
-    free(kk); free(vv); free(w); free(qrow); free(o);
+    free(kk); free(vv); free(w); free(qrow); free(o); free(present);
   }
   return failed ? -1 : 0;
 }
@@ -469,13 +491,15 @@ int orc_attention_weights_ext(const orc_cache_desc* d, const uint8_t* cache, con
   double* kk = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * D);
   double* vv = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * D);
   double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
+  unsigned char* present = (unsigned char*)malloc((size_t)(L > 0 ? L : 1));
   int rc = -1;
-  if (kk && vv && qrow && gather(&c, b, hq / G, 0, L, kk, vv) == 0) {
+  if (kk && vv && qrow && present) {
+    gather(&c, b, hq / G, 0, L, kk, vv, present);
     const int64_t tok = (int64_t)query_start_loc[b] + i;
     for (int dd = 0; dd < D; ++dd) qrow[dd] = (double)orc_bf16_to_f32(q[(tok * num_q_heads + hq) * D + dd]);
-    row_weights(qrow, kk, 0, lo, hi, D, sm_scale, softcap, alibi_slope, L - ql + i, sink, w, L);
+    row_weights(qrow, kk, present, 0, lo, hi, D, sm_scale, softcap, alibi_slope, L - ql + i, sink, w, L);
     rc = 0;
   }
-  free(kk); free(vv); free(qrow);
+  free(kk); free(vv); free(qrow); free(present);
   return rc;
 }

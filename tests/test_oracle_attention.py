@@ -215,3 +215,50 @@ def test_invalid_arguments_rejected():
         oracle.attention(c.desc, c.cache, c.q, c.bt, c.seq_lens, c.qsl, 3)  # Hq not a multiple of Hkv
     with pytest.raises(ValueError):
         oracle.attention(c.desc, c.cache, c.q, c.bt, c.seq_lens, c.qsl, 4, causal=False, window=4)
+
+
+def test_absent_blocks_match_sdpa_with_masked_keys():
+    """A block-table entry outside the pool (negative, or >= num_blocks) names no block: the keys of
+    that logical block take no part in the softmax. Pinned against fp64 SDPA whose additive mask is
+    -inf on exactly those keys (on top of the causal mask); a row left with no key at all gives 0."""
+    seqs = [(1, 50), (9, 40), (20, 20), (1, 10)]
+    c = Case(seqs, 8, 2, 64, seed=21)
+    nb = c.desc.num_blocks
+    bt = c.bt.copy()
+    bt[0, 1] = -1          # keys 16..31 of the first decode
+    bt[1, 0] = nb + 7      # keys 0..15 of the chunk (its first queries see nothing else but later keys)
+    bt[2, 1] = nb          # the prefill's keys 16..19
+    bt[3, 0] = -5          # the last decode has no key left
+    _, o64 = oracle.attention(c.desc, c.cache, c.q, bt, c.seq_lens, c.qsl, c.hq, k_scale=c.s, v_scale=2 * c.s,
+                              want_f64=True)
+    qf = bf16_to_f32(c.q).astype(np.float64)
+    g = c.hq // c.hkv
+    for b, (ql, L) in enumerate(seqs):
+        k, v = c.kv_of(b)
+        absent = np.array([not (0 <= bt[b, j // c.bs] < nb) for j in range(L)])
+        pos = L - ql + np.arange(ql)
+        mask = np.where((np.arange(L)[None, :] <= pos[:, None]) & ~absent[None, :], 0.0, -np.inf)
+        qt = torch.from_numpy(qf[c.qsl[b]:c.qsl[b + 1]]).permute(1, 0, 2)[None]
+        kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(g, dim=0)[None]
+        vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(g, dim=0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask))
+        ref = ref[0].permute(1, 0, 2).numpy()
+        empty = np.all(np.isinf(mask), axis=1)
+        ref[empty] = 0.0  # SDPA leaves NaN where a row has no key; the reading gives 0
+        np.testing.assert_allclose(o64[c.qsl[b]:c.qsl[b + 1]], ref, rtol=1e-10, atol=1e-12)
+    assert np.all(o64[c.qsl[3]] == 0.0)
+    # with the table intact the first decode's row differs: the entry is not ignored
+    full = c.run(want_f64=True)[1]
+    assert not np.allclose(full[c.qsl[0]], o64[c.qsl[0]])
+
+
+def test_absent_block_with_sink_gives_zero_and_keeps_weights_finite():
+    c = Case([(1, 10)], 4, 2, 64, seed=22)
+    bt = c.bt.copy()
+    bt[0, 0] = -1
+    out = oracle.attention(c.desc, c.cache, c.q, bt, c.seq_lens, c.qsl, c.hq, k_scale=c.s, v_scale=2 * c.s,
+                           sinks=np.full(c.hq, 0.5))
+    assert np.all(out == 0)
+    w = oracle.attention_weights(c.desc, c.cache, c.q, bt, c.seq_lens, c.qsl, c.hq, 0, 0, 1, k_scale=c.s,
+                                 v_scale=2 * c.s)
+    assert np.all(w == 0)
