@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libaqp.so")
 OBJ_DIR = os.path.join(HERE, "_build")
-SOURCES = ["aqp_host.cpp", "cache_write.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["aqp_host.cpp", "cache_write.hip", "decode.hip", "prefill.hip", "prefill32.hip"]
 # measurement references (MFMA rate and clock, gather rate), a library of its own loaded only by bench.py
 PROBE_LIB = os.path.join(HERE, "libaqp_probe.so")
 PROBE_SOURCES = ["probes.hip"]

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <map>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -66,11 +67,16 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
   g->page_bytes = round_up((int64_t)d.block_size * d.head_dim * g->kv_elem_bytes + (int64_t)d.block_size * g->scale_bytes, 128);
   g->block_bytes = 2 * (int64_t)d.num_kv_heads * g->page_bytes;
   g->total_bytes = (int64_t)d.num_blocks * g->block_bytes;
-  // Prefill work-group: a ring of kPfStages steps, each the K and V codes of kPfKvTile keys
-  // plus their row scales; then two K and two V operand images of a step in bf16 (the codes
-  // widened once per work-group), each V image followed by a copy of its step's scales.
-  g->pf_lds_bytes = kPfStages * (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes + pf_stage_scale_bytes(d.head_dim, d.mode)) +
-                    4 * kPfKvTile * d.head_dim * kPfOperandBytes + 2 * (2 * kPfKvTile * 4);
+  // Prefill work-group. The 32x32 kernel: a ring of kPf32Stages steps of codes (and scales) and
+  // two V images of a step in bf16. The 16x16 kernel (per-group scales, unquantised cache): a
+  // ring of kPfStages steps, each the K and V elements of kPfKvTile keys plus their row scales;
+  // then two K and two V operand images of a step in bf16 (widened once per work-group), each V
+  // image followed by a copy of its step's scales.
+  if (pf32_applies(d.dtype, d.mode, d.head_dim))
+    g->pf_lds_bytes = pf32_lds_bytes(d.head_dim, d.mode);
+  else
+    g->pf_lds_bytes = kPfStages * (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes + pf_stage_scale_bytes(d.head_dim, d.mode)) +
+                      4 * kPfKvTile * d.head_dim * kPfOperandBytes + 2 * (2 * kPfKvTile * 4);
   return AQP_OK;
 }
 
@@ -392,7 +398,9 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
     SplitPlan sp{1, kPfMinSplitSteps, 1};
     int64_t total_steps = 0;
     for (const PfItem& it : pf) total_steps += steps_of(it);
-    const int64_t cap = (int64_t)device_cu_count() * pf_wgs_per_cu(desc->head_dim, rows, g.pf_lds_bytes);
+    const int64_t cap = (int64_t)device_cu_count() *
+                        (pf32_applies(desc->dtype, desc->mode, desc->head_dim) ? pf32_wgs_per_cu(desc->head_dim, rows, g.pf_lds_bytes)
+                                                               : pf_wgs_per_cu(desc->head_dim, rows, g.pf_lds_bytes));
     if (p.prefill_kv_split > 1) {
       sp.max_runs = p.prefill_kv_split;
       sp.min_steps = 1;
@@ -411,7 +419,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   // the prefill and needs the room a second work-group takes), kPfRowsSmall when kPfRows-row items,
   // even after key splits, would give the CUs fewer than two work-groups each
   int32_t pf_rows = p.prefill_rows > 0 ? p.prefill_rows : kPfRows;
-  if (pf_rows < pf_waves(desc->head_dim) * 16)
+  if (!pf32_applies(desc->dtype, desc->mode, desc->head_dim) && pf_rows < pf_waves(desc->head_dim) * 16)
     return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: %d rows per prefill item at head_dim %d is not built", pf_rows, desc->head_dim);
   build_items(pf_rows);
   if (p.prefill_rows == 0 && desc->head_dim <= 128 && total_tiles == 0 && !pf.empty()) {
@@ -459,9 +467,56 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
       }
     }
   }
-  if (pf.size() > 1) std::stable_sort(pf.begin(), pf.end(), [&](const PfItem& x, const PfItem& y) {
-    return steps_of(x) > steps_of(y);
-  });
+  // ---- order of the prefill items. The items of one (sequence, KV head) read the same K and V, and
+  // work-group i runs on XCD i % kXcds, each XCD with an L2 of its own: so the items are packed into
+  // kXcds bins of about equal work, a group at a time (largest first, a group larger than a bin's
+  // share spilling into the next emptiest bin), so that a group's K and V are read into few L2s;
+  // each bin's items run longest first, and the bins are interleaved into the launch order. Bins
+  // short of items are padded with empty items (no rows and no keys: the kernels return at once).
+  if (pf.size() >= (size_t)kXcds) {
+    std::map<std::pair<int32_t, int32_t>, std::vector<size_t>> groups;
+    for (size_t i = 0; i < pf.size(); ++i) groups[{pf[i].seq, pf[i].kvh}].push_back(i);
+    auto work = [&](size_t i) { return std::max<int64_t>(1, steps_of(pf[i])); };
+    std::vector<std::pair<int64_t, const std::vector<size_t>*>> order;
+    int64_t total = 0;
+    for (auto& g : groups) {
+      int64_t w = 0;
+      for (size_t i : g.second) w += work(i);
+      total += w;
+      order.push_back({w, &g.second});
+    }
+    std::stable_sort(order.begin(), order.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+    const int64_t share = (total + kXcds - 1) / kXcds;
+    std::vector<int64_t> load(kXcds, 0);
+    std::vector<std::vector<size_t>> bins(kXcds);
+    auto emptiest = [&]() { return (int)(std::min_element(load.begin(), load.end()) - load.begin()); };
+    for (auto& g : order) {
+      std::vector<size_t> its = *g.second;
+      std::stable_sort(its.begin(), its.end(), [&](size_t x, size_t y) { return work(x) > work(y); });
+      int b = emptiest();
+      for (size_t i : its) {
+        if (load[b] > 0 && load[b] + work(i) > share) b = emptiest();
+        bins[b].push_back(i);
+        load[b] += work(i);
+      }
+    }
+    size_t per = 0;
+    for (auto& bn : bins) {
+      std::stable_sort(bn.begin(), bn.end(), [&](size_t x, size_t y) { return work(x) > work(y); });
+      per = std::max(per, bn.size());
+    }
+    PfItem empty{};
+    empty.L = 1;
+    empty.ql = 1;
+    empty.nheads = 1;
+    empty.slot = -1;
+    std::vector<PfItem> out(per * kXcds, empty);
+    for (int b = 0; b < kXcds; ++b)
+      for (size_t j = 0; j < bins[b].size(); ++j) out[j * kXcds + b] = pf[bins[b][j]];
+    pf.swap(out);
+  } else if (pf.size() > 1) {
+    std::stable_sort(pf.begin(), pf.end(), [&](const PfItem& x, const PfItem& y) { return steps_of(x) > steps_of(y); });
+  }
 
   // ---- sizes and layout
   int64_t off = round_up(sizeof(SchedHeader), 256);
@@ -638,7 +693,8 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
     return r;
   };
   auto run_prefill = [&](void* st) -> int {
-    int r = launch_prefill(desc->dtype, desc->mode, a, st);
+    int r = pf32_applies(desc->dtype, desc->mode, desc->head_dim) ? launch_prefill32(desc->dtype, desc->mode, a, st)
+                                                  : launch_prefill(desc->dtype, desc->mode, a, st);
     if (r == AQP_OK && n_pf_comb > 0) r = launch_combine(a, n_dec_comb, n_pf_comb, st);
     return r;
   };

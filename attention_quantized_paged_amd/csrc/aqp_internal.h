@@ -48,12 +48,42 @@ constexpr int kPfMaxSplit = 8;
 constexpr int kCwRowsPerLane = 4;    // cache write: rows each lane loads before converting
 constexpr int kCwWgsPerCu = 16;      // cache write: resident work-groups per CU (grid cap)
 constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per compute unit (gfx950)
+// Accelerator dies (XCDs) of the chip, each with its own L2: work-group i of a launch runs on XCD
+// i % kXcds.
+constexpr int kXcds = 8;
 // Prefill work-groups a CU holds at once: the register limit of the compiled kernel (8 waves at two
 // per SIMD at head_dim 256; 4 waves at two per SIMD at 128 rows and head_dim 128, three below)
 // and the LDS limit.
 constexpr int pf_wgs_per_cu(int head_dim, int rows, int32_t lds_bytes) {
   return (head_dim >= 256 ? 1 : (head_dim == 128 && rows > kPfRowsSmall ? 2 : 3)) < kLdsPerCu / lds_bytes
              ? (head_dim >= 256 ? 1 : (head_dim == 128 && rows > kPfRowsSmall ? 2 : 3))
+             : kLdsPerCu / lds_bytes;
+}
+// The 32x32 prefill kernel (prefill32.hip) serves one-byte codes with per-tensor or per-token-head
+// scales up to head_dim 128, where it runs two waves per SIMD; per-group scales, the unquantised
+// cache and head_dim 256 keep the 16x16 kernel (prefill.hip), which was measured faster there
+// (a single wave per SIMD hides little of its vector work under its matrix instructions).
+constexpr bool pf32_applies(int dtype, int mode, int head_dim) {
+  return head_dim <= 128 && dtype != AQP_KV_AUTO && (mode == AQP_SCALE_PER_TENSOR || mode == AQP_SCALE_PER_TOKEN_HEAD);
+}
+constexpr int kPf32Stages = 4;  // LDS ring stages of the 32x32 prefill (three steps ahead)
+// Waves per SIMD its registers are sized for: a wave holds 32 rows of Q (D/4 registers), their
+// fp32 output (D/2), the next step's K operands (D/4) and two S tiles.
+constexpr int pf32_waves_per_simd(int head_dim) { return head_dim >= 256 ? 1 : (head_dim == 128 ? 2 : 3); }
+// Ring stage: the codes of kPfKvTile keys of K and of V, then (per token-head) their fp32 scales.
+constexpr int pf32_stage_bytes(int head_dim, int mode) {
+  return 2 * kPfKvTile * head_dim + (mode == AQP_SCALE_PER_TOKEN_HEAD ? 2 * kPfKvTile * 4 : 0);
+}
+// LDS of one 32x32 prefill work-group: the ring, then two slots each holding a step's V image
+// (bf16, kPfKvTile x head_dim).
+// Then the block-table entries of two batches of 64 tiles for each of up to 4 waves (4 bytes each).
+constexpr int kPf32TableBytes = 2 * 4 * 64 * 4;
+constexpr int32_t pf32_lds_bytes(int head_dim, int mode) {
+  return kPf32Stages * pf32_stage_bytes(head_dim, mode) + 2 * kPfKvTile * head_dim * 2 + kPf32TableBytes;
+}
+constexpr int pf32_wgs_per_cu(int head_dim, int rows, int32_t lds_bytes) {
+  return 4 * pf32_waves_per_simd(head_dim) / (rows / 32) < kLdsPerCu / lds_bytes
+             ? 4 * pf32_waves_per_simd(head_dim) / (rows / 32)
              : kLdsPerCu / lds_bytes;
 }
 // fp32 scales stored per cache row: none per tensor, one per token-head, head_dim / 32 per group
@@ -231,6 +261,7 @@ int launch_decode(int dtype, int mode, const AttnArgs& a, void* stream);
 // merges items [first, first + count) of the schedule's merge items (one wave per (item, head))
 int launch_combine(const AttnArgs& a, int32_t first, int32_t count, void* stream);
 int launch_prefill(int dtype, int mode, const AttnArgs& a, void* stream);
+int launch_prefill32(int dtype, int mode, const AttnArgs& a, void* stream);
 
 void set_error(const char* fmt, ...);
 

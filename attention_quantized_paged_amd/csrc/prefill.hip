@@ -98,6 +98,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   const int r16 = lane & 15;
   const int kg = lane >> 4;
   const PfItem it = load_const(as_const(a.items) + blockIdx.x);
+  if (it.q_hi <= it.q_lo) return;  // an empty item (launch-order padding)
   const int G = a.group;
   const int nh = it.nheads;  // q heads per token in this item
   const int ntok = it.q_hi - it.q_lo;

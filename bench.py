@@ -51,12 +51,24 @@ def parse():
     ap.add_argument("--mfma-probe", action="store_true",
                     help="time a large bf16 GEMM from the vendor library and hand-written MFMA loops (two shapes), "
                          "with the shader clock they ran at")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="LDS read rate (16-byte reads and 8-bit transposed reads) and the result layout of the "
+                         "32x32x16 bf16 MFMA, checked on the host")
+    ap.add_argument("--stage-probe", action="store_true",
+                    help="staging 1 KB pages into LDS three ways (direct global -> LDS copies, register loads, "
+                         "register loads plus LDS writes) at the prefill's occupancy")
     ap.add_argument("--gather-probe", action="store_true",
                     help="plain vector loads of the decode batch's K and V pages in the decode's order: the "
                          "achievable rate of that access pattern")
     ap.add_argument("--all-configs", action="store_true",
                     help="one JSON line per configuration (1-5): cache write of its history and one "
                          "attention call, median kernel times with a 1 GiB read between repetitions")
+    ap.add_argument("--only", default="",
+                    help="with --all-configs: comma-separated workload names to run (default: all)")
+    ap.add_argument("--no-oracle", action="store_true",
+                    help="with --all-configs: skip the oracle's CPU timing")
+    ap.add_argument("--reps", type=int, default=20,
+                    help="with --all-configs: timed repetitions of each attention call")
     return ap.parse_args()
 
 
@@ -283,7 +295,10 @@ def run_all_configs(torch, aqp, W, args):
     # the decode batch once more over an unquantised (bf16, "auto") cache: the same kernels with
     # two-byte elements, for the quantisation's bandwidth saving side by side
     auto3 = W.scaled(W.CFG3, name="decode64_bf16_auto_llama8b", kv_dtype="auto")
+    only = set(x for x in args.only.split(",") if x)
     for w in (W.CFG1, W.CFG2, W.CFG3, W.CFG4, W.CFG5A, W.CFG5B, auto3):
+        if only and w.name not in only:
+            continue
         log(args, f"[bench] {w.name}")
         b = W.make_batch(w, with_kv=False)
         desc = aqp.cache_desc(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
@@ -317,7 +332,7 @@ def run_all_configs(torch, aqp, W, args):
         att = lambda: aqp.paged_attention(params, desc, cache, q, bt, sch.meta, md, ks, vs, scr, scr.numel(), out)
         for _ in range(3):
             att()
-        att_ms = timed(att, 20, key="attention")
+        att_ms = timed(att, args.reps, key="attention")
         parts = {}
         qlens = b.query_start_loc[1:] - b.query_start_loc[:-1]
         if (qlens == 1).any() and (qlens > 1).any():
@@ -338,33 +353,34 @@ def run_all_configs(torch, aqp, W, args):
                                                  scrp.numel(), op)
                 for _ in range(3):
                     fn()
-                parts[kind] = timed(fn, 20, key=kind)
+                parts[kind] = timed(fn, args.reps, key=kind)
         kvb = W.kv_read_bytes(w, per_token_head=pth) * eb
         fl = W.prefill_flops(w)
         # the oracle on the host's cores: its own cache write of the same history, then one
         # attention call over the whole batch (three when the first takes under three seconds)
-        od = oracle.CacheDesc(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, ofmt[desc.dtype], desc.mode)
-        ocache = np.zeros(od.total_bytes, dtype=np.uint8)
-        oracle.cache_write(od, ocache, kh, vh, b.slots_hist, ks, vs)
-        del kh, vh
-        qh = host16(q)
         ots = []
-        while len(ots) < 3 and (not ots or ots[0] < 3.0):
-            t0 = time.perf_counter()
-            oracle.attention(od, ocache, qh, b.block_tables, b.seq_lens, b.query_start_loc, w.num_q_heads,
-                             causal=w.causal, window=w.window, softcap=w.softcap, k_scale=ks, v_scale=vs)
-            ots.append(time.perf_counter() - t0)
-        del ocache
-        o_s = float(np.median(ots))
+        if not args.no_oracle:
+            od = oracle.CacheDesc(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, ofmt[desc.dtype], desc.mode)
+            ocache = np.zeros(od.total_bytes, dtype=np.uint8)
+            oracle.cache_write(od, ocache, kh, vh, b.slots_hist, ks, vs)
+            qh = host16(q)
+            while len(ots) < 3 and (not ots or ots[0] < 3.0):
+                t0 = time.perf_counter()
+                oracle.attention(od, ocache, qh, b.block_tables, b.seq_lens, b.query_start_loc, w.num_q_heads,
+                                 causal=w.causal, window=w.window, softcap=w.softcap, k_scale=ks, v_scale=vs)
+                ots.append(time.perf_counter() - t0)
+            del ocache
+        del kh, vh
+        o_s = float(np.median(ots)) if ots else float("nan")
         row = {"workload": w.name, "kv_cache_dtype": w.kv_dtype, "attention_ms": round(att_ms, 4),
                "attention_ms_p10_p90": spread["attention"],
                "cache_write": {"tokens": n, "ms": round(cw_ms, 4), "gbs": round(cw_bytes / cw_ms / 1e6, 1),
                                "frac_of_hbm_peak": round(cw_bytes / cw_ms / 1e6 / HBM_PEAK_GBS, 4)},
                "oracle_cpu": {"attention_s": round(o_s, 3), "calls": len(ots), "cores": oracle.num_threads(),
-                              "kind": "oracle"}}
-        if kvb:
+                              "kind": "oracle"} if ots else None}
+        if kvb and ots:
             row["oracle_cpu"]["decode_gbs"] = round(kvb / o_s / 1e9, 3)
-        if fl:
+        if fl and ots:
             row["oracle_cpu"]["prefill_gflops"] = round(fl / o_s / 1e9, 2)
         if kvb:
             row["decode_kv_bytes"] = kvb
@@ -416,7 +432,156 @@ def probe_lib():
     i32, i64, P = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     lib.aqp_probe_mfma_loop.argtypes = [i32, i32, i32, i32, P, P]
     lib.aqp_probe_gather.argtypes = [P, P, i64, i32, i32, i32, P, P]
+    lib.aqp_probe_mfma_chain.argtypes = [i32, i32, i32, P, P]
+    lib.aqp_probe_mfma32_layout.argtypes = [P, P, P, P]
+    lib.aqp_probe_lds_read.argtypes = [i32, i32, i32, P, P]
+    lib.aqp_probe_stage.argtypes = [P, P, i64, i32, i32, i32, i32, P, P]
+    lib.aqp_probe_xcc.argtypes = [i32, P, P]
+    lib.aqp_probe_mfma_valu.argtypes = [i32, i32, i32, i32, i32, P, P]
     return lib
+
+
+def mfma_valu_probe(torch):
+    """Cycles per 32x32x16 MFMA when each is followed by nv independent fp32 multiply-adds, at one
+    wave per SIMD (96 KB of LDS per work-group of 4 waves) and at two: whether a wave's vector ALU
+    instructions run under its own MFMAs."""
+    lib = probe_lib()
+    cus = lib.aqp_probe_cu_count()
+    st = torch.cuda.current_stream().cuda_stream
+    for wps, lds in ((1, 96 * 1024), (2, 64 * 1024)):
+        blocks = cus * wps
+        out = torch.zeros(blocks * 4 * 5, dtype=torch.int64, device="cuda")
+        for nacc in (1, 2):
+            for nv in (0, 4, 8, 12, 16, 24):
+                iters = 200
+                launch = lambda: lib.aqp_probe_mfma_valu(nv, nacc, blocks, iters, lds, out.data_ptr(), st)
+                ms, clk, cyc = _clock_and_time(torch, launch, 3, out)
+                per = float(np.median(cyc)) / (iters * 8 * nacc)
+                print(json.dumps({"mfma_valu": "32x32x16 bf16 + fp32 fma", "waves_per_simd": wps, "chains": nacc,
+                                  "fma_per_mfma": nv, "cycles_per_mfma": round(per, 2), "clock_mhz": round(clk, 1)}),
+                      flush=True)
+
+
+def xcc_probe(torch):
+    """The die (XCD) each work-group of a launch runs on, as the launch order maps them."""
+    lib = probe_lib()
+    st = torch.cuda.current_stream().cuda_stream
+    for blocks in (64, 4096):
+        out = torch.full((blocks,), -1, dtype=torch.int32, device="cuda")
+        assert lib.aqp_probe_xcc(blocks, out.data_ptr(), st) == 0
+        torch.cuda.synchronize()
+        x = out.cpu().numpy()
+        rr = bool(np.all(x == np.arange(blocks) % 8))
+        print(json.dumps({"xcc_probe_blocks": blocks, "first_32": x[:32].tolist(), "round_robin_mod_8": rr,
+                          "counts": np.bincount(x[x >= 0], minlength=8).tolist()}), flush=True)
+
+
+def stage_probe(torch):
+    """Rates of the three ways of staging 1 KB pages into LDS (direct global -> LDS copies, plain
+    register loads, register loads plus LDS writes) at the prefill's occupancy (one or two
+    work-groups of 4 waves per CU), from an L2-sized buffer (4 MB, the prefill's shared K and V)
+    and from a 2 GiB one (HBM)."""
+    lib = probe_lib()
+    cus = lib.aqp_probe_cu_count()
+    st = torch.cuda.current_stream().cuda_stream
+    for label, nbytes in (("4MB", 4 << 20), ("2GiB", 2 << 30)):
+        buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        rng = np.random.default_rng(7)
+        npg = nbytes // 1024
+        # every wave reads 256 pages: sequential runs (as the prefill's 1 KB copies of consecutive
+        # rows), the runs in random order
+        runs = rng.permutation(npg // 16)
+        for wgs in (1, 2):
+            blocks = wgs * cus
+            total = blocks * 4 * 256
+            pg = (runs[np.arange(total // 16) % runs.size][:, None] * 16 + np.arange(16)[None, :]).reshape(-1)[:total]
+            pages = (pg.astype(np.int64) * 1024)
+            assert pages.min() >= 0 and pages.max() + 1024 <= nbytes
+            pd = torch.from_numpy(pages).cuda()
+            out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+            for mode, mname in ((0, "global_load_lds"), (1, "register"), (2, "register+ds_write")):
+                for inflight in (4, 8, 12):
+                    lds = (96 if wgs == 1 else 80) * 1024
+                    call = lambda: lib.aqp_probe_stage(buf.data_ptr(), pd.data_ptr(), pages.size, mode, inflight, blocks,
+                                                       lds, out.data_ptr(), st)
+                    assert call() == 0
+                    torch.cuda.synchronize()
+                    ms = timed_flushed(torch, call, 10)[0] if label == "2GiB" else _timed_plain(torch, call, 20)
+                    print(json.dumps({"stage": mname, "source": label, "wgs_per_cu": wgs, "pages_in_flight_per_wave": inflight,
+                                      "bytes": int(pages.size) * 1024, "ms": round(ms, 4),
+                                      "GBps": round(pages.size * 1024 / ms / 1e6, 1)}), flush=True)
+        del buf
+
+
+def _timed_plain(torch, fn, reps):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _clock_and_time(torch, launch, reps, out):
+    """Mean milliseconds per launch over reps launches, and the median shader clock (MHz) the waves
+    of the last launch ran at (s_memtime cycles over s_memrealtime's 100 MHz ticks)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        assert launch() == 0
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        launch()
+    e1.record()
+    torch.cuda.synchronize()
+    o = out.view(-1, 5).cpu().numpy().astype(np.int64)
+    clk = float(np.median((o[:, 2] - o[:, 1]) / np.maximum(o[:, 4] - o[:, 3], 1) * 100.0))
+    cyc = o[:, 2] - o[:, 1]
+    return e0.elapsed_time(e1) / reps, clk, cyc
+
+
+def lds_probe(torch):
+    """The result layout of v_mfma_f32_32x32x16_bf16 (checked against a host product), then the LDS
+    read rate in bytes per clock per CU for 16-byte reads and 8-bit transposed reads, at one and
+    two waves per SIMD."""
+    lib = probe_lib()
+    st = torch.cuda.current_stream().cuda_stream
+    rng = np.random.default_rng(7)
+    A = rng.integers(-4, 5, size=(32, 16)).astype(np.float32)
+    B = rng.integers(-4, 5, size=(16, 32)).astype(np.float32)
+    av = np.zeros((64, 8), np.float32)
+    bv = np.zeros((64, 8), np.float32)
+    for l in range(64):
+        for j in range(8):
+            av[l, j] = A[l % 32, 8 * (l // 32) + j]
+            bv[l, j] = B[8 * (l // 32) + j, l % 32]
+    C = A @ B
+    want = np.zeros((64, 16), np.float32)
+    for l in range(64):
+        for i in range(16):
+            want[l, i] = C[8 * (i // 4) + 4 * (l // 32) + (i % 4), l % 32]
+    a_d, b_d = torch.from_numpy(av).cuda(), torch.from_numpy(bv).cuda()
+    o_d = torch.zeros(64 * 16, dtype=torch.float32, device="cuda")
+    assert lib.aqp_probe_mfma32_layout(a_d.data_ptr(), b_d.data_ptr(), o_d.data_ptr(), st) == 0
+    got = o_d.view(64, 16).cpu().numpy()
+    print(json.dumps({"mfma32x32x16_layout": "A: lane l row l%32, k 8(l/32)..+7; B: lane l col l%32, same k; "
+                                             "C reg i of lane l: row 8(i/4) + 4(l/32) + i%4, col l%32",
+                      "matches": bool(np.array_equal(got, want))}), flush=True)
+    cus = lib.aqp_probe_cu_count()
+    for kind, name, bytes_per_read in ((0, "ds_read_b128", 1024), (1, "ds_read_b64_tr_b8", 512)):
+        for wpc in (4, 8):
+            blocks = wpc // 4 * cus
+            iters = 20000
+            out = torch.zeros(blocks * 4 * 5, dtype=torch.int64, device="cuda")
+            ms, clk, cyc = _clock_and_time(torch, lambda: lib.aqp_probe_lds_read(kind, blocks, iters, out.data_ptr(), st),
+                                           3, out)
+            # bytes per CU per clock over the waves' own loop cycles (median wave)
+            per_cu = wpc * iters * 8 * bytes_per_read / float(np.median(cyc))
+            print(json.dumps({"lds_read": name, "waves_per_cu": wpc, "bytes_per_clk_per_cu": round(per_cu, 1),
+                              "shader_clock_mhz": round(clk, 1), "ms": round(ms, 4)}), flush=True)
 
 
 def mfma_probe(torch):
@@ -444,6 +609,18 @@ def mfma_probe(torch):
     lib = probe_lib()
     cus = lib.aqp_probe_cu_count()
     st = torch.cuda.current_stream().cuda_stream
+    for nacc in (1, 2):
+        for wpc in (4, 8):
+            blocks = wpc // 4 * cus
+            iters = 2000
+            out = torch.zeros(blocks * 4 * 5, dtype=torch.int64, device="cuda")
+            ms, clk, cyc = _clock_and_time(torch, lambda: lib.aqp_probe_mfma_chain(nacc, blocks, iters, out.data_ptr(), st),
+                                           3, out)
+            n_mfma = iters * 8 * nacc
+            print(json.dumps({"mfma_chain": f"v_mfma_f32_32x32x16_bf16, {nacc} dependent chain(s) per wave, "
+                                            f"{wpc} waves per CU", "shader_clock_mhz": round(clk, 1),
+                              "simd_cycles_per_mfma": round(float(np.median(cyc)) / (wpc // 4) / n_mfma, 2),
+                              "ms": round(ms, 4)}), flush=True)
     for shape, nacc, flops_per in ((16, 8, 16384), (16, 16, 16384), (32, 4, 32768), (32, 8, 32768)):
         for wpc in (4, 8, 16):  # waves per CU: 1, 2 and 4 per SIMD
             iters = 40000 // nacc * (16 if shape == 16 else 8)
@@ -530,11 +707,19 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
+    if args.stage_probe:
+        stage_probe(torch)
+        xcc_probe(torch)
+        mfma_valu_probe(torch)
+        return
     if args.copy_probe:
         copy_probe(torch)
         return
     if args.mfma_probe:
         mfma_probe(torch)
+        return
+    if args.lds_probe:
+        lds_probe(torch)
         return
     import attention_quantized_paged_amd as aqp
     import workloads as W

@@ -131,30 +131,36 @@ def _steps(it, window):
 
 
 @pytest.mark.parametrize("split", [0, 1, 3])
+@pytest.mark.parametrize("dtype", ["fp8_e4m3", "int8_per_group"])
 @pytest.mark.parametrize("rows", [0, 64, 128])
 @pytest.mark.parametrize("seqs,hq,hkv,d,bs,window,par", CASES)
-def test_prefill_coverage_and_order(seqs, hq, hkv, d, bs, window, par, rows, split):
+def test_prefill_coverage_and_order(seqs, hq, hkv, d, bs, window, par, rows, split, dtype):
     """Every (query token, q head) of every prefill sequence is in exactly one item; a split item's
     runs tile its key range in whole 32-key steps, own consecutive blocks of partial-result slots
     and have one merge item per query token; items run heaviest first."""
-    _check_prefill(seqs, hq, hkv, d, bs, window, par, rows, split)
+    _check_prefill(seqs, hq, hkv, d, bs, window, par, rows, split, dtype=dtype)
 
 
-def _check_prefill(seqs, hq, hkv, d, bs, window, par, rows, split):
+def _check_prefill(seqs, hq, hkv, d, bs, window, par, rows, split, dtype="fp8_e4m3"):
+    # (64-row items at head_dim 256 are not built: that head size runs the 16x16 prefill, whose
+    # 8 waves of 16 rows make 128-row items)
     if rows == 64 and d > 128:
         with pytest.raises(aqp.AqpError) as e:
-            _sched(seqs, hq, hkv, d, bs, window=window, par=par, rows=rows, split=split)
+            _sched(seqs, hq, hkv, d, bs, dtype=dtype, window=window, par=par, rows=rows, split=split)
         assert e.value.status == aqp.ERR_UNSUPPORTED
         return
-    s, sl, qsl, params, desc = _sched(seqs, hq, hkv, d, bs, window=window, par=par, rows=rows, split=split)
+    s, sl, qsl, params, desc = _sched(seqs, hq, hkv, d, bs, dtype=dtype, window=window, par=par, rows=rows, split=split)
     h = s.header
     if rows:
         assert h_rows(s) == rows
     _, _, comb, pf = _arrays(s)
     G = hq // hkv
     gh = min(G, 16 if d <= 128 else 8)
+    _check_launch_order(pf, window)
     families = {}
     for it in pf:
+        if it["q_hi"] == it["q_lo"]:
+            continue  # launch-order padding
         assert 0 <= it["q_lo"] < it["q_hi"] <= it["ql"]
         assert 0 <= it["head0"] < it["head0"] + it["nheads"] <= G
         assert (it["q_hi"] - it["q_lo"]) * it["nheads"] <= h_rows(s)
@@ -198,8 +204,55 @@ def _check_prefill(seqs, hq, hkv, d, bs, window, par, rows, split):
     expect = {(b, k, t, hh) for b, (ql, L) in enumerate(seqs) if ql > 1 for k in range(hkv) for t in range(ql)
               for hh in range(G)}
     assert set(seen) == expect
-    work = [_steps(it, window) for it in pf]
-    assert work == sorted(work, reverse=True)
+
+
+XCDS = 8
+
+
+def _check_launch_order(pf, window):
+    """Work-group i runs on L2 domain (XCD) i % 8: with 8 or more items, each domain's items run
+    longest first, padding (empty items: no rows, no keys, no slot) only after a domain's real
+    items, and the domains' work within one item of an equal share; fewer items run longest
+    first."""
+    real = lambda it: it["q_hi"] > it["q_lo"]
+    for it in pf:
+        if not real(it):
+            assert it["slot"] == -1 and it["k_hi_max"] == 0 and it["split_hi"] == 0
+    if len(pf) < XCDS:
+        work = [_steps(it, window) for it in pf]
+        assert work == sorted(work, reverse=True)
+        return
+    assert len(pf) % XCDS == 0
+    loads = []
+    for b in range(XCDS):
+        dom = [pf[i] for i in range(b, len(pf), XCDS)]
+        flags = [real(it) for it in dom]
+        assert flags == sorted(flags, reverse=True), "padding before a real item"
+        work = [max(1, _steps(it, window)) for it in dom if real(it)]
+        assert work == sorted(work, reverse=True)
+        loads.append(sum(work))
+    biggest = max(max(1, _steps(it, window)) for it in pf if real(it))
+    assert max(loads) <= -(-sum(loads) // XCDS) + biggest
+
+
+def test_launch_order_keeps_groups_on_few_l2_domains():
+    """The large prefill (4 sequences x 2 KV heads, 64 items each of equal total work): each L2
+    domain (XCD) gets the items of exactly one (sequence, KV head), so it reads one group's K and V;
+    the mixed batch's prefill (2 sequences x 8 KV heads) puts at most 3 groups on a domain."""
+    w2 = workloads.CFG2
+    s, *_ = _sched(w2.seqs, 16, 2, 256, 2176)
+    _, _, _, pf = _arrays(s)
+    assert len(pf) == 512
+    for b in range(XCDS):
+        groups = {(int(it["seq"]), int(it["kvh"])) for it in pf[b::XCDS] if it["q_hi"] > it["q_lo"]}
+        assert len(groups) == 1
+    w4 = workloads.CFG4
+    seqs = [x for x in w4.seqs if x[0] > 1]
+    s, *_ = _sched(seqs, 32, 8, 128, 16)
+    _, _, _, pf = _arrays(s)
+    for b in range(XCDS):
+        groups = {(int(it["seq"]), int(it["kvh"])) for it in pf[b::XCDS] if it["q_hi"] > it["q_lo"]}
+        assert 1 <= len(groups) <= 3
 
 
 def test_prefill_split_policy():
@@ -219,6 +272,7 @@ def test_prefill_split_policy():
     assert _sched(many, 32, 8, 128, 16)[0].header["num_pf_split"] == 0
     s, *_ = _sched(((100, 300),), 8, 2, 128, 16, split=4)
     _, _, _, pf = _arrays(s)
+    pf = [it for it in pf if it["q_hi"] > it["q_lo"]]  # (without the launch-order padding)
     assert 1 < len(pf) and all(it["slot"] >= 0 for it in pf)
     assert max(sum(1 for x in pf if (x["kvh"], x["q_lo"]) == (it["kvh"], it["q_lo"])) for it in pf) <= 4
 
@@ -294,10 +348,20 @@ def test_large_block_size_geometry_is_consistent():
     s, *_ = _sched(((1024, 1024),) * 4, 16, 2, 256, 2176)
     h = s.header
     assert h["pf_kv_tile"] == 32 and h["staged_elem_bytes"] == 1
-    # prefill: 4 ring stages of codes and scales, two K and two V bf16 images, two scale copies
+    # prefill (the 16x16 kernel at head_dim 256): 4 ring stages of codes and scales, two K and two V
+    # bf16 images, two scale copies
     assert h["pf_lds_bytes"] == 4 * (2 * 32 * 256 * 1 + 2 * 32 * 4) + 4 * 32 * 256 * 2 + 2 * 2 * 32 * 4
     # decode: per wave 2 ring slots of 16 keys of K and V, one Q slot of 8 heads; merge area of 4 waves
     assert h["dec_lds_bytes"] == 4 * (2 * (2 * 16 * 256) + 8 * 256 * 2) + 4 * 8 * (256 + 4) * 4
+
+
+def test_prefill32_geometry():
+    """Head_dim 128, one-byte codes per token-head (the 32x32 prefill): 4 ring stages of the K and
+    V codes of 32 keys and their scales, two bf16 V images of a step, and the block-table entries of
+    two batches of 64 tiles for up to 4 waves."""
+    s, *_ = _sched(((512, 2560),) * 2, 32, 8, 128, 16, dtype="int8_per_token_head")
+    h = s.header
+    assert h["pf_lds_bytes"] == 4 * (2 * 32 * 128 * 1 + 2 * 32 * 4) + 2 * 32 * 128 * 2 + 2 * 4 * 64 * 4
 
 
 def test_per_sequence_causal_flags_and_seq_lens_are_recorded():
@@ -396,7 +460,7 @@ def _batches(draw):
         seqs.append((ql, L))
     window = draw(st.sampled_from([0, 0, 1, 17, 300]))
     par = draw(st.sampled_from([0, 1, 7, 100]))
-    rows = draw(st.sampled_from([0, 128] if d > 128 else [0, 64, 128]))
+    rows = draw(st.sampled_from([0, 64, 128]))
     split = draw(st.sampled_from([0, 1, 2, 5]))
     return tuple(seqs), g * hkv, hkv, d, bs, window, par, rows, split
 
