@@ -58,9 +58,12 @@ def _load() -> ctypes.CDLL:
                                      ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.aqp_paged_attention.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(CacheDesc), P, P, P, P, P, f32,
                                         f32, P, sz, P, P]
+    lib.aqp_paged_attention_noalloc.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(CacheDesc), P, P, P, P,
+                                                P, f32, f32, P, P]
     lib.aqp_last_error.argtypes = []
     lib.aqp_last_error.restype = ctypes.c_char_p
-    for fn in ("aqp_parse_kv_dtype", "aqp_cache_bytes", "aqp_cache_write", "aqp_get_schedule", "aqp_paged_attention"):
+    for fn in ("aqp_parse_kv_dtype", "aqp_cache_bytes", "aqp_cache_write", "aqp_get_schedule", "aqp_paged_attention",
+               "aqp_paged_attention_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -279,6 +282,29 @@ def paged_attention(params: AttnParams, desc: CacheDesc, cache, q, block_tables,
     _check(_lib.aqp_paged_attention(ctypes.byref(params), ctypes.byref(desc), _ptr(cache), _ptr(q),
                                     _ptr(block_tables), _ptr(meta_host), _ptr(meta_dev), float(k_scale),
                                     float(v_scale), _ptr(scratch), int(scratch_bytes), _ptr(out), _stream(stream)))
+
+
+# scratch bytes of the library's own buffer behind paged_attention_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def paged_attention_noalloc(params: AttnParams, desc: CacheDesc, cache, q, block_tables, meta_host, meta_dev,
+                            k_scale: float, v_scale: float, out, stream=None) -> None:
+    """paged_attention with the library's fixed scratch buffer (for callers that cannot allocate)."""
+    for t, nm in ((cache, "cache"), (q, "q"), (block_tables, "block_tables"), (meta_dev, "meta_dev"), (out, "out")):
+        _dev_ok(t, nm)
+    if isinstance(meta_host, np.ndarray) and meta_host.nbytes >= 256:
+        h = parse_header(meta_host)
+        if h["magic"] == 0x53505141:
+            rowb = 2 * h["num_q_heads"] * h["head_dim"]
+            _need(q, h["total_q_tokens"] * rowb, "q")
+            _need(out, h["total_q_tokens"] * rowb, "out")
+            _need(block_tables, 4 * h["num_seqs"] * h["max_blocks_per_seq"], "block_tables")
+            _need(meta_dev, h["meta_bytes"], "meta_dev")
+            _need(cache, cache_bytes(desc)[2], "cache")
+    _check(_lib.aqp_paged_attention_noalloc(ctypes.byref(params), ctypes.byref(desc), _ptr(cache), _ptr(q),
+                                            _ptr(block_tables), _ptr(meta_host), _ptr(meta_dev), float(k_scale),
+                                            float(v_scale), _ptr(out), _stream(stream)))
 
 
 def last_error() -> str:

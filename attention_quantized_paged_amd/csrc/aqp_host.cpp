@@ -626,10 +626,14 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
     if (cond) return fail(AQP_ERR_SCHEDULE_MISMATCH, "aqp_paged_attention: schedule was built for a different %s", what); \
   } while (0)
 
-extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cache_desc* desc, const void* cache,
-                                   const void* q, const int32_t* block_tables, const void* meta_host,
-                                   const void* meta_dev, float k_scale, float v_scale, void* scratch,
-                                   size_t scratch_bytes, void* out, void* stream) {
+namespace aqp {
+
+// The attention call on a given work buffer (`work`, `work_bytes` bytes). side: a mixed batch may
+// run its decode on the device's second stream (created on first use); without it the decode and
+// the prefill run one after the other on `stream`.
+static int attention(const aqp_attn_params* params, const aqp_cache_desc* desc, const void* cache, const void* q,
+                     const int32_t* block_tables, const void* meta_host, const void* meta_dev, float k_scale,
+                     float v_scale, void* work, size_t work_bytes, void* out, void* stream, bool side) {
   if (!params || !desc || !meta_host) return fail(AQP_ERR_INVALID, "aqp_paged_attention: null argument");
   Geometry g;
   const char* why = "";
@@ -654,9 +658,9 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
               h.pf_kv_tile != kPfKvTile || h.heads_per_unit != heads_per_unit(desc->head_dim) ||
               h.dec_lds_bytes != dec_lds_bytes(desc->head_dim, desc->mode, std::min<int32_t>(params->num_q_heads / params->num_kv_heads, heads_per_unit(desc->head_dim)), g.kv_elem_bytes) ||
               h.pf_lds_bytes != g.pf_lds_bytes, "tile geometry");
-  if ((int64_t)scratch_bytes < h.scratch_bytes)
-    return fail(AQP_ERR_SCRATCH_TOO_SMALL, "aqp_paged_attention: scratch of %zu bytes, schedule needs %lld", scratch_bytes, (long long)h.scratch_bytes);
-  if (h.scratch_bytes > 0 && !scratch) return fail(AQP_ERR_INVALID, "aqp_paged_attention: null scratch");
+  if ((int64_t)work_bytes < h.scratch_bytes)
+    return fail(AQP_ERR_SCRATCH_TOO_SMALL, "aqp_paged_attention: scratch of %zu bytes, schedule needs %lld", work_bytes, (long long)h.scratch_bytes);
+  if (h.scratch_bytes > 0 && !work) return fail(AQP_ERR_INVALID, "aqp_paged_attention: null scratch");
   if (h.total_q_tokens == 0) return AQP_OK;
   if (!cache || !q || !block_tables || !meta_dev || !out) return fail(AQP_ERR_INVALID, "aqp_paged_attention: null pointer");
   if (desc->mode == AQP_SCALE_PER_TENSOR && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
@@ -666,7 +670,7 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
   a.q = (const uint16_t*)q;
   a.block_tables = block_tables;
   a.meta_dev = (const uint8_t*)meta_dev;
-  a.scratch = (float*)scratch;
+  a.scratch = (float*)work;
   a.out = (uint16_t*)out;
   a.page_bytes = g.page_bytes;
   a.block_bytes = g.block_bytes;
@@ -698,7 +702,7 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
     if (r == AQP_OK && n_pf_comb > 0) r = launch_combine(a, n_dec_comb, n_pf_comb, st);
     return r;
   };
-  if (h.num_pf_items > 0 && h.num_dec_segs > 0) {
+  if (side && h.num_pf_items > 0 && h.num_dec_segs > 0) {
     // A mixed batch: the decode (HBM-bound) runs beside the prefill (matrix-bound) on a second
     // stream of this device, forked from and joined back into the caller's stream, so the two
     // kernels share the CUs instead of running one after the other.
@@ -726,4 +730,65 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
     if (rc) return rc;
   }
   return AQP_OK;
+}
+
+// Scratch of the allocation-free call: a file-scope device array, one per GPU the library runs on,
+// kept until the process ends. Host code never uses its name as an address (on the host the name is
+// a stand-in, not device memory): the device address is taken once per device with
+// hipGetSymbolAddress and used from then on.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// Device address of this device's copy of `scratch` (taken on the first call on the device, with
+// the device current), or null with the error set.
+static void* noalloc_scratch() {
+  static std::mutex mu;
+  static void* per_dev[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    set_error("aqp_paged_attention_noalloc: no current HIP device");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_dev[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      set_error("aqp_paged_attention_noalloc: hipGetSymbolAddress of the scratch array failed: %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    per_dev[dev] = p;
+  }
+  return per_dev[dev];
+}
+
+}  // namespace aqp
+
+extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cache_desc* desc, const void* cache,
+                                   const void* q, const int32_t* block_tables, const void* meta_host,
+                                   const void* meta_dev, float k_scale, float v_scale, void* scratch_buf,
+                                   size_t scratch_bytes, void* out, void* stream) {
+  return attention(params, desc, cache, q, block_tables, meta_host, meta_dev, k_scale, v_scale, scratch_buf,
+                   scratch_bytes, out, stream, true);
+}
+
+extern "C" int aqp_paged_attention_noalloc(const aqp_attn_params* params, const aqp_cache_desc* desc,
+                                           const void* cache, const void* q, const int32_t* block_tables,
+                                           const void* meta_host, const void* meta_dev, float k_scale,
+                                           float v_scale, void* out, void* stream) {
+  if (!meta_host) return fail(AQP_ERR_INVALID, "aqp_paged_attention_noalloc: null argument");
+  SchedHeader h;
+  std::memcpy(&h, meta_host, sizeof h);
+  // refused before any device call: a schedule whose partial results exceed the fixed buffer
+  if (h.magic == kMagic && h.version == kVersion && h.scratch_bytes > (int64_t)kNoAllocScratchBytes)
+    return fail(AQP_ERR_SCRATCH_TOO_SMALL,
+                "aqp_paged_attention_noalloc: the schedule needs %lld bytes of scratch, the allocation-free call "
+                "has a fixed %zu (use aqp_paged_attention with a caller buffer)",
+                (long long)h.scratch_bytes, kNoAllocScratchBytes);
+  void* work = h.scratch_bytes > 0 ? noalloc_scratch() : nullptr;
+  if (h.scratch_bytes > 0 && !work) return AQP_ERR_HIP;
+  return attention(params, desc, cache, q, block_tables, meta_host, meta_dev, k_scale, v_scale, work,
+                   kNoAllocScratchBytes, out, stream, false);
 }

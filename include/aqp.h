@@ -234,6 +234,21 @@ int aqp_paged_attention(const aqp_attn_params* params, const aqp_cache_desc* des
                         const void* q, const int32_t* block_tables, const void* meta_host, const void* meta_dev,
                         float k_scale, float v_scale, void* scratch, size_t scratch_bytes, void* out, void* stream);
 
+/* aqp_paged_attention without a scratch argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * partial results of split ranges go to a fixed 64 MiB device array of the library (one per GPU
+ * it runs on, held until the process ends; its address is looked up once per device on the
+ * first call there). The call itself allocates nothing and creates nothing: a mixed batch runs
+ * its decode and its prefill one after the other on `stream` instead of on a second stream.
+ * Arguments, layouts and results are those of aqp_paged_attention. No part of the array has to
+ * start at zero (every partial result is written before it is merged). Every call on one GPU
+ * shares its array: calls that overlap on a GPU (other streams, other threads) race; serialise
+ * them. Errors: those of aqp_paged_attention; SCRATCH_TOO_SMALL, before any device call, when
+ * the schedule's scratch_bytes exceeds 64 MiB; HIP when the array's address cannot be read. */
+int aqp_paged_attention_noalloc(const aqp_attn_params* params, const aqp_cache_desc* desc, const void* cache,
+                                const void* q, const int32_t* block_tables, const void* meta_host,
+                                const void* meta_dev, float k_scale, float v_scale, void* out, void* stream);
+
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* aqp_last_error(void);
 

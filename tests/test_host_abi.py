@@ -172,3 +172,19 @@ def test_binding_refuses_mis_sized_buffers():
                                  (k, k, slots[:4], cache, "slot_mapping"), (k, k, slots, cache[:10], "cache")):
         with pytest.raises(ValueError, match=what):
             aqp.cache_write(desc, cc, kk, vv, ss, 1.0, 1.0, stream=0)
+
+
+def test_noalloc_refuses_schedules_beyond_its_buffer():
+    """The allocation-free call holds a fixed 64 MiB scratch: a schedule needing more (here 4 prefill
+    sequences of 1024 tokens split into 8 key runs: 520 MiB of partial results) is refused with
+    SCRATCH_TOO_SMALL before any device call (so also on a host without a GPU), nothing launched."""
+    sl = np.array([4096] * 4, np.int32)
+    qsl = np.array([0, 1024, 2048, 3072, 4096], np.int32)
+    desc = aqp.cache_desc(4 * 256, 16, 8, 128, "int8_per_token_head")
+    params = aqp.attn_params(32, 8, 128, 256, prefill_kv_split=8)
+    s = aqp.get_schedule(params, desc, sl, qsl)
+    assert s.scratch_bytes > aqp.NOALLOC_SCRATCH_BYTES
+    rc = aqp._lib.aqp_paged_attention_noalloc(ctypes.byref(params), ctypes.byref(desc), 16, 16, 16,
+                                              s.meta.ctypes.data, 16, 1.0, 1.0, 16, None)
+    assert rc == aqp.ERR_SCRATCH_TOO_SMALL
+    assert "64" in aqp.last_error() or str(64 << 20) in aqp.last_error()
