@@ -80,32 +80,6 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
   return AQP_OK;
 }
 
-// Second stream of the current device for mixed batches (created on first use, default
-// priority, kept until the process ends), with the events that fork it from and join it back
-// into a caller's stream. The mutex serialises the fork / launch / join of concurrent callers.
-SideStream* side_stream() {
-  static std::mutex mu;
-  static SideStream* per_dev[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-    set_error("aqp_paged_attention: no current HIP device");
-    return nullptr;
-  }
-  std::lock_guard<std::mutex> lock(mu);
-  if (!per_dev[dev]) {
-    SideStream* ss = new SideStream();
-    if (hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss->join, hipEventDisableTiming) != hipSuccess) {
-      set_error("aqp_paged_attention: could not create the side stream");
-      delete ss;
-      return nullptr;
-    }
-    per_dev[dev] = ss;
-  }
-  return per_dev[dev];
-}
-
 int device_cu_count() {
   static int cached = 0;
   if (cached == 0) {
@@ -628,12 +602,10 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
 
 namespace aqp {
 
-// The attention call on a given work buffer (`work`, `work_bytes` bytes). side: a mixed batch may
-// run its decode on the device's second stream (created on first use); without it the decode and
-// the prefill run one after the other on `stream`.
+// The attention call on a given work buffer (`work`, `work_bytes` bytes).
 static int attention(const aqp_attn_params* params, const aqp_cache_desc* desc, const void* cache, const void* q,
                      const int32_t* block_tables, const void* meta_host, const void* meta_dev, float k_scale,
-                     float v_scale, void* work, size_t work_bytes, void* out, void* stream, bool side) {
+                     float v_scale, void* work, size_t work_bytes, void* out, void* stream) {
   if (!params || !desc || !meta_host) return fail(AQP_ERR_INVALID, "aqp_paged_attention: null argument");
   Geometry g;
   const char* why = "";
@@ -702,31 +674,15 @@ static int attention(const aqp_attn_params* params, const aqp_cache_desc* desc, 
     if (r == AQP_OK && n_pf_comb > 0) r = launch_combine(a, n_dec_comb, n_pf_comb, st);
     return r;
   };
-  if (side && h.num_pf_items > 0 && h.num_dec_segs > 0) {
-    // A mixed batch: the decode (HBM-bound) runs beside the prefill (matrix-bound) on a second
-    // stream of this device, forked from and joined back into the caller's stream, so the two
-    // kernels share the CUs instead of running one after the other.
-    SideStream* ss = side_stream();
-    if (!ss) return AQP_ERR_HIP;
-    std::lock_guard<std::mutex> lock(ss->mu);
-    hipStream_t st = (hipStream_t)stream;
-    if (hipEventRecord(ss->fork, st) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
-      return fail(AQP_ERR_HIP, "aqp_paged_attention: fork to the side stream failed");
-    rc = run_decode(ss->s);
-    if (rc == AQP_OK) rc = run_prefill(stream);
-    // joined whatever happened after the fork: work already enqueued on the side stream may still
-    // be writing `out` and `scratch`, and the caller's stream must not run ahead of it
-    const bool joined = hipEventRecord(ss->join, ss->s) == hipSuccess && hipStreamWaitEvent(st, ss->join, 0) == hipSuccess;
+  // A mixed batch runs its decode and then its prefill on `stream`: the two kernels each fill the
+  // device, and measured one after the other they finish sooner than side by side on two streams
+  // (each takes the other's CUs and LDS).
+  if (h.num_dec_segs > 0) {
+    rc = run_decode(stream);
     if (rc) return rc;
-    if (!joined) return fail(AQP_ERR_HIP, "aqp_paged_attention: join of the side stream failed");
-    return AQP_OK;
   }
   if (h.num_pf_items > 0) {
     rc = run_prefill(stream);
-    if (rc) return rc;
-  }
-  if (h.num_dec_segs > 0) {
-    rc = run_decode(stream);
     if (rc) return rc;
   }
   return AQP_OK;
@@ -771,7 +727,7 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
                                    const void* meta_dev, float k_scale, float v_scale, void* scratch_buf,
                                    size_t scratch_bytes, void* out, void* stream) {
   return attention(params, desc, cache, q, block_tables, meta_host, meta_dev, k_scale, v_scale, scratch_buf,
-                   scratch_bytes, out, stream, true);
+                   scratch_bytes, out, stream);
 }
 
 extern "C" int aqp_paged_attention_noalloc(const aqp_attn_params* params, const aqp_cache_desc* desc,
@@ -790,5 +746,5 @@ extern "C" int aqp_paged_attention_noalloc(const aqp_attn_params* params, const 
   void* work = h.scratch_bytes > 0 ? noalloc_scratch() : nullptr;
   if (h.scratch_bytes > 0 && !work) return AQP_ERR_HIP;
   return attention(params, desc, cache, q, block_tables, meta_host, meta_dev, k_scale, v_scale, work,
-                   kNoAllocScratchBytes, out, stream, false);
+                   kNoAllocScratchBytes, out, stream);
 }

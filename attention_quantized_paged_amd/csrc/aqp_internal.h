@@ -134,12 +134,6 @@ inline void invariant_divisor(uint32_t d, uint32_t* m, int32_t* shift) {
 
 // Compute units of the current device (256 on MI355X; 256 when no device is visible).
 int device_cu_count();
-struct SideStream {
-  hipStream_t s;
-  hipEvent_t fork, join;
-  std::mutex mu;
-};
-SideStream* side_stream();
 
 // Geometry derived from the cache descriptor. One function computes it for
 // both the scheduler and the launcher.

@@ -3,10 +3,11 @@
  *
  * C ABI of the library (libaqp.so). Plain pointers and sizes only; every
  * device buffer is allocated and owned by the caller; the library allocates no
- * device memory. State it keeps: a per-thread last-error message, and per device
- * one second stream with two events (hipStreamNonBlocking, default priority),
- * created by the first mixed decode + prefill batch on that device and kept
- * until the process ends (see aqp_paged_attention).
+ * device memory at run time. State it keeps: a per-thread last-error message,
+ * the compute-unit count of the first device it queried, and the device
+ * address of its one static device array (the scratch of
+ * aqp_paged_attention_noalloc: 64 MiB per GPU the library is loaded on, held
+ * until the process ends).
  *
  * The operations follow three pages summarising vLLM pull requests:
  *  [P39445] "CPU backend adds FP8 KV-cache quantisation" (PR 39445)
@@ -224,10 +225,9 @@ int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_desc* desc, 
  * Per query row: z_j = sm_scale * q . k_j (k_j dequantised), soft-capped if
  * set, masked by causality and window; softmax over the visible keys; output
  * = sum_j p_j v_j rounded to bf16.
- * A batch with both decode and prefill sequences runs its decode kernel on the
- * device's second stream (see the top of this file), forked from `stream` by an
- * event and joined back into it before the call returns, also when a launch
- * fails; the work is complete when `stream`'s work up to this call is.
+ * A batch with both decode and prefill sequences runs its decode kernels and
+ * then its prefill kernels on `stream`; the work is complete when `stream`'s
+ * work up to this call is.
  * Errors: INVALID, SCHEDULE_MISMATCH (schedule built for another cache
  * descriptor, dtype, element size or parameter set), SCRATCH_TOO_SMALL, HIP. */
 int aqp_paged_attention(const aqp_attn_params* params, const aqp_cache_desc* desc, const void* cache,
@@ -238,9 +238,8 @@ int aqp_paged_attention(const aqp_attn_params* params, const aqp_cache_desc* des
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * partial results of split ranges go to a fixed 64 MiB device array of the library (one per GPU
  * it runs on, held until the process ends; its address is looked up once per device on the
- * first call there). The call itself allocates nothing and creates nothing: a mixed batch runs
- * its decode and its prefill one after the other on `stream` instead of on a second stream.
- * Arguments, layouts and results are those of aqp_paged_attention. No part of the array has to
+ * first call there). The call itself allocates nothing and creates nothing. Arguments, layouts,
+ * stream use and results are those of aqp_paged_attention. No part of the array has to
  * start at zero (every partial result is written before it is merged). Every call on one GPU
  * shares its array: calls that overlap on a GPU (other streams, other threads) race; serialise
  * them. Errors: those of aqp_paged_attention; SCRATCH_TOO_SMALL, before any device call, when
