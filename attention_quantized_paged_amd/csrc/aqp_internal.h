@@ -66,7 +66,7 @@ constexpr int pf_wgs_per_cu(int head_dim, int rows, int32_t lds_bytes) {
 constexpr bool pf32_applies(int dtype, int mode, int head_dim) {
   return head_dim <= 128 && dtype != AQP_KV_AUTO && (mode == AQP_SCALE_PER_TENSOR || mode == AQP_SCALE_PER_TOKEN_HEAD);
 }
-constexpr int kPf32Stages = 4;  // LDS ring stages of the 32x32 prefill (three steps ahead)
+constexpr int kPf32Stages = 4;  // LDS ring stages of the 32x32 prefill (four steps ahead)
 // Waves per SIMD its registers are sized for: a wave holds 32 rows of Q (D/4 registers), their
 // fp32 output (D/2), the next step's K operands (D/4) and two S tiles.
 constexpr int pf32_waves_per_simd(int head_dim) { return head_dim >= 256 ? 1 : (head_dim == 128 ? 2 : 3); }
@@ -74,12 +74,12 @@ constexpr int pf32_waves_per_simd(int head_dim) { return head_dim >= 256 ? 1 : (
 constexpr int pf32_stage_bytes(int head_dim, int mode) {
   return 2 * kPfKvTile * head_dim + (mode == AQP_SCALE_PER_TOKEN_HEAD ? 2 * kPfKvTile * 4 : 0);
 }
-// LDS of one 32x32 prefill work-group: the ring, then two slots each holding a step's V image
-// (bf16, kPfKvTile x head_dim).
-// Then the block-table entries of two batches of 64 tiles for each of up to 4 waves (4 bytes each).
+// LDS of one 32x32 prefill work-group: two slots each holding a step's V image and two holding a
+// step's K image (bf16, kPfKvTile x head_dim each), the ring, then the block-table entries of two
+// batches of 64 tiles for each of up to 4 waves (4 bytes each).
 constexpr int kPf32TableBytes = 2 * 4 * 64 * 4;
 constexpr int32_t pf32_lds_bytes(int head_dim, int mode) {
-  return kPf32Stages * pf32_stage_bytes(head_dim, mode) + 2 * kPfKvTile * head_dim * 2 + kPf32TableBytes;
+  return kPf32Stages * pf32_stage_bytes(head_dim, mode) + 4 * kPfKvTile * head_dim * 2 + kPf32TableBytes;
 }
 constexpr int pf32_wgs_per_cu(int head_dim, int rows, int32_t lds_bytes) {
   return 4 * pf32_waves_per_simd(head_dim) / (rows / 32) < kLdsPerCu / lds_bytes

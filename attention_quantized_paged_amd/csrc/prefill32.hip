@@ -133,11 +133,15 @@ void prefill32_kernel(Pf32Args a) {
   constexpr int VBLK = 2 * NDT;                    // V image blocks: [dim tile][16-key chunk]
   constexpr int VB_PW = VBLK / WAVES;              // V blocks each wave widens per step
   static_assert(VB_PW >= 1 && VBLK % WAVES == 0, "V blocks must split evenly over the waves");
-  constexpr int VIMG = VBLK * 1024;                // one step's V image
-  constexpr int RB = 2 * VIMG;                     // the ring follows the two V images
+  constexpr int VIMG = VBLK * 1024;                // one step's V image (and one step's K image)
+  static_assert(QC * 1024 == VIMG, "K and V images are the same size");
+  constexpr int KIM = 2 * VIMG;                    // the two K images follow the two V images
+  constexpr int RB = 4 * VIMG;                     // then the ring
   constexpr int TBL = RB + NS * STAGE;             // then the tile tables: [batch parity][wave][64]
   static_assert(WAVES <= 4 && TBL + kPf32TableBytes == pf32_lds_bytes(D, MODE), "LDS layout");
-  static_assert((NS - 1) * STAGE + 1024 < 65536 && 2 * VIMG <= 65536, "constant LDS offsets fit the 16-bit offset field");
+  static_assert((NS - 1) * STAGE + 1024 < 65536 && 4 * VIMG <= 65536, "constant LDS offsets fit the 16-bit offset field");
+  constexpr int KU = 4 * D / (64 * WAVES);         // 8-code units of a step's K image each lane widens
+  static_assert(KU >= 1 && KU <= 8 && (KU == 1 || KU % 2 == 0) && QC % KU == 0, "K image units per lane");
   constexpr int NSL = QC;                          // slices of a step: one S chunk and one PV block each
   static_assert(QC == 2 * NDT, "as many S chunks as PV blocks");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -319,7 +323,13 @@ void prefill32_kernel(Pf32Args a) {
 #pragma unroll
     for (int j = 0; j < IPW; ++j) *(uint4*)(smem + st_off + (RB + U * STAGE + 1024 * j)) = r.c[j];
     if constexpr (PTH) {
-      if (wave == WAVES - 1 && lane < 16) *(uint4*)(smem + RB + U * STAGE + 2 * KT * ROWB + 16 * lane) = r.sc;
+      if (wave == WAVES - 1 && lane < 16) {
+        // the K scales (lanes 0 .. 7) are staged times the logit scale, one multiply per key here
+        // instead of one per logit in every wave
+        float4 sc = __builtin_bit_cast(float4, r.sc);
+        if (lane < 8) { sc.x *= xscale; sc.y *= xscale; sc.z *= xscale; sc.w *= xscale; }
+        *(float4*)(smem + RB + U * STAGE + 2 * KT * ROWB + 16 * lane) = sc;
+      }
     }
   };
 
@@ -349,7 +359,22 @@ void prefill32_kernel(Pf32Args a) {
       tr_off[j] = (uint32_t)(RB + KT * ROWB + key * ROWB + ((lc ^ pf32_swz<D>(key)) << 4) + 8 * (lane & 1));
     }
   }
-  const uint32_t l16 = (uint32_t)(lane * 16);                                   // V image reads
+  // K image of one step: block i (i = 0 .. QC - 1) holds, for consumer lane l, the codes of key l % 32
+  // at depth (l / 32) D/2 + 8 i .. + 7 widened to bf16 (the S^T operand of chunk i, read as 64 lanes x
+  // 16 bytes). Each lane widens KU consecutive units of one key row: group g = 2 wave + lane / 32
+  // takes units g KU .. of the row's 2 QC (lane half kh = g KU / QC, first chunk ki = g KU % QC).
+  uint32_t kr_off[(KU + 1) / 2];  // its ring reads: 16-byte chunks (one 8-byte half when KU == 1)
+  uint32_t kw_off;                 // its image writes (block ki, then 1024 bytes per further unit)
+  {
+    const int u0 = (2 * wave + hh) * KU;
+    const int kh = u0 / QC, ki = u0 % QC;
+    const int dep = kh * (D / 2) + 8 * ki;  // the first code of the lane's units in the key row
+#pragma unroll
+    for (int c = 0; c < (KU + 1) / 2; ++c)
+      kr_off[c] = (uint32_t)(RB + r32 * ROWB + ((((dep >> 4) + c) ^ pf32_swz<D>(r32)) << 4) + (dep & 15));
+    kw_off = (uint32_t)(KIM + (r32 + 32 * kh) * 16 + 1024 * ki);
+  }
+  const uint32_t l16 = (uint32_t)(lane * 16);                                   // V and K image reads
   const uint32_t vw_off = (uint32_t)(wave * VB_PW * 1024 + lane * 16);          // V image writes
   const uint32_t scl_off = (uint32_t)(RB + 2 * KT * ROWB + 16 * hh);            // scales: 4 hh floats in
   auto lds = [&](uint32_t off) { return smem + off; };
@@ -384,8 +409,33 @@ void prefill32_kernel(Pf32Args a) {
     }
   };
 
-  // ---- prologue helpers: S of one step as one dependent chain, the V image of step 0 and its
-  // (masked) softmax
+  // The K image of the step in ring stage `kc` into image slot `kw`: codes read, then widened
+  // and written (no masking: the logits of masked keys are replaced)
+  auto k_codes = [&](auto kc, uint32_t (&kb)[2 * KU]) {
+    constexpr int KBS = decltype(kc)::value * STAGE;
+    if constexpr (KU == 1) {
+      const uint2 v = *(const uint2*)lds(kr_off[0] + KBS);
+      kb[0] = v.x;
+      kb[1] = v.y;
+    } else {
+#pragma unroll
+      for (int c = 0; c < KU / 2; ++c) {
+        const uint4 v = *(const uint4*)lds(kr_off[c] + KBS);
+        kb[4 * c] = v.x;
+        kb[4 * c + 1] = v.y;
+        kb[4 * c + 2] = v.z;
+        kb[4 * c + 3] = v.w;
+      }
+    }
+  };
+  auto k_image = [&](auto kw, const uint32_t (&kb)[2 * KU]) {
+    constexpr int KIW = decltype(kw)::value;
+#pragma unroll
+    for (int j = 0; j < KU; ++j) *(bf16x8*)lds(kw_off + KIW + 1024 * j) = widen8<DT>(kb[2 * j], kb[2 * j + 1]);
+  };
+
+  // ---- prologue helpers: S of one step as one dependent chain (from the ring's codes), the V
+  // image of step 0 and its (masked) softmax
   auto qk = [&](auto uc) {
     constexpr int KST = decltype(uc)::value * STAGE;
     f32x16 sv = {};
@@ -412,7 +462,7 @@ void prefill32_kernel(Pf32Args a) {
     float x[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      x[e] = sv[e] * xscale * (PTH ? scl[8 * (e >> 2) + (e & 3)] : 1.0f);
+      x[e] = PTH ? sv[e] * scl[8 * (e >> 2) + (e & 3)] : sv[e] * xscale;  // (staged K scales carry xscale)
       if constexpr (CAP) x[e] = a.softcap * kLog2e * tanh_via_exp2(x[e] * a.inv_softcap);
       if constexpr (ALIBI) x[e] += slope2 * (float)(kb + 8 * (e >> 2) + 4 * hh + (e & 3) - pos);
       if (!((uint32_t)(base + 8 * (e >> 2) + (e & 3)) < width)) x[e] = -INFINITY;
@@ -448,16 +498,18 @@ void prefill32_kernel(Pf32Args a) {
   };
 
   // ---- one step of the pipeline at ring phase U (= step % NS), in NSL slices kept in order: each
-  // slice issues one MFMA of S of step + 2 (its K codes widened on the way) and one of the PV product
-  // of step (operands read two slices ahead), and a share of the vector work: the softmax of
-  // step + 1 (whose S is `s_in`) into the probabilities `pb_out`, and the V image of step + 1.
+  // slice issues one MFMA of S of step + 2 (K operand from its image) and one of the PV product of
+  // step (operands read two slices ahead), and a share of the vector work: the softmax of step + 1
+  // (whose S is `s_in`) into the probabilities `pb_out`, the V image of step + 1 and the K image of
+  // step + 3.
   // FULL: no key of step + 1 is masked for this wave and both its tiles are present. Returns whether
   // the reference maximum moved (then *alpha is the factor for the output, applied by the caller
   // once these PV products are done).
   auto slices = [&](auto uc, bool full, const f32x16& s_in, const bf16x8 (&pb_in)[2], f32x16& s_out,
                     bf16x8 (&pb_out)[2], int sm, float* alpha) {
     constexpr int U = decltype(uc)::value;
-    constexpr int KST = ((U + 2) % NS) * STAGE;  // ring stage of step + 2: its K codes
+    constexpr int KIR = KIM + (U & 1) * VIMG;    // K image of step + 2 (slot (step + 2) % 2)
+    constexpr int KIW = ((U + 1) & 1) * VIMG;    // slot of step + 3's K image (relative to KIM)
     constexpr int VST = ((U + 1) % NS) * STAGE;  // ring stage of step + 1: its V codes and scales
     constexpr int PVI = (U & 1) * VIMG;          // V image of step
     constexpr int VOI = ((U + 1) & 1) * VIMG;    // V image of step + 1
@@ -467,18 +519,19 @@ void prefill32_kernel(Pf32Args a) {
     const int ok = okr[(U + 1) % NS];
     const bool ok0 = ok & 1, ok1 = ok & 2;
     const int kb = k_begin + sm * KT;
-    uint4 kc[QC / 2];
-    bf16x8 vo[NSL];
+    bf16x8 ko[NSL], vo[NSL];
+    uint32_t kcode[2 * KU];  // codes of this lane's units of step + 3's K image
     i32x2 trc[VB_PW];
     float x[16], p[16];
     float4 ks4[4], vs4[4];
-    // operands are read VPF slices (V image) and KPF K reads (two slices each) ahead of their MFMA
-    // (further at one wave per SIMD, where nothing else hides the LDS latency)
-    constexpr int VPF = D >= 256 ? 4 : 2, KPF = D >= 256 ? 3 : (QC / 2 >= 2 ? 2 : 1);
+    // operands are read two slices ahead of their MFMA
+    constexpr int VPF = 2, KPF = 2;
+    static_assert(NSL >= 4, "the slices hold the prefetched operands");
 #pragma unroll
-    for (int m = 0; m < KPF; ++m) kc[m] = *(const uint4*)lds(k_off[m] + KST);
+    for (int m = 0; m < KPF; ++m) ko[m] = *(const bf16x8*)lds(l16 + KIR + 1024 * m);
 #pragma unroll
     for (int i = 0; i < VPF; ++i) vo[i] = *(const bf16x8*)lds(l16 + PVI + 1024 * i);
+    k_codes(IC<(U + 3) % NS>{}, kcode);
     if constexpr (PTH) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -493,19 +546,15 @@ void prefill32_kernel(Pf32Args a) {
     constexpr int EXP0 = NSL >= 4 ? 2 : 1, EXPN = NSL >= 4 ? NSL - 3 : 1;  // slices holding the exps
 #pragma unroll
     for (int i = 0; i < NSL; ++i) {
-      if (i % 2 == 0 && i / 2 + KPF < QC / 2) kc[i / 2 + KPF] = *(const uint4*)lds(k_off[i / 2 + KPF] + KST);
+      if (i + KPF < NSL) ko[i + KPF] = *(const bf16x8*)lds(l16 + KIR + 1024 * (i + KPF));
       if (i + VPF < NSL) vo[i + VPF] = *(const bf16x8*)lds(l16 + PVI + 1024 * (i + VPF));
-      {
-        const uint4 c = kc[i / 2];
-        const bf16x8 kop = (i % 2 == 0) ? widen8<DT>(c.x, c.y) : widen8<DT>(c.z, c.w);
-        s_out = mfma32x32x16(kop, qb[i], i == 0 ? f32x16{} : s_out);
-      }
+      s_out = mfma32x32x16(ko[i], qb[i], i == 0 ? f32x16{} : s_out);
       acc[i / 2] = mfma32x32x16(vo[i], pb_in[i % 2], acc[i / 2]);
       if (i == 0) {
         // logits (log2 domain) of keys kb + 8 (e / 4) + 4 hh + e % 4; a plain per-tensor step keeps
         // S as it is and folds the scale into the exponent's multiply-add below
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = PLAIN ? s_in[e] : s_in[e] * xscale * (PTH ? ks4[e >> 2][e & 3] : 1.0f);
+        for (int e = 0; e < 16; ++e) x[e] = PLAIN ? s_in[e] : (PTH ? s_in[e] * ks4[e >> 2][e & 3] : s_in[e] * xscale);
         if constexpr (CAP) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) x[e] = a.softcap * kLog2e * tanh_via_exp2(x[e] * a.inv_softcap);
@@ -558,21 +607,30 @@ void prefill32_kernel(Pf32Args a) {
         if (full) v_image(IC<VOI>{}, IC<0>{}, trc, sm);
         else v_image(IC<VOI>{}, IC<1>{}, trc, sm);
       }
+      if (i == NSL / 2 - 1) k_image(IC<KIW>{}, kcode);
       if (i == NSL - 1) {
         float psum;
         if constexpr (PTH) {
           psum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])) +
                  ((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15]));
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            // a masked key may have an unwritten scale slot: select, do not multiply, its zero
-            p[e] = x[e] == -INFINITY ? 0.0f : p[e] * vs4[e >> 2][e & 3];
+          for (int e = 0; e < 16; ++e) p[e] *= vs4[e >> 2][e & 3];
+          if (!full) {
+            // a masked key may have an unwritten scale slot: its product is replaced by zero
+#pragma unroll
+            for (int e = 0; e < 16; ++e) p[e] = x[e] == -INFINITY ? 0.0f : p[e];
           }
         }
+        // (pairs: one v_cvt_pk_bf16_f32 each)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) pb_out[kk][j] = (__bf16)p[8 * kk + j];
+          for (int j = 0; j < 4; ++j) {
+            const f32x2 pr = {p[8 * kk + 2 * j], p[8 * kk + 2 * j + 1]};
+            const bf16x2 b = __builtin_convertvector(pr, bf16x2);
+            pb_out[kk][2 * j] = b[0];
+            pb_out[kk][2 * j + 1] = b[1];
+          }
         if constexpr (!PTH) {
           // the row sum of the probabilities as they enter the PV product (bf16), two at a time
           psum = 0.0f;
@@ -592,17 +650,18 @@ void prefill32_kernel(Pf32Args a) {
     return grow;
   };
 
-  // ---- software pipeline. Prologue: steps 0 .. 2 into their stages, S of steps 0 and 1, the
-  // softmax of step 0 and its V image. Iteration t (0 <= t < n - 1), after one barrier: the loads of
-  // step t + 3 start; the slices run S of step t + 2 (beyond the last step: unused), the PV product
-  // of step t, the softmax and the V image of step t + 1 (whose S came from iteration t - 1); then
-  // step t + 3 goes into the stage that step t - 1 left. The PV product of the last step follows
-  // the loop. The V image is written one iteration before it is read, each ring stage is read while
-  // later ones fill, so one barrier per step orders every writer and reader. The loop is unrolled over the four ring stages, so every LDS offset is a constant
-  // and S, the probabilities and the V image alternate between two buffers without copies. A move of
-  // the reference maximum (rare) stops the loop after the iteration whose PV product still used the
-  // old one; the output is rescaled outside the loop, so inside it only matrix instructions touch the
-  // output and it stays in the matrix accumulation registers.
+  // ---- software pipeline. Prologue: steps 0 .. 3 into their stages, S of steps 0 and 1, the
+  // softmax of step 0, its V image and the K image of step 2. Iteration t (0 <= t < n - 1), after
+  // one barrier: the loads of step t + 4 start; the slices run S of step t + 2 (beyond the last
+  // step: unused), the PV product of step t, the softmax and the V image of step t + 1 (whose S came
+  // from iteration t - 1) and the K image of step t + 3; then step t + 4 goes into the stage step t
+  // left. The PV product of the last step follows the loop. Each image is written one iteration
+  // before it is read and each ring stage is read while later ones fill, so one barrier per step
+  // orders every writer and reader. The loop is unrolled over the four ring stages, so every LDS
+  // offset is a constant and S, the probabilities and the images alternate between two buffers
+  // without copies. A move of the reference maximum (rare) stops the loop after the iteration whose
+  // PV product still used the old one; the output is rescaled outside the loop, so inside it only
+  // matrix instructions touch the output and it stays in the matrix accumulation registers.
   if (n_steps > 0) {
     // the first batch's entries (waited for here, before any KV copy), then the second's gather
     gather(0);
@@ -611,20 +670,22 @@ void prefill32_kernel(Pf32Args a) {
     if (n_steps > 32) gather(1);
   }
   {
-    Staged t0, t1, t2;
+    Staged t0, t1, t2, t3;
     if (n_steps > 0) t0 = load_step(IC<0>{}, 0);
     if (n_steps > 1) t1 = load_step(IC<1>{}, 1);
     if (n_steps > 2) t2 = load_step(IC<2>{}, 2);
+    if (n_steps > 3) t3 = load_step(IC<3>{}, 3);
     if (n_steps > 0) store_step(IC<0>{}, t0);
     if (n_steps > 1) store_step(IC<1>{}, t1);
     if (n_steps > 2) store_step(IC<2>{}, t2);
+    if (n_steps > 3) store_step(IC<3>{}, t3);
   }
   f32x16 sA, sB;     // S of the even and of the odd steps
   bf16x8 pA[2], pB[2];  // probabilities of the even and of the odd steps
   if (n_steps > 0) {
-    __syncthreads();  // stages 0 .. 2 written by every wave
-    // S of steps 0 and 1, the V image and the softmax of step 0 (the output is still zero: a move of
-    // the reference maximum needs no rescale)
+    __syncthreads();  // stages 0 .. 3 written by every wave
+    // S of steps 0 and 1 (from the codes), the V image of step 0, the K image of step 2 and the
+    // softmax of step 0 (the output is still zero: a move of the reference maximum needs no rescale)
     const f32x16 s0 = qk(IC<0>{});
     if (n_steps > 1) sB = qk(IC<1>{});
     {
@@ -632,6 +693,9 @@ void prefill32_kernel(Pf32Args a) {
 #pragma unroll
       for (int j = 0; j < VB_PW; ++j) trc[j] = lds_read_tr8(lds(tr_off[j]));
       v_image(IC<0>{}, IC<1>{}, trc, 0);
+      uint32_t kb[2 * KU];
+      k_codes(IC<2>{}, kb);
+      k_image(IC<0>{}, kb);
     }
     float alpha0;
     softmax0(s0, pA, &alpha0);
@@ -644,9 +708,9 @@ void prefill32_kernel(Pf32Args a) {
   auto iter = [&](auto uc) {
     constexpr int U = decltype(uc)::value;
     if (step + 1 >= n_steps) return true;
-    __syncthreads();  // stage step + 2 and the V image of step written by every wave
+    __syncthreads();  // stage step + 3, the V image of step and the K image of step + 2 written by every wave
     Staged st;
-    if (step + 3 < n_steps) st = load_step(IC<(U + 3) % NS>{}, step + 3);
+    if (step + 4 < n_steps) st = load_step(IC<U>{}, step + 4);
     const int s1 = step + 1;
     const bool full = s1 >= f_lo && s1 <= f_hi && okr[(U + 1) % NS] == 3;
     f32x16& s_in = pick<(U + 1) & 1>(sA, sB);
@@ -654,8 +718,9 @@ void prefill32_kernel(Pf32Args a) {
     bf16x8(&pb_in)[2] = pick<U & 1>(pA, pB);
     bf16x8(&pb_out)[2] = pick<(U + 1) & 1>(pA, pB);
     rescale = slices(uc, full, s_in, pb_in, s_out, pb_out, s1, &alpha);
-    // step + 3 into its stage (read from the next iteration on: its barrier orders the writes)
-    if (step + 3 < n_steps) store_step(IC<(U + 3) % NS>{}, st);
+    // step + 4 into the stage step left (read from the next iteration on: its barrier orders the
+    // writes)
+    if (step + 4 < n_steps) store_step(IC<U>{}, st);
     step = s1;
     return rescale;
   };

@@ -357,11 +357,11 @@ def test_large_block_size_geometry_is_consistent():
 
 def test_prefill32_geometry():
     """Head_dim 128, one-byte codes per token-head (the 32x32 prefill): 4 ring stages of the K and
-    V codes of 32 keys and their scales, two bf16 V images of a step, and the block-table entries of
-    two batches of 64 tiles for up to 4 waves."""
+    V codes of 32 keys and their scales, two bf16 V images and two bf16 K images of a step, and the
+    block-table entries of two batches of 64 tiles for up to 4 waves."""
     s, *_ = _sched(((512, 2560),) * 2, 32, 8, 128, 16, dtype="int8_per_token_head")
     h = s.header
-    assert h["pf_lds_bytes"] == 4 * (2 * 32 * 128 * 1 + 2 * 32 * 4) + 2 * 32 * 128 * 2 + 2 * 4 * 64 * 4
+    assert h["pf_lds_bytes"] == 4 * (2 * 32 * 128 * 1 + 2 * 32 * 4) + 4 * 32 * 128 * 2 + 2 * 4 * 64 * 4
 
 
 def test_per_sequence_causal_flags_and_seq_lens_are_recorded():
