@@ -11,12 +11,13 @@
 // row r is token r / nheads, q head r % nheads, so all rows share the K/V tiles); each wave owns 32
 // rows, the 32 columns of its MFMA tiles. Per step of 32 keys:
 //   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, one dependent chain over the head dimension: A = 32
-//                   keys x 16 depth, widened from the codes to bf16 in registers right before each
-//                   MFMA (each wave reads the codes straight from the LDS ring); B = Q^T, in registers
-//                   for the whole item. Lane l holds row l % 32 and keys 8 (i / 4) + 4 (l / 32) + i % 4
-//                   of its 16 accumulators i.
+//                   keys x 16 depth from a bf16 image of the step's keys (widened once per
+//                   work-group, a quarter per wave, one step ahead; 1 KB operand blocks read as 64
+//                   lanes x 16 bytes); B = Q^T, in registers for the whole item. Lane l holds row
+//                   l % 32 and keys 8 (i / 4) + 4 (l / 32) + i % 4 of its 16 accumulators i.
 //   softmax         per row over the lane's 16 keys and its partner lane l ^ 32 (one lane swap);
-//                   exp2 domain, lazy rescaling; per-token-head scales read from the ring stage.
+//                   exp2 domain, lazy rescaling; per-token-head scales read from the ring stage
+//                   (the K scales staged times the logit scale).
 //   O^T += V^T P^T  A = V^T from a bf16 image of the step's values (widened once per work-group,
 //                   64 lanes x 16 bytes per 1 KB operand block, in exactly the key order the
 //                   probabilities sit in: lane half h of 16-key chunk c holds keys
@@ -25,10 +26,12 @@
 // The codes of 32 keys of K and V (and their per-token-head scales) go from HBM through registers
 // (16-byte loads, one iteration ahead of their LDS write) into a 4-stage LDS ring (16-byte chunks,
 // XOR-swizzled so that both the 16-row K reads and the 8-row transposed V reads hit distinct
-// banks); one barrier per step orders the ring and the V image. The direct global -> LDS copy
-// (global_load_lds) was measured at about half the rate of plain loads on this chip, with no gain
-// from more copies in flight, so it is not used. The block-table entries of the item's tiles are
-// gathered 64 tiles at a time into a small LDS table and held one per lane.
+// banks); one barrier per step orders the ring and the images. Register staging rather than the
+// direct global -> LDS copy: the compiler counts these loads and waits for exactly the ones a store
+// needs, while hand-issued copies are invisible to its counting, so any load it issues itself
+// (spill reloads, table reads) gets a vmcnt(0) wait that drains every copy in flight. The
+// block-table entries of the item's tiles are gathered 64 tiles at a time into a small LDS table
+// and held one per lane.
 #include <type_traits>
 
 #include "device_common.h"

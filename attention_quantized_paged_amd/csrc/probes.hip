@@ -137,10 +137,15 @@ extern "C" int aqp_probe_gather(const void* base, const int64_t* pages, int64_t 
 }
 
 // Staging: every wave copies its run of 1 KB pages (byte offsets into one buffer) into LDS, with
-// `inflight` pages in flight, three ways: MODE 0 the direct global -> LDS copy
+// `inflight` pages in flight, four ways: MODE 0 the direct global -> LDS copy
 // (global_load_lds_dwordx4; the wave waits until at most inflight - 1 copies are outstanding before
 // the next), MODE 1 plain 16-byte loads into registers (inflight pages loaded before the first is
-// used), MODE 2 the same loads each followed, once it lands, by a 16-byte LDS write. The launch's
+// used), MODE 2 the same loads each followed, once it lands, by a 16-byte LDS write, MODE 3 the
+// direct copy in the batches of MODE 1 (inflight copies issued, then one wait for all of them).
+// MODES 4 and 5 read each wave's run as consecutive pages (addresses computed, no offset loads) with
+// a rolling window of inflight direct copies (wait until inflight - 1 are outstanding, then copy the
+// next); MODE 4 also reads one LDS word of the oldest landed page per copy and waits for that read
+// (s_waitcnt lgkmcnt(0)), which shows whether the copies in flight hold that counter up. The launch's
 // LDS size sets how many work-groups of 4 waves a CU holds, as in the prefill kernel.
 template <int MODE, int INFL>
 __global__ __launch_bounds__(256) void stage_kernel(const uint8_t* base, const int64_t* pages, int64_t npages,
@@ -163,6 +168,37 @@ __global__ __launch_bounds__(256) void stage_kernel(const uint8_t* base, const i
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     acc = *(const uint32_t*)slot0;
+  } else if constexpr (MODE == 4 || MODE == 5) {
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(sm + wave * INFL * 1024);
+    const uint8_t* src = base + p0 * 1024 + 16 * lane;
+    for (int64_t p = p0; p < p1; ++p) {
+      const uint32_t dst = lds0 + (uint32_t)((p - p0) % INFL) * 1024u;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory");
+      src += 1024;
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(INFL - 1) : "memory");
+      if constexpr (MODE == 4) {
+        // the oldest copy in the window has landed; read a word of it
+        uint32_t v;
+        const uint32_t rd = lds0 + (uint32_t)((p - p0 + 1) % INFL) * 1024u + 16u * (uint32_t)lane;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(rd) : "memory");
+        acc ^= v;
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    acc ^= *(const uint32_t*)slot0;
+  } else if constexpr (MODE == 3) {
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(sm + wave * INFL * 1024);
+    for (int64_t p = p0; p < p1; p += INFL) {
+      int64_t off[INFL];
+#pragma unroll
+      for (int i = 0; i < INFL; ++i) off[i] = pages[p + i < p1 ? p + i : p1 - 1];
+#pragma unroll
+      for (int i = 0; i < INFL; ++i)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds0 + 1024u * i),
+                     "v"(base + off[i] + 16 * lane) : "memory");
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    acc = *(const uint32_t*)slot0;
   } else {
     for (int64_t p = p0; p < p1; p += INFL) {
       uint4 v[INFL];
@@ -182,7 +218,8 @@ __global__ __launch_bounds__(256) void stage_kernel(const uint8_t* base, const i
   out[w * 64 + lane] = acc;
 }
 
-// pages: device int64 [npages] byte offsets into base (each 1 KB page in bounds); mode 0, 1 or 2;
+// pages: device int64 [npages] byte offsets into base (each 1 KB page in bounds); mode 0 .. 5 (4, 5:
+// npages * 1 KB <= the buffer, pages unused);
 // inflight 4, 8 or 12; waves = blocks * 4; lds_bytes >= 4 * inflight * 1024 (at most 160 KB);
 // out: device uint32 [blocks * 256]. Returns 0 or -1.
 extern "C" int aqp_probe_stage(const void* base, const int64_t* pages, int64_t npages, int32_t mode, int32_t inflight,
@@ -204,6 +241,9 @@ extern "C" int aqp_probe_stage(const void* base, const int64_t* pages, int64_t n
   AQP_STAGE(0, 4) AQP_STAGE(0, 8) AQP_STAGE(0, 12)
   AQP_STAGE(1, 4) AQP_STAGE(1, 8) AQP_STAGE(1, 12)
   AQP_STAGE(2, 4) AQP_STAGE(2, 8) AQP_STAGE(2, 12)
+  AQP_STAGE(3, 4) AQP_STAGE(3, 8) AQP_STAGE(3, 12)
+  AQP_STAGE(4, 4) AQP_STAGE(4, 8) AQP_STAGE(4, 12)
+  AQP_STAGE(5, 4) AQP_STAGE(5, 8) AQP_STAGE(5, 12)
 #undef AQP_STAGE
   return -1;
 }

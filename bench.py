@@ -477,8 +477,8 @@ def xcc_probe(torch):
 
 
 def stage_probe(torch):
-    """Rates of the three ways of staging 1 KB pages into LDS (direct global -> LDS copies, plain
-    register loads, register loads plus LDS writes) at the prefill's occupancy (one or two
+    """Rates of the ways of staging 1 KB pages into LDS (direct global -> LDS copies one at a time
+    and in batches, plain register loads, register loads plus LDS writes) at the prefill's occupancy (one or two
     work-groups of 4 waves per CU), from an L2-sized buffer (4 MB, the prefill's shared K and V)
     and from a 2 GiB one (HBM)."""
     lib = probe_lib()
@@ -499,7 +499,11 @@ def stage_probe(torch):
             assert pages.min() >= 0 and pages.max() + 1024 <= nbytes
             pd = torch.from_numpy(pages).cuda()
             out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
-            for mode, mname in ((0, "global_load_lds"), (1, "register"), (2, "register+ds_write")):
+            for mode, mname in ((0, "global_load_lds"), (1, "register"), (2, "register+ds_write"),
+                                (3, "global_load_lds_batched"), (4, "global_load_lds_window+lds_read"),
+                                (5, "global_load_lds_window")):
+                if mode >= 4 and pages.size * 1024 > nbytes:
+                    continue  # (these modes read the wave's pages consecutively from the buffer's start)
                 for inflight in (4, 8, 12):
                     lds = (96 if wgs == 1 else 80) * 1024
                     call = lambda: lib.aqp_probe_stage(buf.data_ptr(), pd.data_ptr(), pages.size, mode, inflight, blocks,
