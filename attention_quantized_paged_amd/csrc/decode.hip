@@ -26,7 +26,8 @@
 //    into the final normalisation; per token-head, each key's scale multiplies
 //    its logit and each value's scale its probability;
 //  * softmax: running max / sum in the exp2 domain, reduced across the four lanes that
-//    share a head with lane permutes; lazy rescaling;
+//    share a head with lane permutes; lazy rescaling; two of the wave's tiles per loop
+//    iteration share one reduction and one rescale check (their S products are independent);
 //  * V: ds_read_b64_tr_b8 hands each lane 4 keys of one head-dim column for two column
 //    tiles at once: the key-contiguous operand that O^T = V^T * P^T on
 //    v_mfma_f32_16x16x16_bf16 needs, so the probabilities stay in the registers the
@@ -338,8 +339,9 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
       qpos = as_const(a.seq_lens)[sg.seq] - 1;
       slope2 = head_ok ? a.alibi[sg.kvh * a.group + sg.head0 + r16] * kLog2e : 0.0f;
     }
-    Pos pc;
-    const int n_my = first_pos(sg, pc);
+    Pos pc0;
+    const int n_my = first_pos(sg, pc0);
+    int ck0 = pc0.k0;  // first key of the wave's next tile
 
     float m = -INFINITY;  // reference max (log2 domain) of this lane's head
     float l = 0.0f;       // sum of this lane's probabilities relative to m
@@ -347,28 +349,18 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int k = 0; k < n_my; ++k) {
-      // this tile's copies are done once only the later tiles' copies are outstanding (the Q
-      // copies and merge stores are not counted, which only makes the wait longer)
-      wait_tiles_ahead<IPT, NS>(n_issued - n_done - 1);
-      if (k == 0) {
-        // Q^T operand: lane (column head r16, group kg) holds q[head][kg*D/4 + 8*st + 0..7]
-        // (per group: q[head][32*st + 8*kg + 0..7], so that MFMA step st covers scale group st)
-        const uint8_t* qp = qslots + (q_read % NQ) * QB + r16 * (D * 2) + (PG ? kg * 16 : kg * (D / 2));
-#pragma unroll
-        for (int st = 0; st < QS; ++st) {
-          uint4 u = *(const uint4*)(qp + st * (PG ? 64 : 16));
-          if (!head_ok) u = make_uint4(0, 0, 0, 0);
-          qb[st] = __builtin_bit_cast(bf16x8, u);
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        ++q_read;
-        issue_next(n_done, q_read);  // a copy held back for want of a Q slot
-      }
-      const uint8_t* kl = ring + c_slot;
+    // One tile's scores (keys k0 + 4 kg + r of head r16, log2 domain, masked) and its V operands,
+    // read from the ring slot at `kl`.
+    struct TileS {
+      float x[4];
+      i32x2 vw[EB == 1 ? NT / 2 : 1];
+      uint32_t vb[EB == 2 ? NT : 1][2];
+      float4 vs;
+      uint32_t vmask;
+      bool full;
+    };
+    auto score = [&](const uint8_t* kl, int k0, bool ok, TileS& t) {
       const uint8_t* vl = kl + TB;
-      const bool ok = (ok_bits >> (n_done & 63)) & 1;
-
       // ---- S^T = K * Q^T: lane holds keys k0 + 4kg + r of head r16
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
       if constexpr (PG) {
@@ -396,77 +388,66 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
           s = mfma16x16x32(*(const bf16x8*)(kl + r16 * ROWB + (((kg * QS + st) ^ k_swz) << 4)), qb[st], s);
       }
       // V^T operands: transposed reads issued now, used after the softmax
-      i32x2 vw[EB == 1 ? NT / 2 : 1];
-      uint32_t vb[EB == 2 ? NT : 1][2];
       if constexpr (EB == 1) {
 #pragma unroll
-        for (int t2 = 0; t2 < NT / 2; ++t2) vw[t2] = lds_read_tr8(vl + tr_base + (((2 * t2 + tr_hi) ^ tr_swz) << 4));
+        for (int t2 = 0; t2 < NT / 2; ++t2) t.vw[t2] = lds_read_tr8(vl + tr_base + (((2 * t2 + tr_hi) ^ tr_swz) << 4));
       } else {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
+        for (int tt = 0; tt < NT; ++tt) {
           uint32_t e[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            e[r] = *(const uint16_t*)(vl + v16_row[r] + (((2 * t + (r16 >> 3)) ^ v16_swz[r]) << 4));
-          vb[t][0] = e[0] | (e[1] << 16);
-          vb[t][1] = e[2] | (e[3] << 16);
+            e[r] = *(const uint16_t*)(vl + v16_row[r] + (((2 * tt + (r16 >> 3)) ^ v16_swz[r]) << 4));
+          t.vb[tt][0] = e[0] | (e[1] << 16);
+          t.vb[tt][1] = e[2] | (e[3] << 16);
         }
       }
-      float4 ks, vs;
+      float4 ks;
       if constexpr (PTH) {
         ks = *(const float4*)(kl + 2 * TB + 16 * kg);
-        vs = *(const float4*)(kl + 2 * TB + 64 + 16 * kg);
+        t.vs = *(const float4*)(kl + 2 * TB + 64 + 16 * kg);
       }
-      float x[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = s[r] * xscale;
+      for (int r = 0; r < 4; ++r) t.x[r] = s[r] * xscale;
       if constexpr (PTH) {
-        x[0] *= ks.x; x[1] *= ks.y; x[2] *= ks.z; x[3] *= ks.w;
+        t.x[0] *= ks.x; t.x[1] *= ks.y; t.x[2] *= ks.z; t.x[3] *= ks.w;
       }
       if constexpr (CAP) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = a.softcap * kLog2e * tanh_via_exp2(x[r] * a.inv_softcap);
+        for (int r = 0; r < 4; ++r) t.x[r] = a.softcap * kLog2e * tanh_via_exp2(t.x[r] * a.inv_softcap);
       }
       if (a.alibi) {
         // + slope * (key - position), after the soft-cap
-        const int base = pc.k0 + 4 * kg - qpos;
+        const int base = k0 + 4 * kg - qpos;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] += slope2 * (float)(base + r);
+        for (int r = 0; r < 4; ++r) t.x[r] += slope2 * (float)(base + r);
       }
       // masking is needed only on the segment's edge tiles (and tiles of an invalid block); rows
       // outside the range may hold unwritten bytes: their logits are replaced, their V codes
       // masked to zero and (per token-head) their scales replaced, so no NaN reaches the sums
-      const bool full = ok && pc.k0 >= sg.k_lo && pc.k0 + kTileKeys <= sg.k_hi;
-      uint32_t vmask = 0xFFFFFFFFu;
-      if (!full) {
-        vmask = 0;
+      t.full = ok && k0 >= sg.k_lo && k0 + kTileKeys <= sg.k_hi;
+      t.vmask = 0xFFFFFFFFu;
+      if (!t.full) {
+        t.vmask = 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = pc.k0 + 4 * kg + r;
+          const int key = k0 + 4 * kg + r;
           const bool kok = ok && key >= sg.k_lo && key < sg.k_hi;
-          x[r] = kok ? x[r] : -INFINITY;
-          if (kok) vmask |= 0xFFu << (8 * r);
+          t.x[r] = kok ? t.x[r] : -INFINITY;
+          if (kok) t.vmask |= 0xFFu << (8 * r);
         }
       }
-      const float mx = max_over_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-      // lazy rescaling: the reference max moves (and O, l are rescaled) only when some head's
-      // max exceeds it by more than 2^8, so probabilities stay <= 256 and the common case
-      // leaves the accumulators alone
-      if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f) != 0) {
-        const float m_new = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.0f : m_new));
-        l *= alpha;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] *= alpha;
-        m = m_new;
-      }
-      const float m_use = m == -INFINITY ? 0.0f : m;
+    };
+    // the probabilities of one tile (relative to m_use) into l and its PV product into acc
+    auto accumulate = [&](const uint8_t* kl, TileS& t, float m_use) {
       float p4[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p4[r] = fast_exp2(x[r] - m_use);
+      for (int r = 0; r < 4; ++r) p4[r] = fast_exp2(t.x[r] - m_use);
       l += (p4[0] + p4[1]) + (p4[2] + p4[3]);
+      const uint32_t vmask = t.vmask;
       if constexpr (PTH) {
-        if (!full) {
+        float4 vs = t.vs;
+        if (!t.full) {
           vs.x = (vmask & 0xFFu) ? vs.x : 0.0f;
           vs.y = (vmask & 0xFF00u) ? vs.y : 0.0f;
           vs.z = (vmask & 0xFF0000u) ? vs.z : 0.0f;
@@ -490,30 +471,92 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
             const bool kok = (vmask >> (8 * r)) & 1;
             pg[r] = (__bf16)(kok ? p4[r] * vsg[r * NG + t2] : 0.0f);
           }
-          acc[2 * t2] = mfma16x16x16(widen4v<DT>((uint32_t)vw[t2].x & vmask), pg, acc[2 * t2]);
-          acc[2 * t2 + 1] = mfma16x16x16(widen4v<DT>((uint32_t)vw[t2].y & vmask), pg, acc[2 * t2 + 1]);
+          acc[2 * t2] = mfma16x16x16(widen4v<DT>((uint32_t)t.vw[t2].x & vmask), pg, acc[2 * t2]);
+          acc[2 * t2 + 1] = mfma16x16x16(widen4v<DT>((uint32_t)t.vw[t2].y & vmask), pg, acc[2 * t2 + 1]);
         }
       } else if constexpr (EB == 1) {
 #pragma unroll
         for (int t2 = 0; t2 < NT / 2; ++t2) {
-          acc[2 * t2] = mfma16x16x16(widen4v<DT>((uint32_t)vw[t2].x & vmask), pb, acc[2 * t2]);
-          acc[2 * t2 + 1] = mfma16x16x16(widen4v<DT>((uint32_t)vw[t2].y & vmask), pb, acc[2 * t2 + 1]);
+          acc[2 * t2] = mfma16x16x16(widen4v<DT>((uint32_t)t.vw[t2].x & vmask), pb, acc[2 * t2]);
+          acc[2 * t2 + 1] = mfma16x16x16(widen4v<DT>((uint32_t)t.vw[t2].y & vmask), pb, acc[2 * t2 + 1]);
         }
       } else {
         // masked keys: their (possibly unwritten) bf16 values are zeroed like the codes above
         const uint32_t m01 = ((vmask & 0xFFu) ? 0xFFFFu : 0u) | ((vmask & 0xFF00u) ? 0xFFFF0000u : 0u);
         const uint32_t m23 = ((vmask & 0xFF0000u) ? 0xFFFFu : 0u) | ((vmask & 0xFF000000u) ? 0xFFFF0000u : 0u);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const uint2 u = make_uint2(vb[t][0] & m01, vb[t][1] & m23);
-          acc[t] = mfma16x16x16(__builtin_bit_cast(bf16x4, u), pb, acc[t]);
+        for (int tt = 0; tt < NT; ++tt) {
+          const uint2 u = make_uint2(t.vb[tt][0] & m01, t.vb[tt][1] & m23);
+          acc[tt] = mfma16x16x16(__builtin_bit_cast(bf16x4, u), pb, acc[tt]);
         }
       }
-      ++n_done;
-      c_slot = c_slot + SLOT == NS * SLOT ? 0u : c_slot + SLOT;
-      pc = advance(pc);
+    };
+    // lazy rescaling: the reference max moves (and O, l are rescaled) only when some head's max
+    // exceeds it by more than 2^8, so probabilities stay <= 256 and the common case leaves the
+    // accumulators alone; returns the reference the probabilities are taken against
+    auto rescale_to = [&](float mx) {
+      if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f) != 0) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.0f : m_new));
+        l *= alpha;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+        m = m_new;
+      }
+      return m == -INFINITY ? 0.0f : m;
+    };
+    auto load_q = [&]() {
+      // Q^T operand: lane (column head r16, group kg) holds q[head][kg*D/4 + 8*st + 0..7]
+      // (per group: q[head][32*st + 8*kg + 0..7], so that MFMA step st covers scale group st)
+      const uint8_t* qp = qslots + (q_read % NQ) * QB + r16 * (D * 2) + (PG ? kg * 16 : kg * (D / 2));
+#pragma unroll
+      for (int st = 0; st < QS; ++st) {
+        uint4 u = *(const uint4*)(qp + st * (PG ? 64 : 16));
+        if (!head_ok) u = make_uint4(0, 0, 0, 0);
+        qb[st] = __builtin_bit_cast(bf16x8, u);
+      }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      issue_next(n_done, q_read);  // into the slot this tile used: every read of it is complete
+      ++q_read;
+      issue_next(n_done, q_read);  // a copy held back for want of a Q slot
+    };
+    auto next_slot = [&](uint32_t c) { return c + SLOT == NS * SLOT ? 0u : c + SLOT; };
+    // two of the wave's tiles per iteration (one reduction and rescale check for both), then the
+    // odd one out
+    int k = 0;
+    for (; k + 1 < n_my; k += 2) {
+      // both tiles' copies are done once only later tiles' copies are outstanding
+      wait_tiles_ahead<IPT, NS>(n_issued - n_done - 2);
+      if (k == 0) load_q();
+      const uint8_t* kl0 = ring + c_slot;
+      const uint8_t* kl1 = ring + next_slot(c_slot);
+      TileS t0, t1;
+      score(kl0, ck0, (ok_bits >> (n_done & 63)) & 1, t0);
+      score(kl1, ck0 + STEP, (ok_bits >> ((n_done + 1) & 63)) & 1, t1);
+      const float mx = max_over_rows(fmaxf(fmaxf(fmaxf(t0.x[0], t0.x[1]), fmaxf(t0.x[2], t0.x[3])),
+                                           fmaxf(fmaxf(t1.x[0], t1.x[1]), fmaxf(t1.x[2], t1.x[3]))));
+      const float m_use = rescale_to(mx);
+      accumulate(kl0, t0, m_use);
+      accumulate(kl1, t1, m_use);
+      n_done += 2;
+      c_slot = next_slot(next_slot(c_slot));
+      ck0 += 2 * STEP;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue_next(n_done, q_read);  // into the slots these tiles used: every read of them is complete
+      issue_next(n_done, q_read);
+    }
+    if (k < n_my) {
+      wait_tiles_ahead<IPT, NS>(n_issued - n_done - 1);
+      if (k == 0) load_q();
+      const uint8_t* kl0 = ring + c_slot;
+      TileS t0;
+      score(kl0, ck0, (ok_bits >> (n_done & 63)) & 1, t0);
+      const float m_use = rescale_to(max_over_rows(fmaxf(fmaxf(t0.x[0], t0.x[1]), fmaxf(t0.x[2], t0.x[3]))));
+      accumulate(kl0, t0, m_use);
+      ++n_done;
+      c_slot = next_slot(c_slot);
+      ck0 += STEP;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue_next(n_done, q_read);
     }
 
     // ---- hand (O, m, l) to the fetching wave, which merges the four waves and writes the
