@@ -26,8 +26,9 @@
 //    into the final normalisation; per token-head, each key's scale multiplies
 //    its logit and each value's scale its probability;
 //  * softmax: running max / sum in the exp2 domain, reduced across the four lanes that
-//    share a head with lane permutes; lazy rescaling; two of the wave's tiles per loop
-//    iteration share one reduction and one rescale check (their S products are independent);
+//    share a head with lane permutes; lazy rescaling; with a ring of three or more tiles, two of
+//    the wave's tiles per loop iteration share one reduction and one rescale check (their S
+//    products are independent);
 //  * V: ds_read_b64_tr_b8 hands each lane 4 keys of one head-dim column for two column
 //    tiles at once: the key-contiguous operand that O^T = V^T * P^T on
 //    v_mfma_f32_16x16x16_bf16 needs, so the probabilities stay in the registers the
@@ -520,10 +521,11 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
       issue_next(n_done, q_read);  // a copy held back for want of a Q slot
     };
     auto next_slot = [&](uint32_t c) { return c + SLOT == NS * SLOT ? 0u : c + SLOT; };
-    // two of the wave's tiles per iteration (one reduction and rescale check for both), then the
-    // odd one out
+    // two of the wave's tiles per iteration (one reduction and rescale check for both) where the
+    // ring holds at least three tiles (so one stays in flight while a pair is computed), then the
+    // rest one at a time
     int k = 0;
-    for (; k + 1 < n_my; k += 2) {
+    for (; NS >= 3 && k + 1 < n_my; k += 2) {
       // both tiles' copies are done once only later tiles' copies are outstanding
       wait_tiles_ahead<IPT, NS>(n_issued - n_done - 2);
       if (k == 0) load_q();
@@ -544,7 +546,7 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
       issue_next(n_done, q_read);  // into the slots these tiles used: every read of them is complete
       issue_next(n_done, q_read);
     }
-    if (k < n_my) {
+    for (; k < n_my; ++k) {
       wait_tiles_ahead<IPT, NS>(n_issued - n_done - 1);
       if (k == 0) load_q();
       const uint8_t* kl0 = ring + c_slot;
