@@ -546,6 +546,11 @@ void prefill32_kernel(Pf32Args a) {
     for (int j = 0; j < VB_PW; ++j) trc[j] = lds_read_tr8(lds(tr_off[j] + VST));
     float mx = 0.0f, m_use = 0.0f;
     bool grow = false;
+    // per-token-head scales without soft-cap or bias: each logit is taken relative to the current
+    // reference (one multiply-add instead of a multiply and a subtraction); only a step that moves
+    // the reference shifts them once more
+    constexpr bool REL = PTH && !CAP && !ALIBI;
+    const float m_old = m_run == -INFINITY ? 0.0f : m_run;
     constexpr int EXP0 = NSL >= 4 ? 2 : 1, EXPN = NSL >= 4 ? NSL - 3 : 1;  // slices holding the exps
 #pragma unroll
     for (int i = 0; i < NSL; ++i) {
@@ -557,7 +562,10 @@ void prefill32_kernel(Pf32Args a) {
         // logits (log2 domain) of keys kb + 8 (e / 4) + 4 hh + e % 4; a plain per-tensor step keeps
         // S as it is and folds the scale into the exponent's multiply-add below
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = PLAIN ? s_in[e] : (PTH ? s_in[e] * ks4[e >> 2][e & 3] : s_in[e] * xscale);
+        for (int e = 0; e < 16; ++e)
+          x[e] = PLAIN ? s_in[e]
+                       : (REL ? __builtin_fmaf(s_in[e], ks4[e >> 2][e & 3], -m_old)
+                              : (PTH ? s_in[e] * ks4[e >> 2][e & 3] : s_in[e] * xscale));
         if constexpr (CAP) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) x[e] = a.softcap * kLog2e * tanh_via_exp2(x[e] * a.inv_softcap);
@@ -594,17 +602,27 @@ void prefill32_kernel(Pf32Args a) {
         mx = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
         // lazy rescaling: the reference maximum moves only when some row's logits exceed it by 8
         if constexpr (PLAIN) mx *= xscale;  // the logit scale is positive: max(x * scale) = max(x) * scale
+        if constexpr (REL) mx += m_old;     // (the logits were taken relative to m_old)
         grow = __builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0;
         const float m_new = grow ? fmaxf(m_run, mx) : m_run;
         *alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.0f : m_new));
         m_run = m_new;
         m_use = m_run == -INFINITY ? 0.0f : m_run;
+        if constexpr (REL) {
+          // (the reference stays where it was unless it moved: then the logits shift once)
+          if (grow) {
+            const float d = m_use - m_old;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[e] -= d;
+          }
+        }
       }
       if (i >= EXP0 && i < EXP0 + EXPN) {
         // exps e with e * EXPN / 16 == i - EXP0: an even spread of the 16 over the slices
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (e * EXPN / 16 == i - EXP0) p[e] = fast_exp2(PLAIN ? __builtin_fmaf(x[e], xscale, -m_use) : x[e] - m_use);
+          if (e * EXPN / 16 == i - EXP0)
+            p[e] = fast_exp2(PLAIN ? __builtin_fmaf(x[e], xscale, -m_use) : (REL ? x[e] : x[e] - m_use));
       }
       if (i == NSL / 2) {
         if (full) v_image(IC<VOI>{}, IC<0>{}, trc, sm);
