@@ -179,9 +179,11 @@ void prefill32_kernel(Pf32Args a) {
   const float sink2 = a.sinks ? a.sinks[hq] * kLog2e : -INFINITY;
   const int64_t orow = ((int64_t)(it.q_start + tq) * a.num_q_heads + hq) * D;
   // Q^T operands: chunk c of lane half h is depth h * D/2 + 8 c .. + 7 (the K operands below read
-  // the same depths), so each lane holds one contiguous half of its row
+  // the same depths), so each lane holds one contiguous half of its row. (Loaded in the prologue
+  // after the first steps' key/value loads: the wait for the block-table gather then does not
+  // wait for the item's Q rows too, and their transfer overlaps the key/value loads.)
   bf16x8 qb[QC];
-  {
+  auto load_q = [&]() {
     const uint16_t* qp = a.q + orow + hh * (D / 2);
 #pragma unroll
     for (int c = 0; c < QC; ++c) {
@@ -192,7 +194,7 @@ void prefill32_kernel(Pf32Args a) {
       // ordinary registers are the scarcer ones here)
       if constexpr (D >= 256) asm volatile("" : "+a"(qb[c]));
     }
-  }
+  };
   // keys visible to every row of the wave: [vis_lo, vis_hi)
   const int tw0 = min(ntok - 1, (wave * 32) / nh);
   const int tw1 = min(ntok - 1, (wave * 32 + 31) / nh);
@@ -696,6 +698,7 @@ void prefill32_kernel(Pf32Args a) {
     if (n_steps > 1) t1 = load_step(IC<1>{}, 1);
     if (n_steps > 2) t2 = load_step(IC<2>{}, 2);
     if (n_steps > 3) t3 = load_step(IC<3>{}, 3);
+    load_q();
     if (n_steps > 0) store_step(IC<0>{}, t0);
     if (n_steps > 1) store_step(IC<1>{}, t1);
     if (n_steps > 2) store_step(IC<2>{}, t2);
