@@ -590,6 +590,17 @@ __global__ __launch_bounds__(64) void combine_kernel(const CombItem* items, cons
   const int P = it.num_parts;
   const float* ml = scratch + num_slots * D;
   auto slot = [&](int s) { return (int64_t)it.first_slot + (int64_t)s * it.part_stride + h; };
+  constexpr int PER = D / 64;
+  // the rows of the first PRE parts are loaded at once with the (m, l) values: they do not depend
+  // on the weights, so their latency overlaps the max and sum reductions
+  constexpr int PRE = 8;
+  const int npre = min(P, PRE);
+  float vp[PRE][PER];
+#pragma unroll
+  for (int u = 0; u < PRE; ++u)
+    if (u < npre)
+#pragma unroll
+      for (int j = 0; j < PER; ++j) vp[u][j] = scratch[slot(u) * D + lane + 64 * j];
   // (m, l) of the parts: lane s takes parts s, s + 64, ..., so their loads are all in flight at once
   float M = -INFINITY;
   for (int s = lane; s < P; s += 64) M = fmaxf(M, ml[slot(s) * 2]);
@@ -600,7 +611,6 @@ __global__ __launch_bounds__(64) void combine_kernel(const CombItem* items, cons
   for (int s = lane; s < P; s += 64) L += fast_exp2(ml[slot(s) * 2] - M_use) * ml[slot(s) * 2 + 1];
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) L += shfl_xor_f(L, k);
-  constexpr int PER = D / 64;
   float o[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) o[j] = 0.0f;
@@ -609,6 +619,16 @@ __global__ __launch_bounds__(64) void combine_kernel(const CombItem* items, cons
     const float fl = s0 + lane < P ? fast_exp2(ml[slot(s0 + lane) * 2] - M_use) : 0.0f;
     const int n = min(64, P - s0);
     int s = 0;
+    if (s0 == 0) {
+#pragma unroll
+      for (int u = 0; u < PRE; ++u)
+        if (u < npre) {
+          const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), u));
+#pragma unroll
+          for (int j = 0; j < PER; ++j) o[j] += f * vp[u][j];
+        }
+      s = npre;
+    }
     for (; s + 4 <= n; s += 4) {
       float v[4][PER];
 #pragma unroll
