@@ -68,15 +68,17 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
   g->block_bytes = 2 * (int64_t)d.num_kv_heads * g->page_bytes;
   g->total_bytes = (int64_t)d.num_blocks * g->block_bytes;
   // Prefill work-group. The 32x32 kernel: a ring of kPf32Stages steps of codes (and scales) and
-  // two V images of a step in bf16. The 16x16 kernel (per-group scales, unquantised cache): a
-  // ring of kPfStages steps, each the K and V elements of kPfKvTile keys plus their row scales;
-  // then two K and two V operand images of a step in bf16 (widened once per work-group), each V
-  // image followed by a copy of its step's scales.
+  // two V images of a step in bf16. The 16x16 kernel (per-group scales, head_dim 256, the
+  // unquantised cache): a ring of pf_stages steps, each the K and V elements of kPfKvTile keys
+  // plus their row scales; then two K and two V operand images of a step in bf16 (widened once
+  // per work-group), each V image followed by a copy of its step's scales (none unquantised).
   if (pf32_applies(d.dtype, d.mode, d.head_dim))
     g->pf_lds_bytes = pf32_lds_bytes(d.head_dim, d.mode);
   else
-    g->pf_lds_bytes = kPfStages * (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes + pf_stage_scale_bytes(d.head_dim, d.mode)) +
-                      4 * kPfKvTile * d.head_dim * kPfOperandBytes + 2 * (2 * kPfKvTile * 4);
+    g->pf_lds_bytes = pf_stages(d.head_dim, g->staged_elem_bytes) *
+                          (2 * kPfKvTile * d.head_dim * g->staged_elem_bytes +
+                           pf_stage_scale_bytes(d.head_dim, d.mode, g->staged_elem_bytes)) +
+                      4 * kPfKvTile * d.head_dim * kPfOperandBytes + 2 * pf_vslot_scale_bytes(g->staged_elem_bytes);
   return AQP_OK;
 }
 
@@ -249,7 +251,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   wg_start.clear();
   comb.clear();
   pf.clear();
-  const int32_t max_hpu = heads_per_unit(desc->head_dim);
+  const int32_t max_hpu = heads_per_unit(desc->head_dim, g.kv_elem_bytes);
   const int32_t hpu = std::min<int32_t>(G, max_hpu);
   const int32_t dec_lds = dec_lds_bytes(desc->head_dim, desc->mode, hpu, g.kv_elem_bytes);
   if (dec_lds > kLdsPerCu) return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: decode needs %d bytes of LDS", dec_lds);
@@ -328,9 +330,6 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
     }
     while (w_cur < P) wg_start[++w_cur] = (int32_t)segs.size();
   }
-
-  if (desc->dtype == AQP_KV_AUTO && desc->head_dim > 128 && total_q > 0)
-    return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: an unquantised cache at head_dim %d is not built", desc->head_dim);
 
   // ---- prefill items: (sequence, KV head, run of query tokens, run of its q heads): all G
   // heads of the KV head when G <= rows, else one token and `rows` heads at a time;
@@ -627,8 +626,8 @@ static int attention(const aqp_attn_params* params, const aqp_cache_desc* desc, 
   MISMATCH_IF(h.sm_scale != effective_sm_scale(*params) || h.softcap != params->softcap, "logit scale / soft-cap");
   MISMATCH_IF(h.tile_keys != kTileKeys || h.dec_iter_keys != kDecIterKeys || h.dec_waves != kDecWaves || (h.pf_rows != kPfRows && h.pf_rows != kPfRowsSmall) ||
               (params->prefill_rows != 0 && h.pf_rows != params->prefill_rows) ||
-              h.pf_kv_tile != kPfKvTile || h.heads_per_unit != heads_per_unit(desc->head_dim) ||
-              h.dec_lds_bytes != dec_lds_bytes(desc->head_dim, desc->mode, std::min<int32_t>(params->num_q_heads / params->num_kv_heads, heads_per_unit(desc->head_dim)), g.kv_elem_bytes) ||
+              h.pf_kv_tile != kPfKvTile || h.heads_per_unit != heads_per_unit(desc->head_dim, g.kv_elem_bytes) ||
+              h.dec_lds_bytes != dec_lds_bytes(desc->head_dim, desc->mode, std::min<int32_t>(params->num_q_heads / params->num_kv_heads, heads_per_unit(desc->head_dim, g.kv_elem_bytes)), g.kv_elem_bytes) ||
               h.pf_lds_bytes != g.pf_lds_bytes, "tile geometry");
   if ((int64_t)work_bytes < h.scratch_bytes)
     return fail(AQP_ERR_SCRATCH_TOO_SMALL, "aqp_paged_attention: scratch of %zu bytes, schedule needs %lld", work_bytes, (long long)h.scratch_bytes);

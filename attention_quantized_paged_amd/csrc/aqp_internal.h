@@ -25,9 +25,10 @@ constexpr uint32_t kVersion = 4;
 constexpr int kTileKeys = 16;        // keys per KV tile: one 16-row MFMA operand; block_size % 16 == 0
 constexpr int kDecIterKeys = 16;     // keys per decode iteration (one tile; PV on 16x16x16 MFMA)
 constexpr int kDecWaves = 4;         // compute waves per decode work-group (they split a segment's iterations)
-// q heads per decode unit (MFMA column block): 16, or 8 at head_dim 256 so the work-group's LDS
-// (Q rows and the merge area grow with the heads) stays within one CU's
-constexpr int heads_per_unit(int head_dim) { return head_dim >= 256 ? 8 : 16; }
+// q heads per decode unit (MFMA column block): 16, or at head_dim 256 8 (one-byte codes) or 4 (the
+// unquantised cache, whose tiles take twice the ring) so the work-group's LDS (Q rows and the
+// merge area grow with the heads) stays within one CU's
+constexpr int heads_per_unit(int head_dim, int eb) { return head_dim >= 256 ? (eb == 2 ? 4 : 8) : 16; }
 constexpr int kPfRows = 128;         // prefill: query rows (token, q head) per work item
 // prefill: rows per item when 128-row items would leave CUs with fewer than two work-groups
 // (head_dim <= 128): twice the items, so a CU overlaps one work-group's waits with another's work
@@ -38,6 +39,10 @@ constexpr int kPfRowsSmall = 64;
 constexpr int pf_waves(int head_dim) { return head_dim >= 256 ? 8 : 4; }
 constexpr int kPfKvTile = 32;        // prefill: keys staged in LDS per step
 constexpr int kPfStages = 4;         // prefill: LDS ring stages of codes (two steps ahead of the widening)
+// Ring stages of the 16x16 prefill: kPfStages, or three (one step ahead of the widening) where a
+// stage holds 512-byte rows (the unquantised cache at head_dim 256), so that the ring and the
+// operand images fill one CU's LDS exactly
+constexpr int pf_stages(int head_dim, int eb) { return head_dim * eb >= 512 ? 3 : kPfStages; }
 constexpr int kPfOperandBytes = 2;   // prefill: bf16 operand images in LDS
 constexpr int kMinRunTiles = 32;     // decode: fewest 16-key tiles a work-group is given
 // prefill key splits: when a batch has fewer prefill items than the device holds work-groups at
@@ -90,10 +95,14 @@ constexpr int pf32_wgs_per_cu(int head_dim, int rows, int32_t lds_bytes) {
 constexpr int row_scales(int head_dim, int mode) {
   return mode == AQP_SCALE_PER_TOKEN_HEAD ? 1 : (mode == AQP_SCALE_PER_GROUP ? head_dim / AQP_SCALE_GROUP : 0);
 }
-// prefill: scale bytes of one ring stage (K and V of kPfKvTile keys; at least one float per key)
-constexpr int pf_stage_scale_bytes(int head_dim, int mode) {
-  return 2 * kPfKvTile * 4 * (row_scales(head_dim, mode) > 1 ? row_scales(head_dim, mode) : 1);
+// prefill: scale bytes of one ring stage (K and V of kPfKvTile keys; at least one float per key
+// for the codes, none for the unquantised cache)
+constexpr int pf_stage_scale_bytes(int head_dim, int mode, int eb) {
+  return eb == 2 ? 0 : 2 * kPfKvTile * 4 * (row_scales(head_dim, mode) > 1 ? row_scales(head_dim, mode) : 1);
 }
+// prefill: scale bytes after each of the two V images (a step's K and V scales; none for the
+// unquantised cache)
+constexpr int pf_vslot_scale_bytes(int eb) { return eb == 2 ? 0 : 2 * kPfKvTile * 4; }
 
 // Decode LDS: per compute wave, a ring of dec_stages tiles (each the K and V codes of 16 keys plus
 // their per-token-head scales) and one Q slot (the q rows of one segment); then the merge area

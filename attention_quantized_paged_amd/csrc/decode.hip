@@ -199,12 +199,16 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
   const int tr_swz = dec_swz<ROWB>(tr_row);
   const int k_swz = dec_swz<ROWB>(r16);
   // unquantised V rows: lane (r16, kg) reads keys 4kg + r of head-dim column t * 16 + r16, one bf16
-  // each, from logical chunk 2t + r16 / 8 of row 4kg + r
-  int v16_row[4], v16_swz[4];
+  // each, from logical chunk 2t + r16 / 8 of row 4kg + r, stored at chunk (2t + r16 / 8) ^ swz.
+  // Its byte offset in the tile is v16_off[r] ^ (t << 5): the swizzle and t touch only bits 4 to
+  // log2(ROWB) - 1, which the row offset, the lane's byte in the chunk and the tile's position in
+  // LDS (a multiple of 16 rows) leave clear. Applying t as an XOR to the tile's own address keeps
+  // one base per row instead of one hoisted address per (row, t) (NT x 4 registers at head_dim 256).
+  uint32_t v16_off[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    v16_row[r] = (4 * kg + r) * ROWB + (r16 & 7) * 2;
-    v16_swz[r] = dec_swz<ROWB>(4 * kg + r);
+    const int sw = dec_swz<ROWB>(4 * kg + r);
+    v16_off[r] = (uint32_t)((4 * kg + r) * ROWB + (r16 & 7) * 2 + ((sw >> 1) << 5) + (((r16 >> 3) ^ (sw & 1)) << 4));
   }
   // byte offset, within a tile's 16 rows of a page, of this lane's 16-byte chunk in copy i:
   // LDS chunk q = 64 i + lane holds logical chunk (q % CPR) ^ dec_swz(row) of row q / CPR
@@ -393,12 +397,13 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
 #pragma unroll
         for (int t2 = 0; t2 < NT / 2; ++t2) t.vw[t2] = lds_read_tr8(vl + tr_base + (((2 * t2 + tr_hi) ^ tr_swz) << 4));
       } else {
+        static_assert(TB % (16 * ROWB) == 0 && SLOT % (16 * ROWB) == 0, "V tiles start at multiples of 16 rows");
+        const uint32_t vo = (uint32_t)(vl - smem);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
           uint32_t e[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            e[r] = *(const uint16_t*)(vl + v16_row[r] + (((2 * tt + (r16 >> 3)) ^ v16_swz[r]) << 4));
+          for (int r = 0; r < 4; ++r) e[r] = *(const uint16_t*)(smem + ((vo + v16_off[r]) ^ (uint32_t)(tt << 5)));
           t.vb[tt][0] = e[0] | (e[1] << 16);
           t.vb[tt][1] = e[2] | (e[3] << 16);
         }
@@ -709,10 +714,7 @@ static int dec_d(const AttnArgs& a, hipStream_t st) {
   switch (a.head_dim) {
     case 64: return launch_dec<64, DT, MODE>(a, st);
     case 128: return launch_dec<128, DT, MODE>(a, st);
-    case 256:
-      // the unquantised cache at head_dim 256 needs more LDS than a CU has (the schedule refuses it)
-      if constexpr (DT != AQP_KV_AUTO) return launch_dec<256, DT, MODE>(a, st);
-      break;
+    case 256: return launch_dec<256, DT, MODE>(a, st);
   }
   set_error("aqp_paged_attention: unsupported head_dim %d", a.head_dim);
   return AQP_ERR_UNSUPPORTED;

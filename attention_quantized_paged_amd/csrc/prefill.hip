@@ -67,11 +67,11 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   static_assert(RT >= 1 && ROWS % (16 * WAVES) == 0, "rows must split evenly over the waves");
   constexpr int RPW = 16 * RT;                    // query rows per wave
   constexpr int KT = kPfKvTile;                   // keys per step (two 16-key tiles)
-  constexpr int NS = kPfStages;                   // LDS ring stages
   constexpr int EB = DT == AQP_KV_AUTO ? 2 : 1;   // bytes per stored element (bf16 when unquantised)
+  constexpr int NS = pf_stages(D, EB);            // LDS ring stages
   constexpr int ROWB = D * EB;                    // bytes of one staged key row
   constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
-  constexpr int STAGE = 2 * KT * ROWB + pf_stage_scale_bytes(D, MODE);  // K rows, V rows, K scales, V scales
+  constexpr int STAGE = 2 * KT * ROWB + pf_stage_scale_bytes(D, MODE, EB);  // K rows, V rows, K scales, V scales
   constexpr int KV_INSTR = KT * CPR / 64;         // 1 KB copies per K (or V) step
   constexpr int IPW = 2 * KV_INSTR / WAVES;       // K+V copies per wave per step
   static_assert(IPW >= 1 && (2 * KV_INSTR) % WAVES == 0, "copies must split evenly over the waves");
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   // written once per work-group and read by every wave
   constexpr int IMG = KT * D * 2;                 // one K (or V) image of a step
   constexpr int KIMG = NS * STAGE;                // two K images after the ring
-  constexpr int VSLOT = IMG + 2 * KT * 4;         // V image + the step's K and V scales
+  constexpr int VSLOT = IMG + pf_vslot_scale_bytes(EB);  // V image + the step's K and V scales
   constexpr int VIMG = KIMG + 2 * IMG;            // two V slots
   constexpr int KBLK = 2 * QS;                    // K blocks per image: [key tile][depth slice]
   constexpr int KB_PW = KBLK / WAVES;             // K blocks each wave converts
@@ -647,10 +647,7 @@ static int pf_d(const AttnArgs& a, hipStream_t st) {
   switch (a.head_dim) {
     case 64: return launch_pf<64, DT, MODE>(a, st);
     case 128: return launch_pf<128, DT, MODE>(a, st);
-    case 256:
-      // the unquantised cache at head_dim 256 needs more LDS than a CU has (the schedule refuses it)
-      if constexpr (DT != AQP_KV_AUTO) return launch_pf<256, DT, MODE>(a, st);
-      break;
+    case 256: return launch_pf<256, DT, MODE>(a, st);
   }
   set_error("aqp_paged_attention: unsupported head_dim %d", a.head_dim);
   return AQP_ERR_UNSUPPORTED;

@@ -292,11 +292,12 @@ def run_all_configs(torch, aqp, W, args):
     import oracle
     ofmt = {0: oracle.FMT_BF16, 1: oracle.FMT_E4M3, 2: oracle.FMT_E5M2, 3: oracle.FMT_INT8}
 
-    # the decode batch once more over an unquantised (bf16, "auto") cache: the same kernels with
-    # two-byte elements, for the quantisation's bandwidth saving side by side
+    # the decode batch and the large prefill once more over an unquantised (bf16, "auto") cache:
+    # the same kernels with two-byte elements, for the quantisation's saving side by side
     auto3 = W.scaled(W.CFG3, name="decode64_bf16_auto_llama8b", kv_dtype="auto")
+    auto2 = W.scaled(W.CFG2, name="prefill_bf16_auto_d256_bs2176", kv_dtype="auto")
     only = set(x for x in args.only.split(",") if x)
-    for w in (W.CFG1, W.CFG2, W.CFG3, W.CFG4, W.CFG5A, W.CFG5B, auto3):
+    for w in (W.CFG1, W.CFG2, W.CFG3, W.CFG4, W.CFG5A, W.CFG5B, auto3, auto2):
         if only and w.name not in only:
             continue
         log(args, f"[bench] {w.name}")

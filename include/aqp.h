@@ -83,7 +83,7 @@ typedef enum {
  *    page + block_size*head_dim + 4*(r*head_dim/32 + g));
  *  - page_bytes is that content rounded up to a multiple of 128 bytes;
  *  - slot s is row (s % block_size) of block (s / block_size).
- * Supported: head_dim in {64, 128, 256} (AUTO: 64 and 128 in attention);
+ * Supported: head_dim in {64, 128, 256} (every dtype and mode);
  * block_size a positive multiple of 16. */
 typedef struct {
   int32_t num_blocks;

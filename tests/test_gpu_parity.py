@@ -63,6 +63,13 @@ SMALL = [
     W.Workload("auto_mixed_d128", "auto", ((1, 600), (70, 310), (33, 33), (1, 17)), 32, 8, 128, 16, 80, seed=90),
     W.Workload("auto_prefill_d64_w_cap", "auto", ((40, 40), (9, 130)), 8, 2, 64, 32, 12, window=50, softcap=10.0,
                seed=96),
+    # the unquantised cache at head_dim 256: decode units of 4 q heads (two or four per KV head),
+    # a three-step prefill ring, split decode ranges and split prefill key runs
+    W.Workload("auto_d256_decode_g8_split", "auto", ((1, 2500), (1, 77), (1, 1), (1, 640)), 16, 2, 256, 16, 220,
+               seed=231),
+    W.Workload("auto_d256_prefill_bs2176", "auto", ((300, 300), (37, 37), (5, 80)), 16, 2, 256, 2176, 3, seed=232),
+    W.Workload("auto_d256_mixed_g16_w_cap", "auto", ((1, 900), (40, 200), (1, 31), (17, 17)), 32, 2, 256, 32, 60,
+               window=150, softcap=20.0, seed=233),
     # per-group scales (one per 32 head-dim channels): every codec and head_dim, decode (split and
     # whole), prefill (64- and 128-row items) and mixed batches, window and soft-cap
     W.scaled(W.CFG3, name="pg_e4m3_decode_llama8b", kv_dtype="fp8_per_group",
@@ -365,7 +372,7 @@ def _random_workload(seed):
     dtypes = ["fp8_e4m3", "fp8_e5m2", "int8", "int8_per_token_head", "fp8_per_token_head",
               "fp8_e5m2_per_token_head", "int8_per_group", "fp8_per_group", "fp8_e5m2_per_group", "auto"]
     dt = dtypes[seed % len(dtypes)]
-    d = int(rng.choice([64, 128] if dt == "auto" else [64, 128, 256]))
+    d = int(rng.choice([64, 128, 256]))
     bs = int(rng.choice([16, 32, 64]))
     hkv = int(rng.integers(1, 4))
     g = int(rng.choice([1, 2, 4, 6, 8, 16]))

@@ -121,8 +121,8 @@ def test_cache_write_argument_errors():
 
 def test_unquantised_cache_geometry_and_limits():
     """The "auto" cache stores two bytes per element: the schedule records that size and sizes
-    the decode and prefill LDS from it; head_dim 256 (more LDS than a CU has) is refused rather
-    than run."""
+    the decode and prefill LDS from it (no scale bytes). At head_dim 256 the prefill ring holds
+    three steps and fills a CU's 160 KB exactly; a decode unit holds 4 q heads."""
     desc = aqp.cache_desc(8, 16, 2, 128, "auto")
     pb, bb, tb = aqp.cache_bytes(desc)
     assert pb == 16 * 128 * 2 and bb == 2 * 2 * pb
@@ -133,12 +133,18 @@ def test_unquantised_cache_geometry_and_limits():
     assert h["dec_lds_bytes"] == 4 * (2 * (2 * 16 * 128 * 2) + 4 * 128 * 2) + 4 * 4 * (128 + 4) * 4
     h2 = aqp.get_schedule(params, desc, np.array([40, 17], np.int32), np.array([0, 5, 6], np.int32)).header
     assert h2["num_pf_items"] > 0
-    assert h2["pf_lds_bytes"] == 4 * (2 * 32 * 128 * 2 + 2 * 32 * 4) + 4 * 32 * 128 * 2 + 2 * 2 * 32 * 4
+    assert h2["pf_lds_bytes"] == 4 * (2 * 32 * 128 * 2) + 4 * 32 * 128 * 2
     assert h2["pf_lds_bytes"] <= 160 * 1024
     d256 = aqp.cache_desc(8, 16, 2, 256, "auto")
-    with pytest.raises(aqp.AqpError) as e:
-        aqp.get_schedule(aqp.attn_params(8, 2, 256, 4), d256, sl, qsl)
-    assert e.value.status == aqp.ERR_UNSUPPORTED
+    h3 = aqp.get_schedule(aqp.attn_params(8, 2, 256, 4), d256, sl, np.array([0, 5, 6], np.int32)).header
+    assert h3["num_pf_items"] > 0 and h3["heads_per_unit"] == 4
+    assert h3["pf_lds_bytes"] == 3 * (2 * 32 * 256 * 2) + 4 * 32 * 256 * 2 == 160 * 1024
+    # 4 compute waves: a ring of two 16-key tiles (K and V) and 4 q rows each, then the merge area
+    assert h3["dec_lds_bytes"] == 4 * (2 * (2 * 16 * 256 * 2) + 4 * 256 * 2) + 4 * 4 * (256 + 4) * 4
+    assert h3["dec_lds_bytes"] <= 160 * 1024
+    # 8 q heads per KV head: two decode units of 4 heads each
+    h4 = aqp.get_schedule(aqp.attn_params(16, 2, 256, 4), aqp.cache_desc(8, 16, 2, 256, "auto"), sl, qsl).header
+    assert h4["group_heads"] == 4
 
 
 def test_binding_refuses_mis_sized_buffers():

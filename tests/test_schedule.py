@@ -57,12 +57,27 @@ def test_decode_coverage_exact(seqs, hq, hkv, d, bs, window, par):
     _check_decode(seqs, hq, hkv, d, bs, window, par)
 
 
-def _check_decode(seqs, hq, hkv, d, bs, window, par, split=0):
-    s, sl, qsl, params, desc = _sched(seqs, hq, hkv, d, bs, window=window, par=par, split=split)
+# the unquantised cache: at head_dim 256 a decode unit holds 4 q heads (8 for one-byte codes)
+AUTO_CASES = [
+    (((1, 17), (1, 40)), 4, 2, 256, 16, 0, 0),
+    (((1, 1000), (1, 33), (5, 70), (1, 16), (0, 9), (1, 1)), 16, 2, 256, 16, 0, 3),
+    (((1, 3000),) * 2 + ((40, 300),), 32, 2, 256, 32, 700, 7),
+    (((1, 900), (1, 77)), 16, 2, 128, 16, 0, 0),
+]
+
+
+@pytest.mark.parametrize("seqs,hq,hkv,d,bs,window,par", AUTO_CASES)
+def test_decode_coverage_exact_unquantised(seqs, hq, hkv, d, bs, window, par):
+    _check_decode(seqs, hq, hkv, d, bs, window, par, dtype="auto")
+
+
+def _check_decode(seqs, hq, hkv, d, bs, window, par, split=0, dtype="fp8_e4m3"):
+    s, sl, qsl, params, desc = _sched(seqs, hq, hkv, d, bs, dtype=dtype, window=window, par=par, split=split)
     h = s.header
     segs, wgs, comb, pf = _arrays(s)
     G = hq // hkv
-    assert h["kv_elem_bytes"] == 1 and h["head_dim"] == d and h["block_size"] == bs
+    eb = 2 if dtype == "auto" else 1
+    assert h["kv_elem_bytes"] == eb and h["head_dim"] == d and h["block_size"] == bs
     if h["num_dec_wgs"] == 0:
         # no decode work: no segments, no work-group ranges, no parts (nothing is launched)
         assert len(segs) == 0 and h["num_parts"] == 0 and h["num_dec_comb"] == 0
@@ -98,7 +113,8 @@ def _check_decode(seqs, hq, hkv, d, bs, window, par, split=0):
     # partial slots: each used exactly once and named by exactly one merge item
     parts = sorted(sg["part"] for sg in segs if sg["part"] >= 0)
     assert parts == list(range(h["num_parts"]))
-    gh = min(G, 16 if d <= 128 else 8)
+    gh = min(G, 16 if d <= 128 else (4 if eb == 2 else 8))
+    assert all(sg["nheads"] <= gh and sg["head0"] % gh == 0 for sg in segs)
     dcomb = comb[: h["num_dec_comb"]]
     assert np.all(dcomb["part_stride"] == gh) and np.all(dcomb["first_slot"] % gh == 0)
     from_comb = sorted(p for c in dcomb for p in range(c["first_slot"] // gh, c["first_slot"] // gh + c["num_parts"]))
@@ -131,7 +147,7 @@ def _steps(it, window):
 
 
 @pytest.mark.parametrize("split", [0, 1, 3])
-@pytest.mark.parametrize("dtype", ["fp8_e4m3", "int8_per_group"])
+@pytest.mark.parametrize("dtype", ["fp8_e4m3", "int8_per_group", "auto"])
 @pytest.mark.parametrize("rows", [0, 64, 128])
 @pytest.mark.parametrize("seqs,hq,hkv,d,bs,window,par", CASES)
 def test_prefill_coverage_and_order(seqs, hq, hkv, d, bs, window, par, rows, split, dtype):
@@ -155,7 +171,7 @@ def _check_prefill(seqs, hq, hkv, d, bs, window, par, rows, split, dtype="fp8_e4
         assert h_rows(s) == rows
     _, _, comb, pf = _arrays(s)
     G = hq // hkv
-    gh = min(G, 16 if d <= 128 else 8)
+    gh = min(G, 16 if d <= 128 else (4 if dtype == "auto" else 8))
     _check_launch_order(pf, window)
     families = {}
     for it in pf:
