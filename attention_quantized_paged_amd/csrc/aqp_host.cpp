@@ -54,8 +54,9 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
   if (rc) return rc;
   if (d.num_blocks < 0 || d.num_kv_heads <= 0 || d.block_size <= 0 || d.head_dim <= 0) { *why = "non-positive cache dimension"; return AQP_ERR_INVALID; }
   if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256) { *why = "head_dim must be 64, 128 or 256"; return AQP_ERR_UNSUPPORTED; }
-  if (d.block_size % kTileKeys != 0) { *why = "block_size must be a multiple of 16"; return AQP_ERR_UNSUPPORTED; }
-  if ((int64_t)d.block_size * d.head_dim > (1ll << 30)) { *why = "block_size too large"; return AQP_ERR_UNSUPPORTED; }
+  // (any block size: the kernels gather a 16-key tile that spans several blocks row by row; the
+  // bound keeps the float quotient of that gather exact)
+  if (d.block_size > kMaxBlockSize || (int64_t)d.block_size * d.head_dim > (1ll << 30)) { *why = "block_size too large"; return AQP_ERR_UNSUPPORTED; }
   g->head_dim = d.head_dim;
   g->block_size = d.block_size;
   // bytes of one stored element: one per code; two for the unquantised bf16 cache. The kernels
@@ -72,7 +73,7 @@ int make_geometry(const aqp_cache_desc& d, Geometry* g, const char** why) {
   // unquantised cache): a ring of pf_stages steps, each the K and V elements of kPfKvTile keys
   // plus their row scales; then two K and two V operand images of a step in bf16 (widened once
   // per work-group), each V image followed by a copy of its step's scales (none unquantised).
-  if (pf32_applies(d.dtype, d.mode, d.head_dim))
+  if (pf32_applies(d.dtype, d.mode, d.head_dim, d.block_size))
     g->pf_lds_bytes = pf32_lds_bytes(d.head_dim, d.mode);
   else
     g->pf_lds_bytes = pf_stages(d.head_dim, g->staged_elem_bytes) *
@@ -173,7 +174,7 @@ extern "C" int aqp_cache_write(const aqp_cache_desc* desc, void* cache, const vo
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.narrow = 2 * num_tokens * desc->num_kv_heads < ((int64_t)1 << 31) && a.total_slots < ((int64_t)1 << 31) &&
-             desc->num_kv_heads >= 2;
+             desc->num_kv_heads >= 2 && desc->block_size >= 2;
   a.heads_magic = a.bs_magic = 0;
   a.heads_shift = a.bs_shift = 0;
   if (a.narrow) {
@@ -372,7 +373,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
     int64_t total_steps = 0;
     for (const PfItem& it : pf) total_steps += steps_of(it);
     const int64_t cap = (int64_t)device_cu_count() *
-                        (pf32_applies(desc->dtype, desc->mode, desc->head_dim) ? pf32_wgs_per_cu(desc->head_dim, rows, g.pf_lds_bytes)
+                        (pf32_applies(desc->dtype, desc->mode, desc->head_dim, desc->block_size) ? pf32_wgs_per_cu(desc->head_dim, rows, g.pf_lds_bytes)
                                                                : pf_wgs_per_cu(desc->head_dim, rows, g.pf_lds_bytes));
     if (p.prefill_kv_split > 1) {
       sp.max_runs = p.prefill_kv_split;
@@ -392,7 +393,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
   // the prefill and needs the room a second work-group takes), kPfRowsSmall when kPfRows-row items,
   // even after key splits, would give the CUs fewer than two work-groups each
   int32_t pf_rows = p.prefill_rows > 0 ? p.prefill_rows : kPfRows;
-  if (!pf32_applies(desc->dtype, desc->mode, desc->head_dim) && pf_rows < pf_waves(desc->head_dim) * 16)
+  if (!pf32_applies(desc->dtype, desc->mode, desc->head_dim, desc->block_size) && pf_rows < pf_waves(desc->head_dim) * 16)
     return fail(AQP_ERR_UNSUPPORTED, "aqp_get_schedule: %d rows per prefill item at head_dim %d is not built", pf_rows, desc->head_dim);
   build_items(pf_rows);
   if (p.prefill_rows == 0 && desc->head_dim <= 128 && total_tiles == 0 && !pf.empty()) {
@@ -668,7 +669,7 @@ static int attention(const aqp_attn_params* params, const aqp_cache_desc* desc, 
     return r;
   };
   auto run_prefill = [&](void* st) -> int {
-    int r = pf32_applies(desc->dtype, desc->mode, desc->head_dim) ? launch_prefill32(desc->dtype, desc->mode, a, st)
+    int r = pf32_applies(desc->dtype, desc->mode, desc->head_dim, desc->block_size) ? launch_prefill32(desc->dtype, desc->mode, a, st)
                                                   : launch_prefill(desc->dtype, desc->mode, a, st);
     if (r == AQP_OK && n_pf_comb > 0) r = launch_combine(a, n_dec_comb, n_pf_comb, st);
     return r;

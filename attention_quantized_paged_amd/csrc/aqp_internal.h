@@ -22,7 +22,8 @@ constexpr uint32_t kMagic = 0x53505141u;  // "AQPS"
 constexpr uint32_t kVersion = 4;
 
 // ---- compile-time tile geometry of the kernels ----------------------------
-constexpr int kTileKeys = 16;        // keys per KV tile: one 16-row MFMA operand; block_size % 16 == 0
+constexpr int kTileKeys = 16;        // keys per KV tile: one 16-row MFMA operand
+constexpr int kMaxBlockSize = 65536; // largest block size (keys per block)
 constexpr int kDecIterKeys = 16;     // keys per decode iteration (one tile; PV on 16x16x16 MFMA)
 constexpr int kDecWaves = 4;         // compute waves per decode work-group (they split a segment's iterations)
 // q heads per decode unit (MFMA column block): 16, or at head_dim 256 8 (one-byte codes) or 4 (the
@@ -68,8 +69,11 @@ constexpr int pf_wgs_per_cu(int head_dim, int rows, int32_t lds_bytes) {
 // scales up to head_dim 128, where it runs two waves per SIMD; per-group scales, the unquantised
 // cache and head_dim 256 keep the 16x16 kernel (prefill.hip), which was measured faster there
 // (a single wave per SIMD hides little of its vector work under its matrix instructions).
-constexpr bool pf32_applies(int dtype, int mode, int head_dim) {
-  return head_dim <= 128 && dtype != AQP_KV_AUTO && (mode == AQP_SCALE_PER_TENSOR || mode == AQP_SCALE_PER_TOKEN_HEAD);
+// Block sizes that are not a multiple of 16 (a 16-key tile may span several blocks) also keep the
+// 16x16 kernel, which gathers such tiles row by row.
+constexpr bool pf32_applies(int dtype, int mode, int head_dim, int block_size) {
+  return head_dim <= 128 && dtype != AQP_KV_AUTO && (mode == AQP_SCALE_PER_TENSOR || mode == AQP_SCALE_PER_TOKEN_HEAD) &&
+         block_size % kTileKeys == 0;
 }
 constexpr int kPf32Stages = 4;  // LDS ring stages of the 32x32 prefill (four steps ahead)
 // Waves per SIMD its registers are sized for: a wave holds 32 rows of Q (D/4 registers), their
@@ -135,6 +139,11 @@ constexpr int decode_wgs_per_cu(int head_dim, int32_t lds_bytes) {
 // l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1; n / d = (t + ((n - t) >> 1)) >> (l - 1) with
 // t = mulhi(n, m). The host computes (m, l - 1); the kernels apply it (div_invariant).
 inline void invariant_divisor(uint32_t d, uint32_t* m, int32_t* shift) {
+  if (d < 2) {  // not covered by the method: callers divide by 1 themselves
+    *m = 0;
+    *shift = 0;
+    return;
+  }
   int l = 0;
   while ((1ull << l) < d) ++l;
   *m = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);

@@ -50,6 +50,7 @@ struct DecArgs {
   uint16_t* out;
   int64_t page_bytes, block_bytes;
   int32_t block_size, num_kv_heads, num_q_heads, group, max_blocks, group_heads, num_blocks;
+  float inv_bs;       // 1 / block_size (float): row quotients where tiles span blocks
   int64_t num_slots;  // partial-result slots of the scratch ((m, l) follow all slots' O)
   float logit_scale;  // sm_scale * k_scale (per tensor) or sm_scale (per token-head)
   float softcap, inv_softcap;
@@ -143,7 +144,10 @@ __device__ __forceinline__ void merge_store(const DecArgs& a, const float* mg, i
   }
 }
 
-template <int D, int DT, int MODE, bool CAP>
+// GBS: the block size is not a multiple of 16, so a tile's 16 rows may lie in several blocks
+// (up to 16): each row is copied from its own block, its scales likewise, and the absent rows
+// of a tile are masked row by row.
+template <int D, int DT, int MODE, bool CAP, bool GBS>
 __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_per_eu(dec_waves_per_simd(D)))) void decode_kernel(DecArgs a) {
   constexpr int NT = D / 16;   // 16-wide head-dim tiles of the output
   constexpr int QS = D / 32;   // 32-deep MFMA steps of QK^T
@@ -159,7 +163,10 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
   constexpr int TB = kDecIterKeys * ROWB;         // bytes of one K (or V) tile
   constexpr int KI = TB / 1024;                   // 1 KB copies per K (or V) tile
   constexpr int SLOT = dec_slot_bytes(D, MODE, EB);  // K tile, V tile, K scales, V scales
-  constexpr int IPT = 2 * KI + PTH + PG;          // copies per tile
+  // copies per tile: K and V codes, then the scales (one 16-byte copy per tile; row by row in
+  // 4-byte copies where tiles span blocks: 32 per token-head, 32 NG per group)
+  constexpr int SCC = GBS ? (PTH ? 1 : (PG ? (NG + 1) / 2 : 0)) : PTH + PG;
+  constexpr int IPT = 2 * KI + SCC;
   static_assert(KI >= 1 && IPT * (NS - 1) <= 63, "tile copies and waits");
   static_assert(EB == 1 || (!PTH && !PG), "the unquantised cache has no scales");
   static_assert(8 * NG <= 64, "one copy holds a tile's group scales");
@@ -226,7 +233,13 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
   auto advance = [&](Pos p) {
     p.k0 += STEP;
     p.r0 += STEP;
-    while (p.r0 >= a.block_size) { p.r0 -= a.block_size; ++p.bi; }
+    if constexpr (GBS) {
+      const int nb = small_quot(p.r0, a.inv_bs);  // r0 < block_size + STEP
+      p.bi += nb;
+      p.r0 -= nb * a.block_size;
+    } else {
+      while (p.r0 >= a.block_size) { p.r0 -= a.block_size; ++p.bi; }
+    }
     return p;
   };
   // the wave's first tile of a segment and its tile count there (iterations it = w, w+4, ...)
@@ -245,6 +258,17 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
   cptr<int32_t> is_bt = as_const(a.block_tables);
   const uint8_t* is_kv = a.cache;  // K page of the segment's KV head in block 0
   int32_t is_blk = 0;              // block-table entry of the next tile (read one tile ahead)
+  int32_t is_ent[16] = {};         // GBS: entries of the 16 blocks from the next tile's first
+  uint64_t ok_rows = 0;            // GBS: bits 16 (n & 3) ..: rows of tile n in blocks of the pool
+  // the next tile's block-table entries (scalar loads; clamped to the sequence's table row)
+  auto fetch_blk = [&]() {
+    if constexpr (GBS) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) is_ent[j] = is_bt[min(is_p.bi + j, a.max_blocks - 1)];
+    } else {
+      is_blk = is_bt[is_p.bi];
+    }
+  };
   bool is_new = false;             // the next tile opens a segment: its Q rows go first
   uint32_t is_slot = 0;            // ring byte offset of the next tile
   uint64_t ok_bits = 0;            // bit (n & 63): tile n lies in a valid block
@@ -258,12 +282,65 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
         is_new = true;
         is_bt = as_const(a.block_tables) + (int64_t)is_sg.seq * a.max_blocks;
         is_kv = a.cache + (int64_t)is_sg.kvh * a.page_bytes;
-        is_blk = is_bt[is_p.bi];
+        fetch_blk();
         return;
       }
     }
     is_si = s_end;
     is_left = 0;
+  };
+  // GBS: the copies of the next tile row by row. Row t (key k0 + t) lies j = (r0 + t) / bs blocks
+  // after the tile's first block, at row r0 + t - j bs; j < 16 as r0 < bs. An entry outside the
+  // pool masks its rows (block 0 is read in their place).
+  auto row_src = [&](int t, const uint8_t* base, int& rr, bool& ok) {
+    const int n = is_p.r0 + t;
+    const int j = small_quot(n, a.inv_bs);
+    rr = n - j * a.block_size;
+    const int32_t e = sel16(is_ent, j);
+    ok = (uint32_t)e < (uint32_t)a.num_blocks;
+    return base + (uint64_t)(ok ? (uint32_t)e : 0u) * (uint64_t)a.block_bytes;
+  };
+  auto issue_rows = [&]() {
+    const uint32_t slot = ring_lds + is_slot;
+    const int64_t voff = (int64_t)a.num_kv_heads * a.page_bytes;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int q = 64 * i + lane, t = q / CPR;
+      int rr;
+      bool ok;
+      const uint8_t* pg = row_src(t, is_kv, rr, ok);
+      const uint8_t* src = pg + (int64_t)rr * ROWB + ((((q % CPR) ^ dec_swz<ROWB>(t))) << 4);
+      dma16_to_lds(src, slot + (uint32_t)(1024 * i));
+      dma16_to_lds(src + voff, slot + (uint32_t)(TB + 1024 * i));
+    }
+    {
+      int rr;
+      bool ok;
+      row_src(lane & 15, is_kv, rr, ok);
+      const uint32_t rows = (uint32_t)__builtin_amdgcn_ballot_w64(ok && lane < 16) & 0xFFFFu;
+      const int sh = 16 * (n_issued & 3);
+      ok_rows = (ok_rows & ~(0xFFFFull << sh)) | ((uint64_t)rows << sh);
+    }
+    if constexpr (PTH) {
+      // lanes 0..15: the K scales of rows 0..15, lanes 16..31: the V scales
+      int rr;
+      bool ok;
+      const uint8_t* pg = row_src(lane & 15, is_kv + ((lane & 16) ? voff : 0), rr, ok);
+      if (lane < 32) dma4_to_lds(pg + (int64_t)a.block_size * D + 4 * rr, slot + (uint32_t)(2 * TB));
+    }
+    if constexpr (PG) {
+      // [K: 16 rows x NG][V: 16 rows x NG] floats, 64 per copy
+#pragma unroll
+      for (int c = 0; c < SCC; ++c) {
+        const int idx = 64 * c + lane;
+        const int kv = idx / (16 * NG), rem = idx % (16 * NG);
+        const int t = rem / NG, g = rem % NG;
+        int rr;
+        bool ok;
+        const uint8_t* pg = row_src(t, is_kv + (kv ? voff : 0), rr, ok);
+        if (idx < 32 * NG) dma4_to_lds(pg + (int64_t)a.block_size * D + 4 * ((int64_t)rr * NG + g), slot + (uint32_t)(2 * TB + 256 * c));
+      }
+    }
   };
   // issues the next tile if its ring slot (and, for a new segment, a Q slot) is free
   auto issue_next = [&](int n_done, int q_read) {
@@ -279,6 +356,9 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
       ++q_issued;
       is_new = false;
     }
+    if constexpr (GBS) {
+      issue_rows();
+    } else {
     // an entry outside the pool masks its tile instead of reading outside the cache
     const bool ok = (uint32_t)is_blk < (uint32_t)a.num_blocks;
     ok_bits = (ok_bits & ~(1ull << (n_issued & 63))) | ((uint64_t)ok << (n_issued & 63));
@@ -303,11 +383,12 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
                           4 * (int64_t)is_p.r0 * NG + 16 * sl;
       if (lane < 8 * NG) dma16_to_lds(sp, slot + (uint32_t)(2 * TB));
     }
+    }
     ++n_issued;
     is_slot = is_slot + SLOT == NS * SLOT ? 0u : is_slot + SLOT;
     if (--is_left > 0) {
       is_p = advance(is_p);
-      is_blk = is_bt[is_p.bi];  // needed only at the next issue: its latency hides behind a tile
+      fetch_blk();  // needed only at the next issue: its latency hides behind a tile
     } else {
       seek(is_si + 1);
     }
@@ -323,7 +404,7 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
     is_new = true;
     is_bt = as_const(a.block_tables) + (int64_t)is_sg.seq * a.max_blocks;
     is_kv = a.cache + (int64_t)is_sg.kvh * a.page_bytes;
-    is_blk = is_bt[is_p.bi];
+    fetch_blk();
   } else {
     seek(s_begin + 1);
   }
@@ -364,7 +445,10 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
       uint32_t vmask;
       bool full;
     };
-    auto score = [&](const uint8_t* kl, int k0, bool ok, TileS& t) {
+    // rows_ok: bit t set when row t of the tile lies in a block of the pool (without GBS a tile
+    // lies in one block: a flag)
+    using RowMask = std::conditional_t<GBS, uint32_t, bool>;
+    auto score = [&](const uint8_t* kl, int k0, RowMask rows_ok, TileS& t) {
       const uint8_t* vl = kl + TB;
       // ---- S^T = K * Q^T: lane holds keys k0 + 4kg + r of head r16
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -431,14 +515,15 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
       // masking is needed only on the segment's edge tiles (and tiles of an invalid block); rows
       // outside the range may hold unwritten bytes: their logits are replaced, their V codes
       // masked to zero and (per token-head) their scales replaced, so no NaN reaches the sums
-      t.full = ok && k0 >= sg.k_lo && k0 + kTileKeys <= sg.k_hi;
+      t.full = (GBS ? (uint32_t)rows_ok == 0xFFFFu : (bool)rows_ok) && k0 >= sg.k_lo && k0 + kTileKeys <= sg.k_hi;
       t.vmask = 0xFFFFFFFFu;
       if (!t.full) {
         t.vmask = 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = k0 + 4 * kg + r;
-          const bool kok = ok && key >= sg.k_lo && key < sg.k_hi;
+          const bool row_ok = GBS ? (((uint32_t)rows_ok >> (4 * kg + r)) & 1) != 0 : (bool)rows_ok;
+          const bool kok = row_ok && key >= sg.k_lo && key < sg.k_hi;
           t.x[r] = kok ? t.x[r] : -INFINITY;
           if (kok) t.vmask |= 0xFFu << (8 * r);
         }
@@ -526,6 +611,10 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
       issue_next(n_done, q_read);  // a copy held back for want of a Q slot
     };
     auto next_slot = [&](uint32_t c) { return c + SLOT == NS * SLOT ? 0u : c + SLOT; };
+    auto tile_rows = [&](int n) -> RowMask {
+      if constexpr (GBS) return (uint32_t)(ok_rows >> (16 * (n & 3))) & 0xFFFFu;
+      else return (ok_bits >> (n & 63)) & 1;
+    };
     // two of the wave's tiles per iteration (one reduction and rescale check for both) where the
     // ring holds at least three tiles (so one stays in flight while a pair is computed), then the
     // rest one at a time
@@ -537,8 +626,8 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
       const uint8_t* kl0 = ring + c_slot;
       const uint8_t* kl1 = ring + next_slot(c_slot);
       TileS t0, t1;
-      score(kl0, ck0, (ok_bits >> (n_done & 63)) & 1, t0);
-      score(kl1, ck0 + STEP, (ok_bits >> ((n_done + 1) & 63)) & 1, t1);
+      score(kl0, ck0, tile_rows(n_done), t0);
+      score(kl1, ck0 + STEP, tile_rows(n_done + 1), t1);
       const float mx = max_over_rows(fmaxf(fmaxf(fmaxf(t0.x[0], t0.x[1]), fmaxf(t0.x[2], t0.x[3])),
                                            fmaxf(fmaxf(t1.x[0], t1.x[1]), fmaxf(t1.x[2], t1.x[3]))));
       const float m_use = rescale_to(mx);
@@ -556,7 +645,7 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
       if (k == 0) load_q();
       const uint8_t* kl0 = ring + c_slot;
       TileS t0;
-      score(kl0, ck0, (ok_bits >> (n_done & 63)) & 1, t0);
+      score(kl0, ck0, tile_rows(n_done), t0);
       const float m_use = rescale_to(max_over_rows(fmaxf(fmaxf(t0.x[0], t0.x[1]), fmaxf(t0.x[2], t0.x[3]))));
       accumulate(kl0, t0, m_use);
       ++n_done;
@@ -683,6 +772,7 @@ static int launch_dec(const AttnArgs& a, hipStream_t st) {
   d.page_bytes = a.page_bytes;
   d.block_bytes = a.block_bytes;
   d.block_size = a.block_size;
+  d.inv_bs = 1.0f / (float)a.block_size;
   d.num_kv_heads = a.num_kv_heads;
   d.num_q_heads = a.num_q_heads;
   d.group = a.group;
@@ -697,10 +787,17 @@ static int launch_dec(const AttnArgs& a, hipStream_t st) {
   d.seq_lens = (const int32_t*)(a.meta_dev + h.off_seq_lens);
   d.alibi = a.alibi_slopes;
   d.sinks = a.sinks;
-  if (a.softcap > 0.0f)
-    hipLaunchKernelGGL((decode_kernel<D, DT, MODE, true>), dim3(h.num_dec_wgs), dim3((kDecWaves + 1) * 64), h.dec_lds_bytes, st, d);
-  else
-    hipLaunchKernelGGL((decode_kernel<D, DT, MODE, false>), dim3(h.num_dec_wgs), dim3((kDecWaves + 1) * 64), h.dec_lds_bytes, st, d);
+  const dim3 grid(h.num_dec_wgs), block((kDecWaves + 1) * 64);
+  if (a.block_size % kTileKeys != 0) {
+    if (a.softcap > 0.0f)
+      hipLaunchKernelGGL((decode_kernel<D, DT, MODE, true, true>), grid, block, h.dec_lds_bytes, st, d);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, DT, MODE, false, true>), grid, block, h.dec_lds_bytes, st, d);
+  } else if (a.softcap > 0.0f) {
+    hipLaunchKernelGGL((decode_kernel<D, DT, MODE, true, false>), grid, block, h.dec_lds_bytes, st, d);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<D, DT, MODE, false, false>), grid, block, h.dec_lds_bytes, st, d);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("aqp_paged_attention: decode launch failed: %s", hipGetErrorString(e));

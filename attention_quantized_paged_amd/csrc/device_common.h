@@ -102,6 +102,12 @@ __device__ __forceinline__ void dma16_to_lds(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory");
 }
 
+// Direct global -> LDS copy of 4 bytes per lane (global_load_lds_dword): lane l's 4 bytes land at
+// LDS byte address lds_base + 4 * l (lanes with exec off write nothing). lds_base wave-uniform.
+__device__ __forceinline__ void dma4_to_lds(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(g) : "memory");
+}
+
 // Wait until at most n of this wave's vector memory operations are outstanding (n < 16).
 __device__ __forceinline__ void wait_vmcnt(int n) {
   switch (n) {
@@ -172,6 +178,24 @@ __device__ __forceinline__ T load_const(cptr<T> p) {
 __device__ __forceinline__ uint32_t div_invariant(uint32_t n, uint32_t m, int32_t shift) {
   const uint32_t t = __umulhi(n, m);
   return (t + ((n - t) >> 1)) >> shift;
+}
+
+// n / d for 0 <= n < d + 128 and 1 <= d <= 65536, from rd = 1.0f / d (rounded to float): the
+// quotient of (n + 1/2) / d lies at least 1/(2d) from an integer, and the rounding of rd and of
+// the product move it by less than 2^-23 of its value (< (d + 129) / d * 2^-23 < 1/(2d)), so
+// truncation gives the exact integer quotient. (Used where a 16-key tile meets blocks of any
+// size: n is a row offset inside the tile's first block plus a row of the tile.)
+__device__ __forceinline__ int small_quot(int n, float rd) { return (int)(((float)n + 0.5f) * rd); }
+
+// e[j] for a per-lane j in [0, 16) and 16 wave-uniform values (a select tree on j's bits).
+__device__ __forceinline__ int32_t sel16(const int32_t (&e)[16], int j) {
+  int32_t a[8], b[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = (j & 1) ? e[2 * i + 1] : e[2 * i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = (j & 2) ? a[2 * i + 1] : a[2 * i];
+  const int32_t c0 = (j & 4) ? b[1] : b[0], c1 = (j & 4) ? b[3] : b[2];
+  return (j & 8) ? c1 : c0;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

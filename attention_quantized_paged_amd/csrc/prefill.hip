@@ -42,8 +42,9 @@ struct PfArgs {
   float v_scale;
   const float* alibi;  // [num_q_heads] slopes or null
   const float* sinks;  // [num_q_heads] sink logits or null
-  uint32_t bs_magic;   // key / block_size = div_invariant(key, bs_magic, bs_shift)
+  uint32_t bs_magic;   // key / block_size = div_invariant(key, bs_magic, bs_shift) (block_size >= 2)
   int32_t bs_shift;
+  float inv_bs;        // 1 / block_size (float): row quotients where tiles span blocks
 };
 
 // 16-byte chunk swizzle of a staged row: chunk c of row `row` is stored at chunk
@@ -58,7 +59,10 @@ __device__ __forceinline__ int swz(int row) {
   return ((row / RPL) % CPR) ^ (((row >> 4) & 1) * (CPR / 2));
 }
 
-template <int D, int DT, int MODE, bool CAP, int ROWS>
+// GBS: the block size is not a multiple of 16, so a 16-key tile may span several blocks (up to
+// 16): its rows are copied from their own blocks, its scales likewise in 4-byte copies, and the
+// absent rows of a tile are masked row by row.
+template <int D, int DT, int MODE, bool CAP, int ROWS, bool GBS>
 __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 2))) void prefill_kernel(PfArgs a) {
   constexpr int NT = D / 16;
   constexpr int QS = D / 32;
@@ -89,7 +93,8 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   constexpr int PG = MODE == AQP_SCALE_PER_GROUP ? 1 : 0;
   constexpr int NG = D / AQP_SCALE_GROUP;          // scale groups of a row (per-group mode)
   constexpr int SCH = 64 * NG;                     // bytes of one 16-key tile's group scales
-  constexpr int SCI = PTH ? 1 : (PG ? (4 * SCH + 1023) / 1024 : 0);  // scale copies per step
+  // scale copies per step (64 x 4 bytes each where tiles span blocks)
+  constexpr int SCI = PTH ? 1 : (PG ? (GBS ? NG : (4 * SCH + 1023) / 1024) : 0);
   static_assert(EB == 1 || (!PTH && !PG), "the unquantised cache has no scales");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
@@ -159,12 +164,47 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   const int n_steps = (k_end - k_begin + KT - 1) / KT;
   const float xscale = CAP ? a.logit_scale : a.logit_scale * kLog2e;
   const int last_tile = ((it.L - 1) / kTileKeys) * kTileKeys;  // first key of the tile holding key L-1
-  // whether the block-table entry of the 16-key tile starting at key k0 names a block of the pool
-  // (keys of a tile whose entry lies outside it are absent: masked like keys out of range, and
-  // their codes, read from block 0 instead, never reach a product)
-  auto tile_ok = [&](int k0) {
-    const int t = min(k0, last_tile);
-    return (uint32_t)bt[(int)div_invariant((uint32_t)t, a.bs_magic, a.bs_shift)] < (uint32_t)a.num_blocks;
+  // block of key k (block_size 1, possible only with GBS, is outside the invariant-division method)
+  auto key_block = [&](int k) {
+    if constexpr (GBS) return a.block_size == 1 ? k : (int)div_invariant((uint32_t)k, a.bs_magic, a.bs_shift);
+    else return (int)div_invariant((uint32_t)k, a.bs_magic, a.bs_shift);
+  };
+  // GBS: entries of the 16 blocks from the one holding key k0 (scalar loads, clamped to the
+  // sequence's table row) and k0's row in its block
+  struct Ents { int32_t e[16]; int r0; };
+  auto tile_ents = [&](int k0) {
+    Ents t;
+    const int bi = key_block(k0);
+    t.r0 = k0 - bi * a.block_size;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) t.e[j] = bt[min(bi + j, a.max_blocks - 1)];
+    return t;
+  };
+  // GBS: block (entry, or 0 outside the pool) and row of row n - r0 of a tile whose first key
+  // sits at row r0 of its block (n = r0 + tile row: j = n / bs < 16 blocks on)
+  auto row_block = [&](const Ents& t, int n, int& rr) {
+    const int j = small_quot(n, a.inv_bs);
+    rr = n - j * a.block_size;
+    const int32_t e = sel16(t.e, j);
+    return (uint32_t)e < (uint32_t)a.num_blocks ? e : 0;
+  };
+  // rows of the 16-key tile starting at key k0 whose block-table entries name blocks of the pool
+  // (bit t: the row copied for key k0 + t, i.e. key min(k0 + t, L - 1); keys of a block whose
+  // entry lies outside it are absent: masked like keys out of range, and their codes, read from
+  // block 0 instead, never reach a product)
+  using RowMask = std::conditional_t<GBS, uint32_t, bool>;  // without GBS a tile is whole or absent
+  auto tile_rows = [&](int k0) -> RowMask {
+    if constexpr (GBS) {
+      // rows past L hold key L - 1's row, whose block may differ from the one of key k0 + t
+      const int base = min(k0, it.L - 1);
+      const Ents en = tile_ents(base);
+      const int key = min(k0 + (lane & 15), it.L - 1);
+      const int j = small_quot(en.r0 + (key - base), a.inv_bs);
+      const bool ok = (uint32_t)sel16(en.e, j) < (uint32_t)a.num_blocks;
+      return (uint32_t)__builtin_amdgcn_ballot_w64(ok && lane < 16) & 0xFFFFu;
+    } else {
+      return (uint32_t)bt[key_block(min(k0, last_tile))] < (uint32_t)a.num_blocks;
+    }
   };
 
   float m[RT], l[RT];
@@ -197,22 +237,54 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       const int lc = (q % CPR) ^ swz<ROWB>(row);
       // tile of this copy (uniform), clamped to the tile of key L-1
       const int tile_k0 = min(kb0 + ((q0 / CPR) & ~15), last_tile);
-      const int tbi = (int)div_invariant((uint32_t)tile_k0, a.bs_magic, a.bs_shift);
-      const int tr0 = tile_k0 - tbi * a.block_size;
-      int32_t blk = bt[tbi];
-      if ((uint32_t)blk >= (uint32_t)a.num_blocks) blk = 0;  // invalid table entry: stay in the pool
-      const int key = min(kb0 + row, it.L - 1);
-      const uint8_t* src = (kv ? vbase : kbase) + (int64_t)blk * a.block_bytes +
-                           (int64_t)(tr0 + (key - tile_k0)) * ROWB + lc * 16;
+      const int key = min(kb0 + row, it.L - 1);  // in [tile_k0, tile_k0 + 16)
+      const uint8_t* src;
+      if constexpr (GBS) {
+        const Ents en = tile_ents(tile_k0);
+        int rr;
+        const int32_t blk = row_block(en, en.r0 + (key - tile_k0), rr);
+        src = (kv ? vbase : kbase) + (int64_t)blk * a.block_bytes + (int64_t)rr * ROWB + lc * 16;
+      } else {
+        const int tbi = key_block(tile_k0);
+        const int tr0 = tile_k0 - tbi * a.block_size;
+        int32_t blk = bt[tbi];
+        if ((uint32_t)blk >= (uint32_t)a.num_blocks) blk = 0;  // invalid table entry: stay in the pool
+        src = (kv ? vbase : kbase) + (int64_t)blk * a.block_bytes + (int64_t)(tr0 + (key - tile_k0)) * ROWB + lc * 16;
+      }
       dma16_to_lds(src, sbase + (uint32_t)(kv * KT * ROWB + q0 * 16));
     }
-    if constexpr (PTH) {
+    if constexpr (GBS && (PTH || PG)) {
+      if (wave == WAVES - 1) {
+        // row by row, 4 bytes per lane: per token-head [K scales of the 32 keys][V scales]; per
+        // group [K tile 0][K tile 1][V tile 0][V tile 1], 16 rows x NG floats each
+        const int t0 = min(kb0, last_tile), t1 = min(kb0 + 16, last_tile);
+        const Ents e0 = tile_ents(t0), e1 = tile_ents(t1);
+#pragma unroll
+        for (int c = 0; c < SCI; ++c) {
+          const int idx = 64 * c + lane;
+          const int per = 16 * (PTH ? 1 : NG);           // floats of one (tile, K or V)
+          const int c2 = idx / per, rem = idx - c2 * per;
+          const int tl = c2 & 1, kv = c2 >> 1;
+          const int row = PTH ? rem : rem / NG, g = PTH ? 0 : rem % NG;
+          const int tk0 = tl ? t1 : t0;
+          const int key = min(kb0 + 16 * tl + row, it.L - 1);  // in [tk0, tk0 + 16)
+          int rr0, rr1;
+          const int32_t b0 = row_block(e0, e0.r0 + (key - tk0), rr0);
+          const int32_t b1 = row_block(e1, e1.r0 + (key - tk0), rr1);
+          const int32_t blk = tl ? b1 : b0;
+          const int rr = tl ? rr1 : rr0;
+          const uint8_t* src = (kv ? vbase : kbase) + (int64_t)blk * a.block_bytes + (int64_t)a.block_size * D +
+                               4 * ((int64_t)rr * (PTH ? 1 : NG) + g);
+          dma4_to_lds(src, sbase + (uint32_t)(2 * KT * ROWB + 256 * c));
+        }
+      }
+    }
+    if constexpr (PTH && !GBS) {
       if (wave == WAVES - 1) {
         // 16 lanes x 16 bytes: [K scales of the 32 keys][V scales], 4 scales per lane
         const int tl = (lane >> 2) & 1, part = lane & 3, kv = lane >> 3;
         const int t0 = min(kb0, last_tile), t1 = min(kb0 + 16, last_tile);
-        const int bi0 = (int)div_invariant((uint32_t)t0, a.bs_magic, a.bs_shift);
-        const int bi1 = (int)div_invariant((uint32_t)t1, a.bs_magic, a.bs_shift);
+        const int bi0 = key_block(t0), bi1 = key_block(t1);
         int32_t b0 = bt[bi0], b1 = bt[bi1];
         if ((uint32_t)b0 >= (uint32_t)a.num_blocks) b0 = 0;
         if ((uint32_t)b1 >= (uint32_t)a.num_blocks) b1 = 0;
@@ -224,12 +296,11 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
         if (lane < 16) dma16_to_lds(src, sbase + (uint32_t)(2 * KT * ROWB));
       }
     }
-    if constexpr (PG) {
+    if constexpr (PG && !GBS) {
       if (wave == WAVES - 1) {
         // [K scales of key tile 0][K tile 1][V tile 0][V tile 1]: 16 rows x NG floats each
         const int t0 = min(kb0, last_tile), t1 = min(kb0 + 16, last_tile);
-        const int bi0 = (int)div_invariant((uint32_t)t0, a.bs_magic, a.bs_shift);
-        const int bi1 = (int)div_invariant((uint32_t)t1, a.bs_magic, a.bs_shift);
+        const int bi0 = key_block(t0), bi1 = key_block(t1);
         int32_t b0 = bt[bi0], b1 = bt[bi1];
         if ((uint32_t)b0 >= (uint32_t)a.num_blocks) b0 = 0;
         if ((uint32_t)b1 >= (uint32_t)a.num_blocks) b1 = 0;
@@ -281,12 +352,20 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   // ---- widen the V codes of one step into its V image: block t holds, for lane l, dim
   // t * 16 + l % 16 of the 8 keys of lane group kg (the A operand of O^T += V^T P^T); the step's
   // K and V scales are copied next to it, so they outlive the ring stage
-  // (ok0, ok1: the step's two 16-key tiles lie in blocks of the pool; the codes of an absent tile
-  // become zeros)
-  auto convert_v = [&](int step, bool ok0, bool ok1) {
+  // (ok0, ok1: bit t set when row t of the step's first (second) 16-key tile lies in a block of
+  // the pool; the codes of an absent row become zeros)
+  auto convert_v = [&](int step, RowMask ok0, RowMask ok1) {
     const uint8_t* kl = smem + (step % NS) * STAGE;
     uint8_t* slot = smem + VIMG + (step & 1) * VSLOT;
-    const uint32_t msk0 = ok0 ? 0xFFFFFFFFu : 0u, msk1 = ok1 ? 0xFFFFFFFFu : 0u;
+    // the lane's rows i < 4 are keys 4kg + i of the first tile, rows i >= 4 keys 4kg + i - 4 of
+    // the second: one byte per row (codes), or a whole mask per row (16-bit elements)
+    const uint32_t b0 = ((uint32_t)ok0 >> (4 * kg)) & 0xFu, b1 = ((uint32_t)ok1 >> (4 * kg)) & 0xFu;
+    auto bytes = [](uint32_t b) {
+      return ((b & 1u) ? 0xFFu : 0u) | ((b & 2u) ? 0xFF00u : 0u) | ((b & 4u) ? 0xFF0000u : 0u) | ((b & 8u) ? 0xFF000000u : 0u);
+    };
+    const uint32_t msk0 = GBS ? bytes(b0) : (ok0 ? 0xFFFFFFFFu : 0u), msk1 = GBS ? bytes(b1) : (ok1 ? 0xFFFFFFFFu : 0u);
+    // row i of the lane present in its block (without GBS a tile's rows share one block)
+    auto present_row = [&](int i) { return GBS ? (((i < 4 ? b0 : b1) >> (i & 3)) & 1) != 0 : (bool)(i < 4 ? ok0 : ok1); };
     if constexpr (EB == 1) {
       const uint8_t* rp = kl + KT * ROWB + tr_row * ROWB + (r16 & 1) * 8;
 #pragma unroll
@@ -304,7 +383,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int row = i < 4 ? 4 * kg + i : 16 + 4 * kg + i - 4;
-            const bool present = k_begin + step * KT + row < it.L && (i < 4 ? ok0 : ok1);
+            const bool present = k_begin + step * KT + row < it.L && present_row(i);
             const float sc = present ? vsc[row * NG + (t >> 1)] : 0.0f;
             r[i] = (__bf16)((float)e[i] * sc);
           }
@@ -323,7 +402,8 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int row = i < 4 ? 4 * kg + i : 16 + 4 * kg + i - 4;
-          e[i] = *(const uint16_t*)(vl + row * ROWB + (((2 * t + (r16 >> 3)) ^ swz<ROWB>(row)) << 4)) & (i < 4 ? msk0 : msk1);
+          e[i] = *(const uint16_t*)(vl + row * ROWB + (((2 * t + (r16 >> 3)) ^ swz<ROWB>(row)) << 4)) &
+                 (GBS ? (present_row(i) ? 0xFFFFu : 0u) : (i < 4 ? msk0 : msk1));
         }
         *(uint4*)(slot + t * 1024 + lane * 16) =
             make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
@@ -393,18 +473,18 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
     __syncthreads();  // stages 0 and 1 landed for every wave
     convert_k(0);
     convert_k(1);
-    convert_v(0, tile_ok(k_begin), tile_ok(k_begin + kTileKeys));
+    convert_v(0, tile_rows(k_begin), tile_rows(k_begin + kTileKeys));
     __syncthreads();
     bf16x8 kw[2][QS];
     read_k(0, kw);
     qk_half(0, kw, s_cur, 0);
     qk_half(1, kw, s_cur, 0);
   }
-  bool cur_ok0 = n_steps > 0 && tile_ok(k_begin), cur_ok1 = n_steps > 0 && tile_ok(k_begin + kTileKeys);
+  RowMask cur_ok0 = n_steps > 0 ? tile_rows(k_begin) : RowMask(0), cur_ok1 = n_steps > 0 ? tile_rows(k_begin + kTileKeys) : RowMask(0);
   for (int step = 0; step < n_steps; ++step) {
     // validity of the next step's tiles (its V codes are widened in this iteration; its keys are
     // masked in the next)
-    const bool nxt_ok0 = tile_ok(k_begin + (step + 1) * KT), nxt_ok1 = tile_ok(k_begin + (step + 1) * KT + kTileKeys);
+    const RowMask nxt_ok0 = tile_rows(k_begin + (step + 1) * KT), nxt_ok1 = tile_rows(k_begin + (step + 1) * KT + kTileKeys);
     // stage step + 2 landed once only the copies of later stages are outstanding
     const int issued = min(n_steps, step + NS);
     // (issued - step - 3 is 1, or 0 at the last steps: compile-time counts, no runtime switch)
@@ -453,14 +533,17 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
         for (int e = 0; e < 8; ++e) x[rt][e] += slope_r[rt] * (float)(base + (e >> 2) * 16 + (e & 3));
       }
     }
-    const bool full = wave_rows_full && kb0 >= vis_lo && kb0 + KT <= vis_hi && kb0 + KT <= it.L && cur_ok0 && cur_ok1;
+    const bool full = wave_rows_full && kb0 >= vis_lo && kb0 + KT <= vis_hi && kb0 + KT <= it.L &&
+                      (GBS ? ((uint32_t)cur_ok0 & (uint32_t)cur_ok1) == 0xFFFFu : (cur_ok0 && cur_ok1));
     if (!full) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = kb0 + (e >> 2) * 16 + 4 * kg + (e & 3);
-          if (!(j >= lo_r[rt] && j < hi_r[rt] && ((e >> 2) == 0 ? cur_ok0 : cur_ok1))) x[rt][e] = -INFINITY;
+          const RowMask okm = (e >> 2) == 0 ? cur_ok0 : cur_ok1;
+          const bool present = GBS ? (((uint32_t)okm >> (4 * kg + (e & 3))) & 1) != 0 : (bool)okm;
+          if (!(j >= lo_r[rt] && j < hi_r[rt] && present)) x[rt][e] = -INFINITY;
         }
     }
 
@@ -603,6 +686,7 @@ static int launch_pf(const AttnArgs& a, hipStream_t st) {
   p.block_bytes = a.block_bytes;
   p.block_size = a.block_size;
   invariant_divisor((uint32_t)a.block_size, &p.bs_magic, &p.bs_shift);
+  p.inv_bs = 1.0f / (float)a.block_size;
   p.num_kv_heads = a.num_kv_heads;
   p.num_q_heads = a.num_q_heads;
   p.group = a.group;
@@ -616,24 +700,33 @@ static int launch_pf(const AttnArgs& a, hipStream_t st) {
   p.alibi = a.alibi_slopes;
   p.sinks = a.sinks;
   const dim3 grid(h.num_pf_items), block(pf_waves(D) * 64);
+  const bool gbs = a.block_size % kTileKeys != 0;  // tiles may span blocks
+#define AQP_PF_GO(CAPV, ROWSV)                                                                                    \
+  if (gbs)                                                                                                        \
+    hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, CAPV, ROWSV, true>), grid, block, h.pf_lds_bytes, st, p);  \
+  else                                                                                                            \
+    hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, CAPV, ROWSV, false>), grid, block, h.pf_lds_bytes, st, p);
   if (h.pf_rows == kPfRows) {
-    if (a.softcap > 0.0f)
-      hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, true, kPfRows>), grid, block, h.pf_lds_bytes, st, p);
-    else
-      hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, false, kPfRows>), grid, block, h.pf_lds_bytes, st, p);
+    if (a.softcap > 0.0f) {
+      AQP_PF_GO(true, kPfRows)
+    } else {
+      AQP_PF_GO(false, kPfRows)
+    }
   } else if constexpr (pf_waves(D) * 16 <= kPfRowsSmall) {
     if (h.pf_rows != kPfRowsSmall) {
       set_error("aqp_paged_attention: schedule rows per prefill item %d not built", h.pf_rows);
       return AQP_ERR_SCHEDULE_MISMATCH;
     }
-    if (a.softcap > 0.0f)
-      hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, true, kPfRowsSmall>), grid, block, h.pf_lds_bytes, st, p);
-    else
-      hipLaunchKernelGGL((prefill_kernel<D, DT, MODE, false, kPfRowsSmall>), grid, block, h.pf_lds_bytes, st, p);
+    if (a.softcap > 0.0f) {
+      AQP_PF_GO(true, kPfRowsSmall)
+    } else {
+      AQP_PF_GO(false, kPfRowsSmall)
+    }
   } else {
     set_error("aqp_paged_attention: schedule rows per prefill item %d not built at head_dim %d", h.pf_rows, D);
     return AQP_ERR_SCHEDULE_MISMATCH;
   }
+#undef AQP_PF_GO
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("aqp_paged_attention: prefill launch failed: %s", hipGetErrorString(e));

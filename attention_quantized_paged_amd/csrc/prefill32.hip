@@ -109,11 +109,6 @@ __device__ __forceinline__ T& pick(T& a, T& b) {
   else return b;
 }
 
-// Copy 4 bytes per lane from global memory into LDS: lane l's word at p lands at LDS byte lds + 4 l.
-__device__ __forceinline__ void dma4_to_lds(const void* p, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(p) : "memory");
-}
-
 template <int D, int DT, int MODE, bool CAP, bool ALIBI, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(pf32_waves_per_simd(D))))
 void prefill32_kernel(Pf32Args a) {

@@ -84,7 +84,8 @@ typedef enum {
  *  - page_bytes is that content rounded up to a multiple of 128 bytes;
  *  - slot s is row (s % block_size) of block (s / block_size).
  * Supported: head_dim in {64, 128, 256} (every dtype and mode);
- * block_size a positive multiple of 16. */
+ * block_size from 1 to 65536 (a multiple of 16 keeps each 16-key tile in one
+ * page; other sizes are gathered row by row). */
 typedef struct {
   int32_t num_blocks;
   int32_t block_size;

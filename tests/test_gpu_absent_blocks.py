@@ -6,7 +6,8 @@ pool (an absent tile is read from block 0 and masked), so these cases cannot fau
 Covered: decode, with an absent entry past a decode wave's 64th tile (one work-group per
 sequence, so each of its four waves walks more than 64 tiles) and split ranges whose every key
 is absent; prefill at head_dim 128 and 256, per-tensor and per-token-head codes, with key splits;
-a cache whose unwritten bytes are NaN codes."""
+block sizes that are not a multiple of 16 (absent rows inside a tile); a cache whose unwritten
+bytes are NaN codes."""
 import numpy as np
 import pytest
 
@@ -69,7 +70,24 @@ PREFILL = [
                16, 50, seed=204),
     W.Workload("absent_prefill_d256_e4m3", "fp8_e4m3", ((200, 200), (33, 150)), 16, 2, 256, 32, 16, seed=205),
     W.Workload("absent_prefill_d64_pg", "fp8_per_group", ((120, 120), (20, 64)), 8, 2, 64, 16, 16, seed=206),
+    # block sizes that are not a multiple of 16: an absent block masks some rows of a tile only
+    W.Workload("absent_prefill_bs8_d128_pth", "fp8_per_token_head", ((300, 300), (40, 200), (1, 90)), 16, 4, 128, 8,
+               100, seed=207),
+    W.Workload("absent_prefill_bs3_d64_pg", "int8_per_group", ((120, 120), (20, 64)), 8, 2, 64, 3, 70, seed=208),
 ]
+
+
+@pytest.mark.parametrize("par", [0, 9])
+def test_decode_absent_blocks_odd_block_size(aqp, par):
+    w = W.Workload("absent_decode_bs5_pth", "int8_per_token_head", ((1, 900), (1, 50), (1, 333)), 16, 4, 128, 5, 300,
+                   window=400, seed=209)
+    r = Run(w, torch, aqp, par=par, fill=0xFF)
+    # single 5-key blocks inside tiles, the second sequence's every block
+    _absent(r, [(0, 3), (0, 100), (0, 179), (2, 0), (2, 66)] + [(1, j) for j in range(10)])
+    out = r.gpu_attention()
+    ref, rows = r.oracle_attention()
+    assert np.all(ref[1] == 0), "a sequence with no key left outputs zeros"
+    compare(out[rows], ref, f"{w.name} par={par}")
 
 
 @pytest.mark.parametrize("split", [1, 3])

@@ -70,6 +70,23 @@ SMALL = [
     W.Workload("auto_d256_prefill_bs2176", "auto", ((300, 300), (37, 37), (5, 80)), 16, 2, 256, 2176, 3, seed=232),
     W.Workload("auto_d256_mixed_g16_w_cap", "auto", ((1, 900), (40, 200), (1, 31), (17, 17)), 32, 2, 256, 32, 60,
                window=150, softcap=20.0, seed=233),
+    # block sizes that are not a multiple of 16: a 16-key tile spans up to 16 blocks (block 1) or
+    # two (24, 40, 2200); every scale mode, head_dim and the unquantised cache; decode, prefill
+    # and mixed batches with window and soft-cap
+    W.Workload("bs1_decode_e4m3_pt_d128", "fp8_e4m3", ((1, 300), (1, 17), (1, 1000), (1, 1)), 8, 2, 128, 1, 1400,
+               seed=241),
+    W.Workload("bs8_mixed_int8_pth_d64", "int8_per_token_head", ((1, 500), (40, 200), (1, 9)), 8, 2, 64, 8, 100,
+               seed=242),
+    W.Workload("bs24_prefill_e4m3_pt_d128_w_cap", "fp8_e4m3", ((70, 70), (9, 130), (1, 48)), 16, 2, 128, 24, 16,
+               window=50, softcap=10.0, seed=243),
+    W.Workload("bs40_mixed_pg_e5m2_d256", "fp8_e5m2_per_group", ((1, 700), (1, 41), (5, 90)), 16, 2, 256, 40, 30,
+               seed=244),
+    W.Workload("bs3_auto_mixed_d128", "auto", ((1, 200), (20, 60), (1, 5)), 8, 2, 128, 3, 100, seed=245),
+    W.Workload("bs5_prefill_e4m3_pth_d256", "fp8_per_token_head", ((37, 37), (1, 100)), 16, 2, 256, 5, 40,
+               softcap=8.0, seed=246),
+    W.Workload("bs1_mixed_pg_int8_d64", "int8_per_group", ((1, 64), (17, 17), (1, 33)), 8, 2, 64, 1, 130, seed=247),
+    W.Workload("bs2200_mixed_e4m3_d256", "fp8_e4m3", ((1, 5000), (30, 30)), 16, 2, 256, 2200, 6, seed=248),
+    W.Workload("bs7_auto_d256_prefill", "auto", ((50, 50), (3, 70)), 16, 2, 256, 7, 24, seed=249),
     # per-group scales (one per 32 head-dim channels): every codec and head_dim, decode (split and
     # whole), prefill (64- and 128-row items) and mixed batches, window and soft-cap
     W.scaled(W.CFG3, name="pg_e4m3_decode_llama8b", kv_dtype="fp8_per_group",
@@ -373,7 +390,7 @@ def _random_workload(seed):
               "fp8_e5m2_per_token_head", "int8_per_group", "fp8_per_group", "fp8_e5m2_per_group", "auto"]
     dt = dtypes[seed % len(dtypes)]
     d = int(rng.choice([64, 128, 256]))
-    bs = int(rng.choice([16, 32, 64]))
+    bs = int(rng.choice([16, 32, 64, 1, 8, 24]))
     hkv = int(rng.integers(1, 4))
     g = int(rng.choice([1, 2, 4, 6, 8, 16]))
     seqs = []

@@ -72,7 +72,8 @@ FMT = {aqp.KV_AUTO: oracle.FMT_BF16, aqp.KV_FP8_E4M3: oracle.FMT_E4M3, aqp.KV_FP
 @pytest.mark.parametrize("dtype_str", ["fp8_e4m3", "fp8_e5m2", "int8_per_token_head", "fp8_per_token_head", "int8",
                                        "fp8_e5m2_per_token_head", "auto", "int8_per_group", "fp8_per_group",
                                        "fp8_e5m2_per_group"])
-@pytest.mark.parametrize("nb,bs,h,d", [(8, 16, 2, 64), (4, 2176, 2, 256), (40000, 16, 8, 128), (3, 32, 3, 128)])
+@pytest.mark.parametrize("nb,bs,h,d", [(8, 16, 2, 64), (4, 2176, 2, 256), (40000, 16, 8, 128), (3, 32, 3, 128),
+                                      (50, 1, 2, 64), (7, 24, 3, 256), (5, 2200, 2, 128)])
 def test_cache_bytes_match_oracle_layout(dtype_str, nb, bs, h, d):
     desc = aqp.cache_desc(nb, bs, h, d, dtype_str)
     pb, bb, tb = aqp.cache_bytes(desc)
@@ -80,7 +81,7 @@ def test_cache_bytes_match_oracle_layout(dtype_str, nb, bs, h, d):
     assert (pb, bb, tb) == (od.page_bytes, od.block_bytes, od.total_bytes)
 
 
-@pytest.mark.parametrize("bad", [dict(head_dim=96), dict(block_size=8), dict(block_size=1), dict(num_kv_heads=0)])
+@pytest.mark.parametrize("bad", [dict(head_dim=96), dict(block_size=0), dict(block_size=65537), dict(num_kv_heads=0)])
 def test_unsupported_geometry(bad):
     kw = dict(num_blocks=4, block_size=16, num_kv_heads=2, head_dim=64)
     kw.update(bad)
@@ -88,6 +89,39 @@ def test_unsupported_geometry(bad):
     with pytest.raises(aqp.AqpError) as e:
         aqp.cache_bytes(desc)
     assert e.value.status in (aqp.ERR_UNSUPPORTED, aqp.ERR_INVALID)
+
+
+@pytest.mark.parametrize("bs", [1, 3, 8, 24, 40, 2200])
+@pytest.mark.parametrize("dtype", ["fp8_e4m3", "int8_per_token_head", "fp8_per_group", "auto"])
+def test_any_block_size_geometry(bs, dtype):
+    """Block sizes that are not a multiple of 16 are accepted: a page holds block_size rows and
+    their scales, rounded up to 128 bytes, as the oracle lays it out; the schedule is built and
+    routes prefill work to the 16x16 kernel (the one that gathers tiles spanning blocks)."""
+    desc = aqp.cache_desc(64, bs, 2, 128, dtype)
+    pb, bb, tb = aqp.cache_bytes(desc)
+    od = oracle.CacheDesc(64, bs, 2, 128, FMT[desc.dtype], desc.mode)
+    assert (pb, bb, tb) == (od.page_bytes, od.block_bytes, od.total_bytes)
+    L = min(64 * bs // 4, 300)
+    sl, qsl = np.array([L, 1], np.int32), np.array([0, L, L + 1], np.int32)
+    h = aqp.get_schedule(aqp.attn_params(8, 2, 128, -(-L // bs)), desc, sl, qsl).header
+    assert h["block_size"] == bs and h["num_pf_items"] > 0
+    # the 16x16 kernel's LDS (ring of four steps + four images + two scale slots), not the 32x32 one's
+    eb = 2 if dtype == "auto" else 1
+    sc = 0 if eb == 2 else 2 * 32 * 4 * (4 if dtype == "fp8_per_group" else 1)
+    assert h["pf_lds_bytes"] == 4 * (2 * 32 * 128 * eb + sc) + 4 * 32 * 128 * 2 + (0 if eb == 2 else 2 * 2 * 32 * 4)
+
+
+def test_row_quotient_is_exact():
+    """The kernels split a 16-key tile that spans blocks with the quotient n / block_size taken as
+    trunc((n + 1/2) * fl(1 / block_size)) in fp32 (n < block_size + 128): exact for every block
+    size up to the library's limit (checked here in the same fp32 arithmetic, all n, all sizes
+    up to 4096 and a spread of larger ones)."""
+    sizes = np.concatenate([np.arange(1, 4097), np.unique(np.geomspace(4097, 65536, 3000).astype(np.int64)), [65536]])
+    for bs in sizes:
+        n = np.arange(0, int(bs) + 128, dtype=np.int64)
+        rd = np.float32(1.0) / np.float32(bs)
+        q = ((n.astype(np.float32) + np.float32(0.5)) * rd).astype(np.int64)
+        assert np.array_equal(q, n // bs), bs
 
 
 @pytest.mark.parametrize("dt,md", [(aqp.KV_AUTO, 1), (aqp.KV_AUTO, 2)])

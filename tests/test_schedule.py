@@ -49,6 +49,10 @@ CASES = [
     (workloads.CFG5A.seqs, 64, 8, 128, 16, 4096, 0),
     (workloads.CFG2.seqs, 16, 2, 256, 2176, 0, 0),
     (((3, 40), (70, 70), (1, 90)), 192, 1, 64, 16, 0, 0),  # G = 192 > 128: prefill items split the heads
+    # block sizes that are not a multiple of 16 (tiles span blocks; the schedule works in keys)
+    (((1, 300), (1, 17), (40, 200), (1, 1)), 8, 2, 128, 1, 0, 0),
+    (((1, 1000), (33, 90), (1, 16)), 16, 2, 64, 24, 200, 5),
+    (((1, 5000), (30, 30)), 16, 2, 256, 2200, 0, 0),
 ]
 
 
@@ -464,7 +468,7 @@ from hypothesis import given, settings, strategies as st  # noqa: E402
 @st.composite
 def _batches(draw):
     d = draw(st.sampled_from([64, 128, 256]))
-    bs = draw(st.sampled_from([16, 32, 48, 2176] if d == 256 else [16, 32, 48, 64]))
+    bs = draw(st.sampled_from([16, 32, 48, 2176, 5, 24, 2200] if d == 256 else [16, 32, 48, 64, 1, 3, 8, 24]))
     hkv = draw(st.integers(1, 4))
     g = draw(st.sampled_from([1, 2, 3, 4, 8, 16, 24, 40]))
     n = draw(st.integers(1, 6))
