@@ -60,10 +60,12 @@ def _load() -> ctypes.CDLL:
                                         f32, P, sz, P, P]
     lib.aqp_paged_attention_noalloc.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(CacheDesc), P, P, P, P,
                                                 P, f32, f32, P, P]
+    lib.aqp_paged_attention_timed.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(CacheDesc), P, P, P, P, P,
+                                              f32, f32, P, sz, P, P, ctypes.POINTER(P), i32]
     lib.aqp_last_error.argtypes = []
     lib.aqp_last_error.restype = ctypes.c_char_p
     for fn in ("aqp_parse_kv_dtype", "aqp_cache_bytes", "aqp_cache_write", "aqp_get_schedule", "aqp_paged_attention",
-               "aqp_paged_attention_noalloc"):
+               "aqp_paged_attention_noalloc", "aqp_paged_attention_timed"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -264,7 +266,10 @@ def get_schedule(params: AttnParams, desc: CacheDesc, seq_lens, query_start_loc,
 
 
 def paged_attention(params: AttnParams, desc: CacheDesc, cache, q, block_tables, meta_host, meta_dev,
-                    k_scale: float, v_scale: float, scratch, scratch_bytes: int, out, stream=None) -> None:
+                    k_scale: float, v_scale: float, scratch, scratch_bytes: int, out, stream=None,
+                    events=None) -> None:
+    """With ``events`` (up to 6 hipEvent_t handles) the call goes through aqp_paged_attention_timed,
+    which records them around each of its kernels on the call's stream."""
     for t, nm in ((cache, "cache"), (q, "q"), (block_tables, "block_tables"), (meta_dev, "meta_dev"), (out, "out")):
         _dev_ok(t, nm)
     if isinstance(meta_host, np.ndarray) and meta_host.nbytes >= 256:
@@ -279,9 +284,17 @@ def paged_attention(params: AttnParams, desc: CacheDesc, cache, q, block_tables,
             _need(meta_dev, h["meta_bytes"], "meta_dev")
             _need(cache, cache_bytes(desc)[2], "cache")
             _need(scratch, int(scratch_bytes), "scratch")
-    _check(_lib.aqp_paged_attention(ctypes.byref(params), ctypes.byref(desc), _ptr(cache), _ptr(q),
-                                    _ptr(block_tables), _ptr(meta_host), _ptr(meta_dev), float(k_scale),
-                                    float(v_scale), _ptr(scratch), int(scratch_bytes), _ptr(out), _stream(stream)))
+    if events is None:
+        _check(_lib.aqp_paged_attention(ctypes.byref(params), ctypes.byref(desc), _ptr(cache), _ptr(q),
+                                        _ptr(block_tables), _ptr(meta_host), _ptr(meta_dev), float(k_scale),
+                                        float(v_scale), _ptr(scratch), int(scratch_bytes), _ptr(out), _stream(stream)))
+        return
+    # events: up to 6 raw hipEvent_t handles (ints, or None to skip a point)
+    ev = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(int(e)) if e else None for e in events])
+    _check(_lib.aqp_paged_attention_timed(ctypes.byref(params), ctypes.byref(desc), _ptr(cache), _ptr(q),
+                                          _ptr(block_tables), _ptr(meta_host), _ptr(meta_dev), float(k_scale),
+                                          float(v_scale), _ptr(scratch), int(scratch_bytes), _ptr(out),
+                                          _stream(stream), ev, len(events)))
 
 
 # scratch bytes of the library's own buffer behind paged_attention_noalloc

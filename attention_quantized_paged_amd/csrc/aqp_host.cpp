@@ -605,7 +605,8 @@ namespace aqp {
 // The attention call on a given work buffer (`work`, `work_bytes` bytes).
 static int attention(const aqp_attn_params* params, const aqp_cache_desc* desc, const void* cache, const void* q,
                      const int32_t* block_tables, const void* meta_host, const void* meta_dev, float k_scale,
-                     float v_scale, void* work, size_t work_bytes, void* out, void* stream) {
+                     float v_scale, void* work, size_t work_bytes, void* out, void* stream,
+                     void* const* events = nullptr, int32_t num_events = 0) {
   if (!params || !desc || !meta_host) return fail(AQP_ERR_INVALID, "aqp_paged_attention: null argument");
   Geometry g;
   const char* why = "";
@@ -663,29 +664,28 @@ static int attention(const aqp_attn_params* params, const aqp_cache_desc* desc, 
   a.hdr = &h;
   // decode, then the merge of its split ranges; the prefill runs' merge follows the prefill
   const int32_t n_dec_comb = (int32_t)h.num_dec_comb, n_pf_comb = h.num_comb - n_dec_comb;
-  auto run_decode = [&](void* st) -> int {
-    int r = launch_decode(desc->dtype, desc->mode, a, st);
-    if (r == AQP_OK && n_dec_comb > 0) r = launch_combine(a, 0, n_dec_comb, st);
-    return r;
+  auto launch_prefill_kernel = [&](void* st) -> int {
+    return pf32_applies(desc->dtype, desc->mode, desc->head_dim, desc->block_size) ? launch_prefill32(desc->dtype, desc->mode, a, st)
+                                                                                    : launch_prefill(desc->dtype, desc->mode, a, st);
   };
-  auto run_prefill = [&](void* st) -> int {
-    int r = pf32_applies(desc->dtype, desc->mode, desc->head_dim, desc->block_size) ? launch_prefill32(desc->dtype, desc->mode, a, st)
-                                                  : launch_prefill(desc->dtype, desc->mode, a, st);
-    if (r == AQP_OK && n_pf_comb > 0) r = launch_combine(a, n_dec_comb, n_pf_comb, st);
-    return r;
+  // timing marks (aqp_paged_attention_timed): event i recorded on `stream` at point i
+  auto mark = [&](int i) -> int {
+    if (i >= num_events || !events || !events[i]) return AQP_OK;
+    const hipError_t e = hipEventRecord((hipEvent_t)events[i], (hipStream_t)stream);
+    return e == hipSuccess ? AQP_OK : fail(AQP_ERR_HIP, "aqp_paged_attention_timed: event %d: %s", i, hipGetErrorString(e));
   };
   // A mixed batch runs its decode and then its prefill on `stream`: the two kernels each fill the
   // device, and measured one after the other they finish sooner than side by side on two streams
   // (each takes the other's CUs and LDS).
-  if (h.num_dec_segs > 0) {
-    rc = run_decode(stream);
-    if (rc) return rc;
-  }
-  if (h.num_pf_items > 0) {
-    rc = run_prefill(stream);
-    if (rc) return rc;
-  }
-  return AQP_OK;
+  if ((rc = mark(0))) return rc;
+  if (h.num_dec_segs > 0 && (rc = launch_decode(desc->dtype, desc->mode, a, stream))) return rc;
+  if ((rc = mark(1))) return rc;
+  if (h.num_dec_segs > 0 && n_dec_comb > 0 && (rc = launch_combine(a, 0, n_dec_comb, stream))) return rc;
+  if ((rc = mark(2)) || (rc = mark(3))) return rc;
+  if (h.num_pf_items > 0 && (rc = launch_prefill_kernel(stream))) return rc;
+  if ((rc = mark(4))) return rc;
+  if (h.num_pf_items > 0 && n_pf_comb > 0 && (rc = launch_combine(a, n_dec_comb, n_pf_comb, stream))) return rc;
+  return mark(5);
 }
 
 // Scratch of the allocation-free call: a file-scope device array, one per GPU the library runs on,
@@ -728,6 +728,16 @@ extern "C" int aqp_paged_attention(const aqp_attn_params* params, const aqp_cach
                                    size_t scratch_bytes, void* out, void* stream) {
   return attention(params, desc, cache, q, block_tables, meta_host, meta_dev, k_scale, v_scale, scratch_buf,
                    scratch_bytes, out, stream);
+}
+
+extern "C" int aqp_paged_attention_timed(const aqp_attn_params* params, const aqp_cache_desc* desc, const void* cache,
+                                         const void* q, const int32_t* block_tables, const void* meta_host,
+                                         const void* meta_dev, float k_scale, float v_scale, void* scratch_buf,
+                                         size_t scratch_bytes, void* out, void* stream, void* const* events,
+                                         int32_t num_events) {
+  if (num_events < 0 || (num_events > 0 && !events)) return fail(AQP_ERR_INVALID, "aqp_paged_attention_timed: bad event list");
+  return attention(params, desc, cache, q, block_tables, meta_host, meta_dev, k_scale, v_scale, scratch_buf,
+                   scratch_bytes, out, stream, events, std::min<int32_t>(num_events, 6));
 }
 
 extern "C" int aqp_paged_attention_noalloc(const aqp_attn_params* params, const aqp_cache_desc* desc,

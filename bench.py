@@ -151,12 +151,11 @@ def decode_step(torch, aqp, s, ev=None):
         s["meta_dev"][slot][:n].copy_(s["meta_pinned"][slot][:n], non_blocking=True)
         s["copied"][slot].record(cs)
     main.wait_event(s["copied"][slot])
-    if ev is not None:
-        ev[0].record(main)
+    # ev: HIP events the library records on the launch stream before the decode kernel, after it,
+    # and after the merge of its split ranges
     aqp.paged_attention(s["params"], s["desc"], s["cache"], s["q"], s["bt"], sch.meta, s["meta_dev"][slot],
-                        b.k_scale, b.v_scale, s["scratch"], s["scratch"].numel(), s["out"], stream=st)
-    if ev is not None:
-        ev[1].record(main)
+                        b.k_scale, b.v_scale, s["scratch"], s["scratch"].numel(), s["out"], stream=st,
+                        events=None if ev is None else [int(e.cuda_event) for e in ev])
     s["consumed"][slot].record(main)
     s["used"][slot] = True
     return sch
@@ -767,18 +766,25 @@ def main():
         sch = decode_step(torch, aqp, s)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    # kernel time: the same steps again, each attention launch bracketed by HIP events on the
-    # stream it runs on (timing events serialise the stream, so they stay out of the step timing)
+    # kernel time: the same steps again, the library recording HIP events on the launch stream
+    # right before the decode kernel, right after it and after the split-KV merge (timing events
+    # serialise the stream, so they stay out of the step timing)
     log(args, f"[bench] timing {args.steps} attention launches")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for ev in evs:
+        for e in ev:
+            e.record()  # (creates the event, so that its handle exists)
+    torch.cuda.synchronize()
     for i in range(args.steps):
         decode_step(torch, aqp, s, evs[i])
     torch.cuda.synchronize()
-    attn_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    dec_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in evs]))
+    merge_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in evs]))
+    attn_ms = float(np.mean([e0.elapsed_time(e2) for e0, _, e2 in evs]))
     ms_per_step = elapsed / args.steps * 1e3
     value = kv_bytes * args.steps / elapsed / 1e9
     h = sch.header
-    achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
+    achieved = kv_bytes / (dec_ms * 1e-3) / 1e9
     result = {
         "metric": "decode KV-read HBM GB/s (% of peak) + prefill TFLOP/s, paged attn over fp8/int8 KV",
         "value": round(value, 2),
@@ -801,8 +807,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(kv_bytes),
-                     "kernel": "decode_kernel + split-KV merge (one attention launch)",
-                     "launch_ms": round(attn_ms, 4), "decode_workgroups": h["num_dec_wgs"],
+                     "kernel": "decode_kernel",
+                     "kernel_ms": round(dec_ms, 4), "merge_ms": round(merge_ms, 4),
+                     "launch_ms": round(attn_ms, 4),
+                     "launch_frac": round(kv_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "decode_workgroups": h["num_dec_wgs"],
                      "partials": h["num_parts"]},
     }
     result.update(extra)

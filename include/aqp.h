@@ -235,6 +235,21 @@ int aqp_paged_attention(const aqp_attn_params* params, const aqp_cache_desc* des
                         const void* q, const int32_t* block_tables, const void* meta_host, const void* meta_dev,
                         float k_scale, float v_scale, void* scratch, size_t scratch_bytes, void* out, void* stream);
 
+/* aqp_paged_attention for callers that time its kernels one by one (benchmarks, profilers that
+ * read HIP events): identical work and results, and events[i] (hipEvent_t, or NULL to skip) is
+ * recorded on `stream` at point i of the call: 0 before the decode kernel, 1 after it, 2 after the
+ * merge of its split ranges, 3 before the prefill kernel, 4 after it, 5 after the merge of its
+ * split runs. A part the batch does not have leaves its two points back to back. num_events: how
+ * many entries `events` holds (0 to 6; more are ignored). The events belong to the caller and must
+ * have been created on the stream's device. No event is recorded for a batch without query tokens
+ * or when the call fails before its first launch.
+ * Errors: those of aqp_paged_attention; INVALID for num_events < 0 or a null list with
+ * num_events > 0; HIP when an event cannot be recorded. */
+int aqp_paged_attention_timed(const aqp_attn_params* params, const aqp_cache_desc* desc, const void* cache,
+                              const void* q, const int32_t* block_tables, const void* meta_host, const void* meta_dev,
+                              float k_scale, float v_scale, void* scratch, size_t scratch_bytes, void* out,
+                              void* stream, void* const* events, int32_t num_events);
+
 /* aqp_paged_attention without a scratch argument, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * partial results of split ranges go to a fixed 64 MiB device array of the library (one per GPU

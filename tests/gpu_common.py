@@ -113,8 +113,9 @@ class Run:
         bad = np.nonzero(g != self.ocache)[0]
         assert bad.size == 0, f"{bad.size} cache bytes differ, first at {bad[:8]}"
 
-    def gpu_attention(self, calls=1):
-        """Output of the last of `calls` attention calls that reuse one device copy of the schedule."""
+    def gpu_attention(self, calls=1, events=None):
+        """Output of the last of `calls` attention calls that reuse one device copy of the schedule
+        (with `events`, hipEvent_t handles, through the timed entry point)."""
         torch, aqp, b = self.torch, self.aqp, self.b
         sch = aqp.get_schedule(self.params, self.desc, b.seq_lens, b.query_start_loc)
         meta_dev = torch.from_numpy(sch.meta).cuda()
@@ -125,7 +126,7 @@ class Run:
         for _ in range(calls):
             out = torch.full(q.shape, -1, dtype=torch.int16, device="cuda")  # NaN pattern: every row must be written
             aqp.paged_attention(self.params, self.desc, self.gcache, q, bt, sch.meta, meta_dev, b.k_scale, b.v_scale,
-                                scratch, sch.scratch_bytes, out)
+                                scratch, sch.scratch_bytes, out, events=events)
             self.outs.append(out)
         torch.cuda.synchronize()
         self.sched = sch

@@ -237,6 +237,28 @@ def test_reused_schedule_copy_gives_identical_results(aqp):
     compare(last[rows], ref, w.name)
 
 
+def test_timed_call_matches_and_records_its_events_in_order(aqp):
+    """aqp_paged_attention_timed gives the output of aqp_paged_attention bit for bit and records its
+    six events in order: around the decode kernel, its merge, the prefill kernel and its merge (a
+    mixed batch with split decode ranges and split prefill runs)."""
+    w = W.scaled(W.CFG4, name="timed_mixed", seqs=((1, 600), (1, 257), (70, 310)), num_blocks=120)
+    r = Run(w, torch, aqp, par=7, prefill_kv_split=2)
+    plain = r.gpu_attention()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in ev:
+        e.record()  # (creates the event)
+    torch.cuda.synchronize()
+    timed = r.gpu_attention(events=[int(e.cuda_event) for e in ev])
+    assert np.array_equal(plain, timed)
+    t = [ev[0].elapsed_time(e) for e in ev]
+    say(f"  event times (ms): {[round(x, 4) for x in t]}")
+    assert all(t[i] <= t[i + 1] + 1e-3 for i in range(5)), t
+    assert t[1] > 0 and t[4] > t[3], t
+    # a partial list: only the decode kernel's two points
+    timed2 = r.gpu_attention(events=[int(ev[0].cuda_event), int(ev[1].cuda_event)])
+    assert np.array_equal(plain, timed2) and ev[0].elapsed_time(ev[1]) > 0
+
+
 GUARDED = [
     # the large-prefill shape the scratch-sizing page's regression test uses (block 2176, head_dim
     # 256), shortened so the oracle stays fast; a split decode; a mixed per-token-head batch

@@ -181,6 +181,15 @@ def test_unquantised_cache_geometry_and_limits():
     assert h4["group_heads"] == 4
 
 
+def test_timed_call_refuses_a_bad_event_list():
+    """The timed entry point checks its event list before anything else."""
+    f = aqp._lib.aqp_paged_attention_timed
+    args = (None, None, None, None, None, None, None, 1.0, 1.0, None, 0, None, None)
+    assert f(*args, None, 2) == aqp.ERR_INVALID
+    assert f(*args, None, -1) == aqp.ERR_INVALID
+    assert b"event list" in aqp._lib.aqp_last_error()
+
+
 def test_binding_refuses_mis_sized_buffers():
     """The binding checks every buffer's extent against what the kernels will touch (the C ABI
     takes raw pointers and cannot): too-small q, out, block tables, device schedule, scratch,
