@@ -260,11 +260,17 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
   int32_t is_blk = 0;              // block-table entry of the next tile (read one tile ahead)
   int32_t is_ent[16] = {};         // GBS: entries of the 16 blocks from the next tile's first
   uint64_t ok_rows = 0;            // GBS: bits 16 (n & 3) ..: rows of tile n in blocks of the pool
-  // the next tile's block-table entries (scalar loads; clamped to the sequence's table row)
+  // the next tile's block-table entries (scalar loads; clamped to the sequence's table row); with
+  // GBS and block_size >= 16 a tile spans at most two blocks, so two entries do
   auto fetch_blk = [&]() {
     if constexpr (GBS) {
+      if (a.block_size >= kTileKeys) {
+        is_ent[0] = is_bt[is_p.bi];
+        is_ent[1] = is_bt[min(is_p.bi + 1, a.max_blocks - 1)];
+      } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) is_ent[j] = is_bt[min(is_p.bi + j, a.max_blocks - 1)];
+        for (int j = 0; j < 16; ++j) is_ent[j] = is_bt[min(is_p.bi + j, a.max_blocks - 1)];
+      }
     } else {
       is_blk = is_bt[is_p.bi];
     }
@@ -294,9 +300,16 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
   // pool masks its rows (block 0 is read in their place).
   auto row_src = [&](int t, const uint8_t* base, int& rr, bool& ok) {
     const int n = is_p.r0 + t;
-    const int j = small_quot(n, a.inv_bs);
+    int j;
+    int32_t e;
+    if (a.block_size >= kTileKeys) {  // (uniform) n < 2 block_size: the first or the next block
+      j = n >= a.block_size ? 1 : 0;
+      e = j ? is_ent[1] : is_ent[0];
+    } else {
+      j = small_quot(n, a.inv_bs);
+      e = sel16(is_ent, j);
+    }
     rr = n - j * a.block_size;
-    const int32_t e = sel16(is_ent, j);
     ok = (uint32_t)e < (uint32_t)a.num_blocks;
     return base + (uint64_t)(ok ? (uint32_t)e : 0u) * (uint64_t)a.block_bytes;
   };

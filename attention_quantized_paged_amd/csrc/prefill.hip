@@ -170,40 +170,56 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
     else return (int)div_invariant((uint32_t)k, a.bs_magic, a.bs_shift);
   };
   // GBS: entries of the 16 blocks from the one holding key k0 (scalar loads, clamped to the
-  // sequence's table row) and k0's row in its block
+  // sequence's table row) and k0's row in its block; with block_size >= 16 a tile spans at most
+  // two blocks, so two entries do
   struct Ents { int32_t e[16]; int r0; };
   auto tile_ents = [&](int k0) {
     Ents t;
     const int bi = key_block(k0);
     t.r0 = k0 - bi * a.block_size;
+    if (a.block_size >= kTileKeys) {
+      t.e[0] = bt[bi];
+      t.e[1] = bt[min(bi + 1, a.max_blocks - 1)];
+    } else {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) t.e[j] = bt[min(bi + j, a.max_blocks - 1)];
+      for (int j = 0; j < 16; ++j) t.e[j] = bt[min(bi + j, a.max_blocks - 1)];
+    }
     return t;
   };
-  // GBS: block (entry, or 0 outside the pool) and row of row n - r0 of a tile whose first key
-  // sits at row r0 of its block (n = r0 + tile row: j = n / bs < 16 blocks on)
-  auto row_block = [&](const Ents& t, int n, int& rr) {
-    const int j = small_quot(n, a.inv_bs);
+  // GBS: block-table entry (as stored) and row of row n - r0 of a tile whose first key sits at
+  // row r0 of its block (n = r0 + tile row: j = n / bs < 16 blocks on; 0 or 1 when block_size >= 16)
+  auto row_entry = [&](const Ents& t, int n, int& rr) {
+    int j;
+    int32_t e;
+    if (a.block_size >= kTileKeys) {
+      j = n >= a.block_size ? 1 : 0;
+      e = j ? t.e[1] : t.e[0];
+    } else {
+      j = small_quot(n, a.inv_bs);
+      e = sel16(t.e, j);
+    }
     rr = n - j * a.block_size;
-    const int32_t e = sel16(t.e, j);
+    return e;
+  };
+  // ... and the block to read (block 0 for an entry outside the pool)
+  auto row_block = [&](const Ents& t, int n, int& rr) {
+    const int32_t e = row_entry(t, n, rr);
     return (uint32_t)e < (uint32_t)a.num_blocks ? e : 0;
   };
-  // rows of the 16-key tile starting at key k0 whose block-table entries name blocks of the pool
-  // (bit t: the row copied for key k0 + t, i.e. key min(k0 + t, L - 1); keys of a block whose
-  // entry lies outside it are absent: masked like keys out of range, and their codes, read from
-  // block 0 instead, never reach a product)
+  // GBS: row masks of the issued steps, 32 bits per step (16 per tile) in slot step & 3, written
+  // when the step's copies are issued (every wave issues every step)
+  uint64_t ok_lo = 0, ok_hi = 0;
+  // rows of tile tt (0, 1) of step s whose block-table entries name blocks of the pool (bit t: the
+  // row copied for key k0 + t, i.e. key min(k0 + t, L - 1); keys of a block whose entry lies
+  // outside it are absent: masked like keys out of range, and their codes, read from block 0
+  // instead, never reach a product)
   using RowMask = std::conditional_t<GBS, uint32_t, bool>;  // without GBS a tile is whole or absent
-  auto tile_rows = [&](int k0) -> RowMask {
+  auto tile_rows = [&](int s, int tt) -> RowMask {
     if constexpr (GBS) {
-      // rows past L hold key L - 1's row, whose block may differ from the one of key k0 + t
-      const int base = min(k0, it.L - 1);
-      const Ents en = tile_ents(base);
-      const int key = min(k0 + (lane & 15), it.L - 1);
-      const int j = small_quot(en.r0 + (key - base), a.inv_bs);
-      const bool ok = (uint32_t)sel16(en.e, j) < (uint32_t)a.num_blocks;
-      return (uint32_t)__builtin_amdgcn_ballot_w64(ok && lane < 16) & 0xFFFFu;
+      const uint64_t w = (s & 2) ? ok_hi : ok_lo;
+      return (uint32_t)(w >> (32 * (s & 1) + 16 * tt)) & 0xFFFFu;
     } else {
-      return (uint32_t)bt[key_block(min(k0, last_tile))] < (uint32_t)a.num_blocks;
+      return (uint32_t)bt[key_block(min(k_begin + s * KT + kTileKeys * tt, last_tile))] < (uint32_t)a.num_blocks;
     }
   };
 
@@ -227,6 +243,27 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   auto issue = [&](int step) {
     const int kb0 = k_begin + step * KT;
     const uint32_t sbase = lds0 + (uint32_t)((step % NS) * STAGE);
+    // the step's two tiles, clamped to the tile of key L-1 (kb0 itself lies at or before it)
+    const int t0 = min(kb0, last_tile), t1 = min(kb0 + kTileKeys, last_tile);
+    Ents e0, e1;  // GBS: their block-table entries, read once for all of the step's copies
+    if constexpr (GBS) {
+      e0 = tile_ents(t0);
+      e1 = tile_ents(t1);
+      // the step's row masks: row t of tile tt holds key min(kb0 + 16 tt + t, L - 1)
+      uint32_t m2 = 0;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const Ents& en = tt ? e1 : e0;
+        const int key = min(kb0 + kTileKeys * tt + (lane & 15), it.L - 1);  // in [t_tt, t_tt + 16)
+        int rr;
+        const int32_t e = row_entry(en, en.r0 + (key - (tt ? t1 : t0)), rr);
+        const bool ok = (uint32_t)e < (uint32_t)a.num_blocks;
+        m2 |= ((uint32_t)__builtin_amdgcn_ballot_w64(ok && lane < 16) & 0xFFFFu) << (16 * tt);
+      }
+      const int sh = 32 * (step & 1);
+      if (step & 2) ok_hi = (ok_hi & ~(0xFFFFFFFFull << sh)) | ((uint64_t)m2 << sh);
+      else ok_lo = (ok_lo & ~(0xFFFFFFFFull << sh)) | ((uint64_t)m2 << sh);
+    }
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       const int ii = wave + WAVES * j;
@@ -240,7 +277,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       const int key = min(kb0 + row, it.L - 1);  // in [tile_k0, tile_k0 + 16)
       const uint8_t* src;
       if constexpr (GBS) {
-        const Ents en = tile_ents(tile_k0);
+        const Ents& en = ((q0 / CPR) & 16) ? e1 : e0;  // (tile_k0 is t0 or t1 alike)
         int rr;
         const int32_t blk = row_block(en, en.r0 + (key - tile_k0), rr);
         src = (kv ? vbase : kbase) + (int64_t)blk * a.block_bytes + (int64_t)rr * ROWB + lc * 16;
@@ -257,8 +294,6 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
       if (wave == WAVES - 1) {
         // row by row, 4 bytes per lane: per token-head [K scales of the 32 keys][V scales]; per
         // group [K tile 0][K tile 1][V tile 0][V tile 1], 16 rows x NG floats each
-        const int t0 = min(kb0, last_tile), t1 = min(kb0 + 16, last_tile);
-        const Ents e0 = tile_ents(t0), e1 = tile_ents(t1);
 #pragma unroll
         for (int c = 0; c < SCI; ++c) {
           const int idx = 64 * c + lane;
@@ -473,18 +508,18 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
     __syncthreads();  // stages 0 and 1 landed for every wave
     convert_k(0);
     convert_k(1);
-    convert_v(0, tile_rows(k_begin), tile_rows(k_begin + kTileKeys));
+    convert_v(0, tile_rows(0, 0), tile_rows(0, 1));
     __syncthreads();
     bf16x8 kw[2][QS];
     read_k(0, kw);
     qk_half(0, kw, s_cur, 0);
     qk_half(1, kw, s_cur, 0);
   }
-  RowMask cur_ok0 = n_steps > 0 ? tile_rows(k_begin) : RowMask(0), cur_ok1 = n_steps > 0 ? tile_rows(k_begin + kTileKeys) : RowMask(0);
+  RowMask cur_ok0 = n_steps > 0 ? tile_rows(0, 0) : RowMask(0), cur_ok1 = n_steps > 0 ? tile_rows(0, 1) : RowMask(0);
   for (int step = 0; step < n_steps; ++step) {
     // validity of the next step's tiles (its V codes are widened in this iteration; its keys are
     // masked in the next)
-    const RowMask nxt_ok0 = tile_rows(k_begin + (step + 1) * KT), nxt_ok1 = tile_rows(k_begin + (step + 1) * KT + kTileKeys);
+    const RowMask nxt_ok0 = tile_rows(step + 1, 0), nxt_ok1 = tile_rows(step + 1, 1);
     // stage step + 2 landed once only the copies of later stages are outstanding
     const int issued = min(n_steps, step + NS);
     // (issued - step - 3 is 1, or 0 at the last steps: compile-time counts, no runtime switch)
