@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--all-configs", action="store_true",
                     help="one JSON line per configuration (1-5): cache write of its history and one "
                          "attention call, median kernel times with a 1 GiB read between repetitions")
+    ap.add_argument("--block-sizes", action="store_true",
+                    help="with --all-configs: the decode batch (block 1, 24, 32) and the large prefill (block 8, 24, "
+                         "2200) instead of the configurations")
     ap.add_argument("--only", default="",
                     help="with --all-configs: comma-separated workload names to run (default: all)")
     ap.add_argument("--no-oracle", action="store_true",
@@ -296,7 +299,15 @@ def run_all_configs(torch, aqp, W, args):
     auto3 = W.scaled(W.CFG3, name="decode64_bf16_auto_llama8b", kv_dtype="auto")
     auto2 = W.scaled(W.CFG2, name="prefill_bf16_auto_d256_bs2176", kv_dtype="auto")
     only = set(x for x in args.only.split(",") if x)
-    for w in (W.CFG1, W.CFG2, W.CFG3, W.CFG4, W.CFG5A, W.CFG5B, auto3, auto2):
+    configs = (W.CFG1, W.CFG2, W.CFG3, W.CFG4, W.CFG5A, W.CFG5B, auto3, auto2)
+    if args.block_sizes:
+        # the decode batch and the large prefill with only the block size changed (block sizes that
+        # are not a multiple of 16 take the kernels that gather a tile row by row)
+        configs = tuple(W.scaled(W.CFG3, name=f"decode64_fp8e4m3_pt_llama8b_bs{bs}", block_size=bs,
+                                 num_blocks=-(-40000 * 16 // bs) + 64) for bs in (1, 24, 32)) + \
+                  tuple(W.scaled(W.CFG2, name=f"prefill_fp8e4m3_pt_d256_bs{bs}", block_size=bs,
+                                 num_blocks=4 * -(-1024 // bs) + 8) for bs in (8, 24, 2200))
+    for w in configs:
         if only and w.name not in only:
             continue
         log(args, f"[bench] {w.name}")
