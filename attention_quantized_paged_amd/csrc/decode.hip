@@ -258,7 +258,7 @@ __global__ __launch_bounds__((kDecWaves + 1) * 64) __attribute__((amdgpu_waves_p
   cptr<int32_t> is_bt = as_const(a.block_tables);
   const uint8_t* is_kv = a.cache;  // K page of the segment's KV head in block 0
   int32_t is_blk = 0;              // block-table entry of the next tile (read one tile ahead)
-  int32_t is_ent[16] = {};         // GBS: entries of the 16 blocks from the next tile's first
+  i32x16 is_ent = {};              // GBS: entries of the 16 blocks from the next tile's first
   uint64_t ok_rows = 0;            // GBS: bits 16 (n & 3) ..: rows of tile n in blocks of the pool
   // the next tile's block-table entries (scalar loads; clamped to the sequence's table row); with
   // GBS and block_size >= 16 a tile spans at most two blocks, so two entries do

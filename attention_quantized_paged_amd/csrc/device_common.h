@@ -14,6 +14,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+// 16 wave-uniform block-table entries, kept as one vector value (registers): an array here ends
+// up in scratch memory once a select between two of its elements becomes an indexed load
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -188,14 +191,13 @@ __device__ __forceinline__ uint32_t div_invariant(uint32_t n, uint32_t m, int32_
 __device__ __forceinline__ int small_quot(int n, float rd) { return (int)(((float)n + 0.5f) * rd); }
 
 // e[j] for a per-lane j in [0, 16) and 16 wave-uniform values (a select tree on j's bits).
-__device__ __forceinline__ int32_t sel16(const int32_t (&e)[16], int j) {
-  int32_t a[8], b[4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = (j & 1) ? e[2 * i + 1] : e[2 * i];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) b[i] = (j & 2) ? a[2 * i + 1] : a[2 * i];
-  const int32_t c0 = (j & 4) ? b[1] : b[0], c1 = (j & 4) ? b[3] : b[2];
-  return (j & 8) ? c1 : c0;
+__device__ __forceinline__ int32_t sel16(i32x16 e, int j) {
+  const bool b0 = j & 1, b1 = j & 2, b2 = j & 4, b3 = j & 8;
+  const int32_t a0 = b0 ? e[1] : e[0], a1 = b0 ? e[3] : e[2], a2 = b0 ? e[5] : e[4], a3 = b0 ? e[7] : e[6];
+  const int32_t a4 = b0 ? e[9] : e[8], a5 = b0 ? e[11] : e[10], a6 = b0 ? e[13] : e[12], a7 = b0 ? e[15] : e[14];
+  const int32_t c0 = b1 ? a1 : a0, c1 = b1 ? a3 : a2, c2 = b1 ? a5 : a4, c3 = b1 ? a7 : a6;
+  const int32_t d0 = b2 ? c1 : c0, d1 = b2 ? c3 : c2;
+  return b3 ? d1 : d0;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
   // GBS: entries of the 16 blocks from the one holding key k0 (scalar loads, clamped to the
   // sequence's table row) and k0's row in its block; with block_size >= 16 a tile spans at most
   // two blocks, so two entries do
-  struct Ents { int32_t e[16]; int r0; };
+  struct Ents { i32x16 e; int r0; };
   auto tile_ents = [&](int k0) {
     Ents t;
     const int bi = key_block(k0);
