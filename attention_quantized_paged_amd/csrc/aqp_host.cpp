@@ -374,7 +374,7 @@ extern "C" int aqp_get_schedule(const aqp_attn_params* params, const aqp_cache_d
     for (const PfItem& it : pf) total_steps += steps_of(it);
     const int64_t cap = (int64_t)device_cu_count() *
                         (pf32_applies(desc->dtype, desc->mode, desc->head_dim, desc->block_size) ? pf32_wgs_per_cu(desc->head_dim, desc->mode, rows, g.pf_lds_bytes)
-                                                               : pf_wgs_per_cu(desc->head_dim, desc->mode, rows, g.pf_lds_bytes));
+                                                               : pf_wgs_per_cu(desc->head_dim, rows, g.pf_lds_bytes));
     if (p.prefill_kv_split > 1) {
       sp.max_runs = p.prefill_kv_split;
       sp.min_steps = 1;

@@ -57,20 +57,15 @@ constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per compute unit (gfx950)
 // Accelerator dies (XCDs) of the chip, each with its own L2: work-group i of a launch runs on XCD
 // i % kXcds.
 constexpr int kXcds = 8;
-// Waves per SIMD the 16x16 prefill's registers are sized for (the least occupancy the compiler
-// must keep): three at head_dim 64, two above. (Per-group scales at head_dim 64 spill some
-// registers at three, yet measured faster there than without the spill at two: 40.6 against
-// 45.8 us on 8 x 512 tokens, 32/8 heads.)
-constexpr int pf_waves_per_simd(int head_dim, int mode) { return head_dim <= 64 ? 3 : 2; }
 // Prefill work-groups a CU holds at once: the register limit of the compiled kernel (8 waves at two
-// per SIMD at head_dim 256; 4 waves at two per SIMD at 128 rows and head_dim 128, three below) and
-// the LDS limit.
-constexpr int pf_wgs_per_cu_regs(int head_dim, int mode, int rows) {
-  return head_dim >= 256 ? 1 : (head_dim == 128 && rows > kPfRowsSmall ? 2 : 3);
-}
-constexpr int pf_wgs_per_cu(int head_dim, int mode, int rows, int32_t lds_bytes) {
-  return pf_wgs_per_cu_regs(head_dim, mode, rows) < kLdsPerCu / lds_bytes ? pf_wgs_per_cu_regs(head_dim, mode, rows)
-                                                                           : kLdsPerCu / lds_bytes;
+// per SIMD at head_dim 256; 4 waves at two per SIMD at 128 rows and head_dim 128, three below)
+// and the LDS limit. (Per-group scales at head_dim 64 spill some registers at three waves per
+// SIMD, yet measured faster there than without the spill at two: 40.6 against 45.8 us on 8 x 512
+// tokens, 32/8 heads.)
+constexpr int pf_wgs_per_cu(int head_dim, int rows, int32_t lds_bytes) {
+  return (head_dim >= 256 ? 1 : (head_dim == 128 && rows > kPfRowsSmall ? 2 : 3)) < kLdsPerCu / lds_bytes
+             ? (head_dim >= 256 ? 1 : (head_dim == 128 && rows > kPfRowsSmall ? 2 : 3))
+             : kLdsPerCu / lds_bytes;
 }
 // The 32x32 prefill kernel (prefill32.hip) serves one-byte codes with per-tensor or per-token-head
 // scales up to head_dim 128, where it runs two waves per SIMD; per-group scales, the unquantised
@@ -88,7 +83,7 @@ constexpr int kPf32Stages = 4;  // LDS ring stages of the 32x32 prefill (four st
 // (168 registers each) fit the per-tensor kernel; the per-token-head kernel (scales beside the
 // logits and probabilities) would spill to scratch memory there, and takes two (measured: int8 per
 // token-head 55 -> 37-45 us on 8 x 512 tokens, 32/8 heads).
-constexpr int pf32_waves_per_simd(int head_dim, int mode, int waves) {
+constexpr int pf32_waves_per_simd(int head_dim, int mode) {
   return head_dim >= 256 ? 1 : (head_dim == 128 || mode == AQP_SCALE_PER_TOKEN_HEAD ? 2 : 3);
 }
 // Ring stage: the codes of kPfKvTile keys of K and of V, then (per token-head) their fp32 scales.
@@ -103,8 +98,8 @@ constexpr int32_t pf32_lds_bytes(int head_dim, int mode) {
   return kPf32Stages * pf32_stage_bytes(head_dim, mode) + 4 * kPfKvTile * head_dim * 2 + kPf32TableBytes;
 }
 constexpr int pf32_wgs_per_cu(int head_dim, int mode, int rows, int32_t lds_bytes) {
-  return 4 * pf32_waves_per_simd(head_dim, mode, rows / 32) / (rows / 32) < kLdsPerCu / lds_bytes
-             ? 4 * pf32_waves_per_simd(head_dim, mode, rows / 32) / (rows / 32)
+  return 4 * pf32_waves_per_simd(head_dim, mode) / (rows / 32) < kLdsPerCu / lds_bytes
+             ? 4 * pf32_waves_per_simd(head_dim, mode) / (rows / 32)
              : kLdsPerCu / lds_bytes;
 }
 // fp32 scales stored per cache row: none per tensor, one per token-head, head_dim / 32 per group

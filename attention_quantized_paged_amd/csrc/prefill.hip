@@ -63,7 +63,7 @@ __device__ __forceinline__ int swz(int row) {
 // 16): its rows are copied from their own blocks, its scales likewise in 4-byte copies, and the
 // absent rows of a tile are masked row by row.
 template <int D, int DT, int MODE, bool CAP, int ROWS, bool GBS>
-__global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_eu(pf_waves_per_simd(D, MODE)))) void prefill_kernel(PfArgs a) {
+__global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 2))) void prefill_kernel(PfArgs a) {
   constexpr int NT = D / 16;
   constexpr int QS = D / 32;
   constexpr int WAVES = pf_waves(D);

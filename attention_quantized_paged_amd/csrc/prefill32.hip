@@ -110,7 +110,7 @@ __device__ __forceinline__ T& pick(T& a, T& b) {
 }
 
 template <int D, int DT, int MODE, bool CAP, bool ALIBI, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(pf32_waves_per_simd(D, MODE, WAVES))))
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(pf32_waves_per_simd(D, MODE))))
 void prefill32_kernel(Pf32Args a) {
   constexpr int KT = kPfKvTile;                    // keys per step
   static_assert(KT == 32, "one 32x32 S tile per step");
