@@ -449,6 +449,43 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
     }
   };
 
+  // ---- the same two widenings (one-byte codes, per-tensor or per-token-head scales) in two
+  // phases: every code read of both issued before any image write, so that the reads wait on one
+  // LDS round trip together (an image write cannot be moved above a later ring read it might
+  // alias, so the one-block-at-a-time form waits once per block)
+  auto kv_codes = [&](int kstep, int vstep, uint2 (&kc)[KB_PW], i32x2 (&vc)[VB_PW]) {
+    const uint8_t* kl = smem + (kstep % NS) * STAGE;
+#pragma unroll
+    for (int j = 0; j < KB_PW; ++j) {
+      const int blk = wave * KB_PW + j;
+      const int kt = blk / QS, st = blk - (blk / QS) * QS;
+      const int krow = kt * 16 + r16;
+      const int dbyte = kg * (D / 4) + st * 8;
+      kc[j] = *(const uint2*)(kl + krow * ROWB + ((((dbyte >> 4) ^ swz<ROWB>(krow)) << 4) | (dbyte & 8)));
+    }
+    const uint8_t* rp = smem + (vstep % NS) * STAGE + KT * ROWB + tr_row * ROWB + (r16 & 1) * 8;
+#pragma unroll
+    for (int j = 0; j < VB_PW; ++j) vc[j] = lds_read_tr8(rp + (((wave * VB_PW + j) ^ tr_swz) << 4));
+  };
+  auto kv_images = [&](int kstep, int vstep, RowMask ok0, RowMask ok1, const uint2 (&kc)[KB_PW], const i32x2 (&vc)[VB_PW]) {
+    uint8_t* img = smem + KIMG + (kstep & 1) * IMG + lane * 16;
+#pragma unroll
+    for (int j = 0; j < KB_PW; ++j) *(bf16x8*)(img + (wave * KB_PW + j) * 1024) = widen8<DT>(kc[j].x, kc[j].y);
+    uint8_t* slot = smem + VIMG + (vstep & 1) * VSLOT;
+    const uint32_t b0 = ((uint32_t)ok0 >> (4 * kg)) & 0xFu, b1 = ((uint32_t)ok1 >> (4 * kg)) & 0xFu;
+    auto bytes = [](uint32_t b) {
+      return ((b & 1u) ? 0xFFu : 0u) | ((b & 2u) ? 0xFF00u : 0u) | ((b & 4u) ? 0xFF0000u : 0u) | ((b & 8u) ? 0xFF000000u : 0u);
+    };
+    const uint32_t msk0 = GBS ? bytes(b0) : (ok0 ? 0xFFFFFFFFu : 0u), msk1 = GBS ? bytes(b1) : (ok1 ? 0xFFFFFFFFu : 0u);
+#pragma unroll
+    for (int j = 0; j < VB_PW; ++j)
+      *(bf16x8*)(slot + (wave * VB_PW + j) * 1024 + lane * 16) = widen8<DT>((uint32_t)vc[j].x & msk0, (uint32_t)vc[j].y & msk1);
+    if constexpr (PTH) {
+      const uint8_t* kl = smem + (vstep % NS) * STAGE;
+      if (wave == WAVES - 1 && lane < 16) *(uint4*)(slot + IMG + lane * 16) = *(const uint4*)(kl + 2 * KT * ROWB + lane * 16);
+    }
+  };
+
   // ---- K operands of one step from its K image: [key tile][depth slice]
   auto read_k = [&](int step, bf16x8 (&kw)[2][QS]) {
     const uint8_t* img = smem + KIMG + (step & 1) * IMG + lane * 16;
@@ -642,8 +679,15 @@ __global__ __launch_bounds__(pf_waves(D) * 64) __attribute__((amdgpu_waves_per_e
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) acc[rt][t] = mfma16x16x32(vw[t], pb[rt], acc[rt][t]);
-    convert_k(step + 2);
-    convert_v(step + 1, nxt_ok0, nxt_ok1);
+    if constexpr (EB == 1 && !PG) {
+      uint2 kc[KB_PW];
+      i32x2 vc[VB_PW];
+      kv_codes(step + 2, step + 1, kc, vc);
+      kv_images(step + 2, step + 1, nxt_ok0, nxt_ok1, kc, vc);
+    } else {
+      convert_k(step + 2);
+      convert_v(step + 1, nxt_ok0, nxt_ok1);
+    }
     // issue order of this block: half the V reads, then each matrix op of S with four vector ops
     // of the softmax, then each PV matrix op with one LDS read and one vector op
     __builtin_amdgcn_sched_group_barrier(0x100, NT / 2, 0);
