@@ -411,8 +411,8 @@ def test_per_sequence_causal_flags_and_seq_lens_are_recorded():
 
 def test_prefill_rows_choice():
     """128 query rows per prefill item by default; 64 at head_dim <= 128 for a prefill-only batch
-    whose 128-row items would number fewer than two per CU (256 CUs without a device); an explicit
-    choice is kept, recorded and checked."""
+    whose 128-row items would number fewer than two per CU (256 CUs without a device), and for
+    per-group scales at head_dim 128; an explicit choice is kept, recorded and checked."""
     few = ((100, 300), (40, 40))
     assert h_rows(_sched(few, 32, 8, 128, 16)[0]) == 64
     assert h_rows(_sched(few, 8, 2, 64, 16)[0]) == 64
@@ -428,6 +428,14 @@ def test_prefill_rows_choice():
     assert h_rows(_sched(many, 32, 8, 128, 16)[0]) == 128
     assert h_rows(_sched(few, 32, 8, 128, 16, rows=128)[0]) == 128
     assert h_rows(_sched(many, 32, 8, 128, 16, rows=64)[0]) == 64
+    # per-group scales at head_dim 128: 64-row items by default (with or without decode work beside
+    # them, however many items), 128 when asked; at head_dim 64 and 256 the usual choice
+    for dt in ("fp8_per_group", "int8_per_group", "fp8_e5m2_per_group"):
+        assert h_rows(_sched(many, 32, 8, 128, 16, dtype=dt)[0]) == 64
+        assert h_rows(_sched(few + ((1, 500),), 32, 8, 128, 16, dtype=dt)[0]) == 64
+        assert h_rows(_sched(many, 32, 8, 128, 16, dtype=dt, rows=128)[0]) == 128
+    assert h_rows(_sched(((1024, 1024),) * 8, 8, 2, 64, 16, dtype="fp8_per_group")[0]) == 128
+    assert h_rows(_sched(few, 16, 2, 256, 64, dtype="fp8_per_group")[0]) == 128
     with pytest.raises(aqp.AqpError) as e:
         _sched(few, 32, 8, 128, 16, rows=32)
     assert e.value.status == aqp.ERR_INVALID
