@@ -254,7 +254,9 @@ int aqp_paged_attention_timed(const aqp_attn_params* params, const aqp_cache_des
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * partial results of split ranges go to a fixed 64 MiB device array of the library (one per GPU
  * it runs on, held until the process ends; its address is looked up once per device on the
- * first call there). The call itself allocates nothing and creates nothing. Arguments, layouts,
+ * first call there). The call itself allocates nothing and creates nothing (the per-group
+ * prefill kernels at head_dim 64 with 128-row items and at head_dim 256 spill registers: their
+ * launches use the scratch memory the HIP runtime keeps for its queues). Arguments, layouts,
  * stream use and results are those of aqp_paged_attention. No part of the array has to
  * start at zero (every partial result is written before it is merged). Every call on one GPU
  * shares its array: calls that overlap on a GPU (other streams, other threads) race; serialise
